@@ -1,0 +1,126 @@
+/*
+ * lowbit.h -- C ABI of the packed low-bit GEMV/GEMM library for MI355X (gfx950).
+ *
+ * The library multiplies fp16/bf16 activations by weights kept in packed
+ * group-scaled low-bit form and never expands them to a dense matrix in
+ * memory: the sign bits / trits are decoded inside the matrix kernels and
+ * multiplied by their group's FP16 scale there.
+ *
+ * Formats (value maps fixed by the pages this library follows):
+ *  - LOWBIT_Q1_G128, "Binary g128": one sign bit per weight, stored bit 0 means
+ *    -scale and bit 1 means +scale; one FP16 scale per 128 weights, so
+ *    1 + 16/128 = 1.125 bits per weight (lnrk.cn page, Binary g128 section;
+ *    aberweb.com page, section 4.1 and Table 2).
+ *  - LOWBIT_TQ2_G128, "Ternary g128 in 2-bit slots": t in {-1,0,+1} stored as
+ *    the 2-bit code c = t + 1 (code 3 unused), one FP16 scale per 128 weights,
+ *    2.125 bits per weight (ksqn.cn page, ternary weight representation and
+ *    "current limitations").
+ *  - LOWBIT_TQ5_G128, "Ternary g128, 5 trits per byte": base-3 digits
+ *    d = t + 1, five per byte (3^5 = 243 <= 256, cnblogs.com page, section
+ *    2.4), ceil(K/5) bytes per row, one FP16 scale per 128 weights.
+ *  A group is 128 consecutive weights along K inside one row, so K must be a
+ *  multiple of 128.
+ *
+ * Blob ("packed weights"): headerless, exactly packed_bytes_lowbit(fmt,N,K)
+ * bytes: plane A (signs / codes / trit bytes in the device layout v1, an
+ * arrangement of the bits chosen for 128-bit coalesced loads and cheap
+ * in-register decode) followed by plane B, the FP16 scale bit patterns
+ * row-major [N][K/128].  pack_* writes it, unpack_lowbit inverts it exactly.
+ *
+ * Product: for m < M, n < N
+ *     Y[m][n] = sum_k X[m][k] * t[n][k] * s[n][k/128]
+ * W row n is output feature n (nn.Linear order); X is M x K and Y is M x N,
+ * both row-major and contiguous.  Y is overwritten.  Accumulation is fp32
+ * with every product exact (weights are decoded to exact +-1 / 0 and the
+ * FP16 scale is applied in fp32 once per group); an fp16 Y is rounded to
+ * nearest even from the fp32 result.  Results are deterministic for a given
+ * input, shape and device.
+ *
+ * Errors: every call validates its arguments before doing anything and
+ * returns LOWBIT_OK (0) or a negative status; on error nothing is written and
+ * nothing is launched.  No C++ exception, abort or exit crosses this ABI.
+ * Thread safety: all calls are reentrant; the library keeps no state besides
+ * a lazily filled, lock-protected cache of device properties.
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOWBIT_ABI_VERSION 1
+
+typedef enum { LOWBIT_Q1_G128 = 1, LOWBIT_TQ2_G128 = 2, LOWBIT_TQ5_G128 = 3 } lowbit_format;
+typedef enum { LOWBIT_F16 = 1, LOWBIT_BF16 = 2, LOWBIT_F32 = 3 } lowbit_dtype;
+
+enum {
+  LOWBIT_OK = 0,
+  LOWBIT_ERR_NULL = -1,   /* a required pointer is NULL                               */
+  LOWBIT_ERR_ENUM = -2,   /* unknown format or dtype value                            */
+  LOWBIT_ERR_SHAPE = -3,  /* negative M/N/K, or K not a multiple of 128               */
+  LOWBIT_ERR_VALUE = -4,  /* code outside the format's set (pack), tq2 code 3, tq5 byte
+                             >= 243 or non-zero tq5 padding trit (unpack)             */
+  LOWBIT_ERR_SIZE = -5,   /* a buffer is smaller than required                        */
+  LOWBIT_ERR_ALIGN = -6,  /* W or X not 16-byte aligned, Y not aligned to its dtype     */
+  LOWBIT_ERR_DTYPE = -7,  /* unsupported x / y dtype combination                       */
+  LOWBIT_ERR_DEVICE = -8  /* the HIP runtime reported an error                         */
+};
+
+/* Library ABI version (LOWBIT_ABI_VERSION of the build). */
+int lowbit_abi_version(void);
+
+/* Static string describing a status code; never NULL. */
+const char *lowbit_strerror(int status);
+
+/* Size in bytes of a packed blob: plane A + N*(K/128)*2.
+ *   q1: N*K/8 + N*(K/128)*2      (1.125 bits per weight)
+ *   tq2: N*K/4 + N*(K/128)*2     (2.125 bits per weight)
+ *   tq5: N*ceil(K/5) + N*(K/128)*2
+ * Returns a negative status on a bad format or shape. */
+int64_t packed_bytes_lowbit(int fmt, int64_t N, int64_t K);
+
+/* Pack codes and scales (host memory in, host memory out).
+ *   codes:  int8 [N][K], row-major; q1: values in {-1,+1}; tq2/tq5: {-1,0,+1}
+ *   scales: uint16 [N][K/128], FP16 bit patterns, stored bit-exactly
+ *   out:    caller-owned, at least packed_bytes_lowbit(fmt, N, K) bytes
+ * Returns LOWBIT_ERR_VALUE (and writes nothing) if any code is out of set.
+ * Uses up to hardware_concurrency() host threads.                         */
+int pack_q1_g128(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                 void *out, int64_t out_bytes);
+int pack_tq2_g128(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                  void *out, int64_t out_bytes);
+int pack_tq5_g128(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                  void *out, int64_t out_bytes);
+
+/* Exact inverse of pack_* (host memory).  codes_out int8 [N][K] and
+ * scales_out uint16 [N][K/128] are caller-owned; either may be NULL to skip it. */
+int unpack_lowbit(int fmt, const void *packed, int64_t packed_bytes, int64_t N, int64_t K,
+                  int8_t *codes_out, uint16_t *scales_out);
+
+/* Decode GEMV: Y = X W^T for small batches (tuned for M <= 16; any M works).
+ *   Wp: device, packed blob of this (fmt, N, K), 16-byte aligned
+ *   X:  device, M x K, x_dtype LOWBIT_F16 or LOWBIT_BF16, 16-byte aligned
+ *   Y:  device, M x N, y_dtype LOWBIT_F32 or LOWBIT_F16
+ *   hip_stream: hipStream_t to launch on (NULL = default stream); the call is
+ *   asynchronous with respect to the host.
+ * M*N == 0 returns LOWBIT_OK without launching; K == 0 writes Y = 0.       */
+int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype,
+                int64_t M, int64_t N, int64_t K, void *hip_stream);
+
+/* Workspace gemm_lowbit needs for this problem (0 = none). */
+int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
+
+/* Prefill GEMM: Y = X W^T for large batches (M = prompt tokens).  Same
+ * arguments and rules as gemv_lowbit, plus a caller-owned device workspace of
+ * at least gemm_workspace_bytes_lowbit() bytes (may be NULL when that is 0). */
+int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype,
+                int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
+                void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOWBIT_H */

@@ -1,0 +1,203 @@
+"""ctypes binding of liblowbit.so: argument marshalling only.
+
+Every step of the product runs in the library (host packer, HIP kernels).
+There is no Python or CPU fallback: if the library is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblowbit.so")
+
+FORMATS = {"q1": 1, "tq2": 2, "tq5": 3}
+DT_F16, DT_BF16, DT_F32 = 1, 2, 3
+GROUP = 128
+
+_lib = None
+
+
+class LowbitError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"lowbit error {status}: {msg}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m ternary_group_scaled_q1_amd.build`")
+    # torch bundles its own HIP runtime and loads it by the unversioned name
+    # libamdhip64.so.  If this library were loaded first, its dependency
+    # libamdhip64.so.7 would bring in the system runtime and torch would then
+    # load a second HIP (and HSA) runtime into the process.  Importing torch
+    # first lets the dynamic loader satisfy libamdhip64.so.7 with torch's
+    # copy (same SONAME), so the process has exactly one HIP runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    sig = {
+        "lowbit_abi_version": (i32, []),
+        "lowbit_strerror": (ctypes.c_char_p, [i32]),
+        "packed_bytes_lowbit": (i64, [i32, i64, i64]),
+        "pack_q1_g128": (i32, [vp, vp, i64, i64, vp, i64]),
+        "pack_tq2_g128": (i32, [vp, vp, i64, i64, vp, i64]),
+        "pack_tq5_g128": (i32, [vp, vp, i64, i64, vp, i64]),
+        "unpack_lowbit": (i32, [i32, vp, i64, i64, i64, vp, vp]),
+        "gemv_lowbit": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp]),
+        "gemm_workspace_bytes_lowbit": (i64, [i32, i64, i64, i64]),
+        "gemm_lowbit": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp, i64, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise LowbitError(status, load().lowbit_strerror(status).decode())
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown format {fmt!r}")
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def abi_version() -> int:
+    return load().lowbit_abi_version()
+
+
+def strerror(status: int) -> str:
+    return load().lowbit_strerror(int(status)).decode()
+
+
+def packed_bytes(fmt, N: int, K: int) -> int:
+    n = load().packed_bytes_lowbit(_fmt(fmt), N, K)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def pack(fmt, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """codes int8[N,K], scales uint16[N,K/128] (FP16 bits) -> uint8 blob."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    N, K = codes.shape
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    if scales.shape != (N, K // GROUP):
+        raise ValueError("scales must have shape (N, K // 128)")
+    f = _fmt(fmt)
+    out = np.empty(packed_bytes(f, N, K), dtype=np.uint8)
+    fn = {1: load().pack_q1_g128, 2: load().pack_tq2_g128, 3: load().pack_tq5_g128}[f]
+    _check(fn(codes.ctypes.data, scales.ctypes.data, N, K, out.ctypes.data, out.size))
+    return out
+
+
+def unpack(fmt, blob: np.ndarray, N: int, K: int):
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    codes = np.empty((N, K), dtype=np.int8)
+    scales = np.empty((N, K // GROUP), dtype=np.uint16)
+    _check(load().unpack_lowbit(_fmt(fmt), blob.ctypes.data, blob.size, N, K, codes.ctypes.data,
+                                scales.ctypes.data))
+    return codes, scales
+
+
+# ------------------------------------------------------------ device calls --
+def _torch():
+    import torch
+    return torch
+
+
+def _x_dtype(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return DT_F16
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    raise TypeError("x must be float16 or bfloat16")
+
+
+def _y_dtype(dt) -> int:
+    torch = _torch()
+    if dt == torch.float32:
+        return DT_F32
+    if dt == torch.float16:
+        return DT_F16
+    raise TypeError("out dtype must be float32 or float16")
+
+
+def _prep(fmt, w, x, N, K, out_dtype, out):
+    torch = _torch()
+    f = _fmt(fmt)
+    if not (w.is_cuda and x.is_cuda):
+        raise ValueError("w and x must be device tensors")
+    if w.dtype != torch.uint8 or not w.is_contiguous() or w.numel() < packed_bytes(f, N, K):
+        raise ValueError("w must be a contiguous uint8 device tensor of packed_bytes(fmt, N, K) bytes")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dim() != 2 or x.shape[1] != K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous (M, K) tensor")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    elif out.shape != (M, N) or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous (M, N) tensor on x's device")
+    return f, x, M, out
+
+
+def gemv(fmt, w, x, N: int, K: int, out_dtype=None, out=None, stream=None):
+    """y[M,N] = x[M,K] @ W^T on the GPU (decode path, M <= 16 preferred)."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    f, x, M, out = _prep(fmt, w, x, N, K, out_dtype, out)
+    s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+    _check(load().gemv_lowbit(f, w.data_ptr(), x.data_ptr(), _x_dtype(x), out.data_ptr(), _y_dtype(out.dtype),
+                              M, N, K, s))
+    return out
+
+
+def gemm_workspace_bytes(fmt, M: int, N: int, K: int) -> int:
+    n = load().gemm_workspace_bytes_lowbit(_fmt(fmt), M, N, K)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def gemm(fmt, w, x, N: int, K: int, out_dtype=None, out=None, workspace=None, stream=None):
+    """y[M,N] = x[M,K] @ W^T on the GPU (prefill path)."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    f, x, M, out = _prep(fmt, w, x, N, K, out_dtype, out)
+    need = gemm_workspace_bytes(f, M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_n = workspace.numel() if workspace is not None else 0
+    s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+    _check(load().gemm_lowbit(f, w.data_ptr(), x.data_ptr(), _x_dtype(x), out.data_ptr(), _y_dtype(out.dtype),
+                              M, N, K, ws_ptr, ws_n, s))
+    return out
+
+
+def gemv_raw(fmt: int, w_ptr: int, x_ptr: int, x_dtype: int, y_ptr: int, y_dtype: int, M: int, N: int, K: int,
+             stream_ptr: int) -> None:
+    """Pointer-level call (no tensor checks) for tight timing loops."""
+    _check(load().gemv_lowbit(fmt, w_ptr, x_ptr, x_dtype, y_ptr, y_dtype, M, N, K, stream_ptr))
+
+
+def gemm_raw(fmt: int, w_ptr: int, x_ptr: int, x_dtype: int, y_ptr: int, y_dtype: int, M: int, N: int, K: int,
+             stream_ptr: int, ws_ptr: int = 0, ws_bytes: int = 0) -> None:
+    _check(load().gemm_lowbit(fmt, w_ptr, x_ptr, x_dtype, y_ptr, y_dtype, M, N, K, ws_ptr or None, ws_bytes,
+                              stream_ptr))

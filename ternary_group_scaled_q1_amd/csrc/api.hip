@@ -1,0 +1,101 @@
+// C-ABI entry points: argument validation and dispatch to the HIP launchers.
+// Nothing is launched unless every argument is valid; no exception escapes.
+#include <hip/hip_runtime.h>
+
+#include "../../include/lowbit.h"
+#include "kernels.hpp"
+#include "layout.hpp"
+
+using namespace lowbit;
+
+namespace {
+
+int check_product(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M,
+                  int64_t N, int64_t K) {
+  if (fmt < LOWBIT_Q1_G128 || fmt > LOWBIT_TQ5_G128) return LOWBIT_ERR_ENUM;
+  if (x_dtype < LOWBIT_F16 || x_dtype > LOWBIT_F32 || y_dtype < LOWBIT_F16 || y_dtype > LOWBIT_F32)
+    return LOWBIT_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0 || K % kGroup) return LOWBIT_ERR_SHAPE;
+  // Index arithmetic inside the kernels is 32-bit per operand; keep every
+  // operand below 2^31 elements and every packed blob below 2^31 bytes.
+  if (M > (1 << 30) || N > (1 << 30) || K > (1 << 30) || M * K >= (int64_t(1) << 31) ||
+      M * N >= (int64_t(1) << 31) || packed_bytes_lowbit(fmt, N, K) >= (int64_t(1) << 31))
+    return LOWBIT_ERR_SHAPE;
+  if (x_dtype == LOWBIT_F32 || y_dtype == LOWBIT_BF16) return LOWBIT_ERR_DTYPE;
+  if (M == 0 || N == 0) return LOWBIT_OK;
+  if (!Y) return LOWBIT_ERR_NULL;
+  if (K > 0 && (!Wp || !X)) return LOWBIT_ERR_NULL;
+  const uintptr_t yw = y_dtype == LOWBIT_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(Y) % yw) != 0) return LOWBIT_ERR_ALIGN;
+  if (K > 0 && ((reinterpret_cast<uintptr_t>(Wp) & 15) || (reinterpret_cast<uintptr_t>(X) & 15)))
+    return LOWBIT_ERR_ALIGN;
+  return LOWBIT_OK;
+}
+
+int run(bool gemm, int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M, int64_t N,
+        int64_t K, void *stream) {
+  LaunchArgs a;
+  a.fmt = fmt;
+  a.W = static_cast<const uint8_t *>(Wp);
+  a.X = static_cast<const uint16_t *>(X);
+  a.Y = Y;
+  a.x_bf16 = x_dtype == LOWBIT_BF16;
+  a.y_f16 = y_dtype == LOWBIT_F16;
+  a.M = M; a.N = N; a.K = K;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (K == 0) {
+    e = launch_fill_zero(Y, M * N * (a.y_f16 ? 2 : 4), a.stream);
+  } else if (gemm || fmt == LOWBIT_TQ5_G128) {
+    e = launch_gemm(a);
+  } else {
+    e = launch_gemv(a);
+  }
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lowbit_abi_version(void) { return LOWBIT_ABI_VERSION; }
+
+const char *lowbit_strerror(int status) {
+  switch (status) {
+    case LOWBIT_OK: return "ok";
+    case LOWBIT_ERR_NULL: return "a required pointer is NULL";
+    case LOWBIT_ERR_ENUM: return "unknown format or dtype";
+    case LOWBIT_ERR_SHAPE: return "bad shape (negative size, K not a multiple of 128, or too large)";
+    case LOWBIT_ERR_VALUE: return "code or byte outside the format's value set";
+    case LOWBIT_ERR_SIZE: return "buffer smaller than required";
+    case LOWBIT_ERR_ALIGN: return "misaligned pointer (W and X need 16 bytes, Y its element size)";
+    case LOWBIT_ERR_DTYPE: return "unsupported dtype combination (x: f16/bf16, y: f32/f16)";
+    case LOWBIT_ERR_DEVICE: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M, int64_t N,
+                int64_t K, void *hip_stream) {
+  const int st = check_product(fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K);
+  if (st != LOWBIT_OK || M == 0 || N == 0) return st;
+  return run(false, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, hip_stream);
+}
+
+int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (fmt < LOWBIT_Q1_G128 || fmt > LOWBIT_TQ5_G128) return LOWBIT_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0 || K % kGroup) return LOWBIT_ERR_SHAPE;
+  return 0;
+}
+
+int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M, int64_t N,
+                int64_t K, void *workspace, int64_t workspace_bytes, void *hip_stream) {
+  const int st = check_product(fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K);
+  if (st != LOWBIT_OK || M == 0 || N == 0) return st;
+  const int64_t need = gemm_workspace_bytes_lowbit(fmt, M, N, K);
+  if (workspace_bytes < need) return LOWBIT_ERR_SIZE;
+  if (need > 0 && !workspace) return LOWBIT_ERR_NULL;
+  return run(true, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, hip_stream);
+}
+
+}  // extern "C"

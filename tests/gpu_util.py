@@ -1,0 +1,51 @@
+"""Helpers for the GPU parity tests: upload inputs, call the library through
+its binding (C ABI), compare with the oracle computed from the *generated*
+codes and scales (never from anything the library produced)."""
+import numpy as np
+
+import ternary_group_scaled_q1_amd as lb
+from oracle import ref
+
+_TORCH = None
+
+
+def torch():
+    global _TORCH
+    if _TORCH is None:
+        import torch as t
+        if not t.cuda.is_available():
+            raise RuntimeError("GPU tests need a visible MI355X")
+        _TORCH = t
+    return _TORCH
+
+
+def x_tensor(x_bits: np.ndarray, xdt: str):
+    t = torch()
+    host = t.from_numpy(np.ascontiguousarray(x_bits).view(np.int16))
+    return host.view(t.float16 if xdt == "f16" else t.bfloat16).cuda()
+
+
+def w_tensor(blob: np.ndarray):
+    return torch().from_numpy(np.ascontiguousarray(blob)).cuda()
+
+
+def run(path: str, fmt: str, blob_dev, x_bits, xdt, ydt, N, K, x_dev=None):
+    t = torch()
+    x = x_dev if x_dev is not None else x_tensor(x_bits, xdt)
+    out_dtype = t.float32 if ydt == "f32" else t.float16
+    fn = lb.gemv if path == "gemv" else lb.gemm
+    y = fn(fmt, blob_dev, x, N, K, out_dtype=out_dtype)
+    t.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def check(y_gpu, codes, scales, x_bits, xdt, ctx=""):
+    y_ref, a_ref = ref.product(codes, scales, x_bits, xdt)
+    ok, worst = ref.within_tolerance(y_gpu, y_ref, a_ref)
+    if not ok:
+        bad = np.argwhere(np.abs(y_gpu - y_ref) > ref.RTOL * a_ref + ref.ATOL)
+        m, n = bad[0]
+        raise AssertionError(
+            f"{ctx}: {len(bad)} elements out of tolerance (worst ratio {worst:.3g}); first at "
+            f"(m={m}, n={n}) gpu={y_gpu[m, n]!r} ref={y_ref[m, n]!r} a={a_ref[m, n]!r}")
+    return worst

@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Floating point: every element within |y - y_ref| <= 2e-3 * sum|w x| + 1e-6.
+Integer-exact inputs (s = 1, x in {-2..2}): bit-exact.  Inputs are seeded and
+synthetic (synth), the oracle works from the generated codes and scales.
+"""
+import numpy as np
+import pytest
+
+import synth
+import ternary_group_scaled_q1_amd as lb
+from oracle import ref
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["q1", "tq2", "tq5"]
+
+
+def _codes(g, fmt, N, K, p_zero=0.3):
+    return synth.codes_binary(g, N, K) if fmt == "q1" else synth.codes_ternary(g, N, K, p_zero)
+
+
+# (N, K, M): ragged row tiles, ragged group chunks, tq5 tails, M up to 17
+GEMV_SHAPES = [(1, 128, 1), (17, 640, 3), (16, 512, 1), (33, 1152, 4), (256, 1024, 1), (300, 2048, 5),
+               (64, 17408, 8), (4100, 384, 16), (130, 5120, 17), (48, 4096, 2), (2, 768, 9)]
+GEMM_SHAPES = [(1, 16, 128), (130, 200, 640), (512, 256, 1280), (257, 17, 3200), (64, 130, 17408),
+               (200, 33, 896)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("ydt", ["f32", "f16"])
+def test_gemv_small_shapes(fmt, xdt, ydt):
+    g = np.random.default_rng(100)
+    for N, K, M in GEMV_SHAPES:
+        print(f"gemv {fmt} x={xdt} y={ydt} N={N} K={K} M={M}", flush=True)
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        x = synth.x_normal(g, M, K, xdt)
+        blob = gu.w_tensor(lb.pack(fmt, codes, sc))
+        y = gu.run("gemv", fmt, blob, x, xdt, ydt, N, K)
+        gu.check(y, codes, sc, x, xdt, f"gemv {fmt} {xdt}->{ydt} N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("ydt", ["f32", "f16"])
+def test_gemm_small_shapes(fmt, xdt, ydt):
+    g = np.random.default_rng(200)
+    for M, N, K in GEMM_SHAPES:
+        print(f"gemm {fmt} x={xdt} y={ydt} M={M} N={N} K={K}", flush=True)
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        x = synth.x_normal(g, M, K, xdt)
+        blob = gu.w_tensor(lb.pack(fmt, codes, sc))
+        y = gu.run("gemm", fmt, blob, x, xdt, ydt, N, K)
+        gu.check(y, codes, sc, x, xdt, f"gemm {fmt} {xdt}->{ydt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_integer_exact_is_bit_exact(path, fmt, xdt):
+    """s = 1 and x in {-2..2}: every partial sum is an integer below 2^24, so
+    any fp32 order is exact and the result must equal the oracle bitwise; a
+    wrong bit order, plane or code map shows up here."""
+    g = np.random.default_rng(300)
+    for N, K, M in [(17, 640, 3), (64, 2048, 16), (33, 17408, 1)]:
+        print(f"int-exact {path} {fmt} {xdt} N={N} K={K} M={M}", flush=True)
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_const(N, K // 128, 1.0)
+        x = synth.x_small_integers(g, M, K, xdt)
+        y = gu.run(path, fmt, gu.w_tensor(lb.pack(fmt, codes, sc)), x, xdt, "f32", N, K)
+        y_ref, _ = ref.product(codes, sc, x, xdt)
+        assert np.array_equal(y, y_ref), f"{path} {fmt} {xdt} N={N} K={K} M={M}"
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_sign_aligned_ties(path, fmt):
+    """y = a exactly (codes follow the sign of x).  Tie scales catch a scale
+    rounded to bf16; fp16 tie activations catch x rounded to bf16."""
+    g = np.random.default_rng(400)
+    N, K = 48, 2048
+    for xdt in ("bf16", "f16"):
+        x = synth.x_normal(g, 1, K, xdt) if xdt == "bf16" else synth.x_f16_tie(g, 1, K)
+        codes = synth.codes_sign_aligned(x[0], N, xdt, p_zero=0.0 if fmt == "q1" else 0.2, g=g)
+        sc = synth.scales_bf16_tie(g, N, K // 128)
+        y = gu.run(path, fmt, gu.w_tensor(lb.pack(fmt, codes, sc)), x, xdt, "f32", N, K)
+        gu.check(y, codes, sc, x, xdt, f"ties {path} {fmt} {xdt}")
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_deterministic_and_scale_doubling(path, fmt):
+    g = np.random.default_rng(500)
+    N, K, M = 200, 3200, 4
+    codes = _codes(g, fmt, N, K)
+    sc = synth.scales_absnormal(g, N, K // 128)
+    x = synth.x_normal(g, M, K, "bf16")
+    w = gu.w_tensor(lb.pack(fmt, codes, sc))
+    y1 = gu.run(path, fmt, w, x, "bf16", "f32", N, K)
+    y2 = gu.run(path, fmt, w, x, "bf16", "f32", N, K)
+    assert np.array_equal(y1, y2)
+    sc2 = synth.f64_to_f16_bits(2 * synth_decode(sc))
+    y3 = gu.run(path, fmt, gu.w_tensor(lb.pack(fmt, codes, sc2)), x, "bf16", "f32", N, K)
+    assert np.array_equal(y3, 2 * y1)
+
+
+def synth_decode(sc):
+    return sc.view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+def test_formats_agree_on_binary_weights(path):
+    g = np.random.default_rng(600)
+    N, K, M = 90, 1920, 2
+    codes = synth.codes_binary(g, N, K)
+    sc = synth.scales_absnormal(g, N, K // 128)
+    x = synth.x_normal(g, M, K, "f16")
+    for fmt in FMTS:
+        y = gu.run(path, fmt, gu.w_tensor(lb.pack(fmt, codes, sc)), x, "f16", "f32", N, K)
+        gu.check(y, codes, sc, x, "f16", f"{path} {fmt} on binary weights")
+
+
+def test_ternary_all_zero_gives_zero():
+    N, K = 40, 1280
+    codes = np.zeros((N, K), np.int8)
+    sc = synth.scales_const(N, K // 128, 0.5)
+    x = synth.x_normal(np.random.default_rng(1), 3, K, "bf16")
+    for fmt in ("tq2", "tq5"):
+        for path in ("gemv", "gemm"):
+            y = gu.run(path, fmt, gu.w_tensor(lb.pack(fmt, codes, sc)), x, "bf16", "f32", N, K)
+            assert not y.any()
+
+
+def test_degenerate_sizes():
+    t = gu.torch()
+    L = lb.load()
+    # M == 0 or N == 0: OK, nothing launched or written
+    y = t.full((1, 4), 7.0, device="cuda")
+    assert L.gemv_lowbit(1, None, None, 1, y.data_ptr(), 3, 0, 4, 128, None) == 0
+    assert L.gemm_lowbit(1, None, None, 1, y.data_ptr(), 3, 1, 0, 128, None, 0, None) == 0
+    t.cuda.synchronize()
+    assert (y == 7.0).all()
+    # K == 0: the empty sum, Y = 0
+    for fn in ("gemv", "gemm"):
+        y = t.full((3, 5), 7.0, device="cuda")
+        w = t.zeros(16, dtype=t.uint8, device="cuda")
+        x = t.zeros((3, 0), dtype=t.float16, device="cuda")
+        st = (L.gemv_lowbit(1, w.data_ptr(), w.data_ptr(), 1, y.data_ptr(), 3, 3, 5, 0, None) if fn == "gemv"
+              else L.gemm_lowbit(1, w.data_ptr(), w.data_ptr(), 1, y.data_ptr(), 3, 3, 5, 0, None, 0, None))
+        assert st == 0
+        t.cuda.synchronize()
+        assert (y == 0).all()
+    # misaligned device pointers are refused before launch
+    w = t.zeros(1024, dtype=t.uint8, device="cuda")
+    x = t.zeros((1, 128), dtype=t.float16, device="cuda")
+    y = t.zeros(64, dtype=t.float32, device="cuda")
+    assert L.gemv_lowbit(1, w.data_ptr() + 8, x.data_ptr(), 1, y.data_ptr(), 3, 1, 1, 128, None) == -6
+
+
+# ------------------------------------------------ full workload shapes ----
+def _sampled(fmt, N, K, M, xdt, path, cfg, mid, p_zero, rows=48, seed=0):
+    codes, sc = synth.draw_matrix(seed, cfg, mid, N, K, p_zero)
+    x = synth.draw_x(seed, cfg, mid, M, K, xdt)
+    w = gu.w_tensor(lb.pack(fmt, codes, sc))
+    y = gu.run(path, fmt, w, x, xdt, "f32", N, K)
+    g = np.random.default_rng(seed + 17)
+    pick = np.unique(np.concatenate([g.integers(0, N, rows), [0, N - 1]]))
+    y_ref, a_ref = ref.product(codes[pick], sc[pick], x, xdt)
+    ok, worst = ref.within_tolerance(y[:, pick], y_ref, a_ref)
+    assert ok, f"{path} {fmt} N={N} K={K} M={M}: worst {worst}"
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("mid", [0, 1, 2])
+def test_workload_q1_decode_8b_shapes(mid):
+    N, K = synth.CONFIGS[2]["shapes"][mid]
+    print(f"q1 gemv N={N} K={K}", flush=True)
+    _sampled("q1", N, K, 1, "f16", "gemv", 2, mid, None)
+
+
+@pytest.mark.parametrize("mid", [0, 1])
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_workload_tq2_decode_27b_shapes(mid, M):
+    N, K = synth.CONFIGS[3]["shapes"][mid]
+    print(f"tq2 gemv N={N} K={K} M={M}", flush=True)
+    _sampled("tq2", N, K, M, "bf16", "gemv", 3, mid, 0.3)
+
+
+@pytest.mark.parametrize("mid", [0, 1])
+def test_workload_prefill_gemm(mid):
+    c = synth.CONFIGS[4]
+    N, K = c["shapes"][mid]
+    fmt, p0 = c["fmt"][mid], c["p_zero"][mid]
+    print(f"{fmt} gemm M=512 N={N} K={K}", flush=True)
+    _sampled(fmt, N, K, 512, "bf16", "gemm", 4, mid, p0, rows=24)
+
+
+def test_workload_config1_all_outputs():
+    c = synth.CONFIGS[1]
+    N, K = c["shapes"][0]
+    codes, sc = synth.draw_matrix(0, 1, 0, N, K, None, scales=c["scales"])
+    x = synth.draw_x(0, 1, 0, 1, K, "f16")
+    y = gu.run("gemv", "q1", gu.w_tensor(lb.pack("q1", codes, sc)), x, "f16", "f32", N, K)
+    gu.check(y, codes, sc, x, "f16", "config 1")
