@@ -1,26 +1,28 @@
 // Decode GEMV  Y[m][n] = sum_k X[m][k] t[n][k] s[n][k/128]  for M <= 16 tokens.
 //
-// The decode step is bound by streaming the packed weights from HBM (the
-// pages: memory bandwidth, not compute, limits token generation; aberweb.com
-// page, section 2 and summary section 3).  The kernel therefore reads every
-// weight byte exactly once with 16-byte-per-lane coalesced loads (one 1 KB
-// wave load per chunk of 4 groups x 16 rows), decodes the bits in registers
-// with one shift and one bitwise op per pair of weights (device.hpp), and
-// lets the matrix cores do the multiply-adds: a v_mfma_f32_16x16x32 takes 16
-// weight rows x 32 k as its B operand and up to 16 tokens x 32 k of x as its
-// A operand.  The sign decode happens inside the kernel; no dense weight
-// tensor exists anywhere (aberweb.com page, section 4.1).
+// Token generation is bound by streaming the packed weights from HBM
+// (aberweb.com page, section 2 and summary section 3), so the kernel reads
+// every weight byte exactly once, as 16-byte-per-lane coalesced loads (a
+// full chunk of 4 groups x 16 rows is one contiguous 1 KB wave load),
+// keeps the next unit's loads in flight while it works on the current one,
+// decodes the bits in registers with one shift and one bitwise op per pair
+// of weights (device.hpp), and lets the matrix cores do the multiply-adds:
+// a v_mfma_f32_16x16x32 takes 16 weight rows x 32 k as its B operand and up
+// to 16 tokens x 32 k of x as its A operand.  No dense weight tensor exists
+// anywhere: the signs are decoded inside the kernel (aberweb.com page,
+// section 4.1).
 //
-// Per group of 128 weights the 4 k-steps accumulate into a fresh fp32 tile,
-// which is then scaled by the group's FP16 scale in fp32 and added to the
-// running sum (products exact, one fp32 rounding per group).
+// Per group of 128 weights the 4 k-steps accumulate into a fresh fp32 tile
+// that is scaled by the group's FP16 scale in fp32 and added to the running
+// sum (exact products, one fp32 rounding per group).
 //
-// Work split: a workgroup of 8 waves stages x (up to 16 tokens) in LDS as
-// [k/8][token][8] 16-byte cells.  Waves form P = 8/S wave-rows of S waves;
-// a wave-row owns R row tiles (16R rows) at a time and its S waves split the
-// K chunks, reducing their partial sums through LDS in a fixed order
-// (deterministic).  With S = 1 and x resident in LDS every wave runs its own
-// persistent loop over row tiles.
+// Work split: a workgroup of 8 waves stages x in LDS as [k/8][token][8]
+// 16-byte cells, all of K at once when it fits (then the stage is loaded
+// once per workgroup) or S chunks at a time.  The waves form P = 8/S
+// wave-rows; a wave-row owns R row tiles (16R rows) at a time and its S
+// waves split each stage's chunks, adding their partial sums through LDS in
+// a fixed order, so results are deterministic.  All control flow that
+// decides loads, MFMAs and barriers is wave-uniform.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
@@ -39,186 +41,189 @@ struct GemvParams {
   void *Y;             // [M][N]
   int M, N, K, G;
   int tiles, chunks;
-  int S;               // waves splitting the chunks of a stage
-  int SC;              // chunks staged in LDS at once (multiple of S)
-  int n_stages;        // ceil(chunks / SC)
-  int tilesets;        // ceil(tiles / R)
+  int S;         // waves splitting the chunks of a stage
+  int SC;        // chunks per stage (multiple of S)
+  int n_stages;  // ceil(chunks / SC)
+  int tilesets;  // ceil(tiles / R)
   int y_f16;
-  // LDS byte offsets
-  int off_corr, off_x, off_part, off_red;
+  int off_corr, off_x, off_red;
 };
 
 struct LdsMap {
-  int corr, x, part, red, total;
+  int corr, x, red, total;
 };
 
-template <int FMT>
-LdsMap lds_map(int M, int S, int SC, int R) {
+// x cells hold MTS token slots (MTS = 1, 4 or 16); lanes whose token slot is
+// past MTS read a zero region as large as one chunk of cells.
+inline LdsMap lds_map(int MTS, int S, int SC, int R, int E) {
   LdsMap m;
-  int o = 16;  // zero cell
+  int o = MTS == 16 ? 0 : 64 * 16 * MTS;
   m.corr = o;
-  if (FMT == 1) o += SC * 4 * 16 * 4;
+  o += SC * 4 * 16 * 4;
   m.x = o;
-  o += M * SC * 1024;
-  m.part = o;
-  if (FMT == 1) o += SC * 64 * M * 4;
-  o = (o + 15) & ~15;
+  o += MTS * SC * 1024;
   m.red = o;
-  if (S > 1) o += kWaves * R * 4 * 64 * 4;
+  if (S > 1) o += kWaves * R * E * 64 * 4;
   m.total = o;
   return m;
 }
 
-// Stage chunks [c0, c0+nc) of x into LDS: cell (oct, m) = x[m][8*(32*c0 + oct) ..] at
-// ((oct * M) + m) * 16.  For q1 also the per-(group, token) correction
-//   corr[gs][m] = sum of x[m][k] over the group's k with k % 4 in {2, 3}
-// (the weights the q1 operand feeds as t + 1 instead of t).
-template <int FMT, bool BF>
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Stage chunks [c0, c0 + nc) of x: cell (oct, m) holds x[m][k0 + 8 oct .. + 8] at
+// byte off_x + (oct * MTS + m) * 16 (zeros past K and for m >= M).  One thread
+// per (group, token slot) also sums the group's activations at k % 4 in {2, 3}:
+// the q1 operand feeds those weights as t + 1, so minus that sum is stored in
+// corr[group][token] and seeds the group's accumulator.
+template <int FMT, bool BF, int MTS>
 __device__ void stage_x(const GemvParams &p, char *lds, int c0, int nc) {
-  const int M = p.M;
-  const int oct_total = nc * 64;
   const int k0 = c0 * 512;
   uint4 *xl = reinterpret_cast<uint4 *>(lds + p.off_x);
-  float *part = reinterpret_cast<float *>(lds + p.off_part);
-  for (int idx = threadIdx.x; idx < oct_total * M; idx += kThreads) {
-    const int oct = idx / M, m = idx - oct * M;
-    const int k = k0 + oct * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (k < p.K) v = *reinterpret_cast<const uint4 *>(p.X + (int64_t)m * p.K + k);
-    xl[oct * M + m] = v;
-    if constexpr (FMT == 1) {
-      const float a = x_to_float(uint16_t(v.y), BF) + x_to_float(uint16_t(v.y >> 16), BF);
-      const float b = x_to_float(uint16_t(v.w), BF) + x_to_float(uint16_t(v.w >> 16), BF);
-      part[oct * M + m] = a + b;
+  float *corr = reinterpret_cast<float *>(lds + p.off_corr);
+  for (int idx = threadIdx.x; idx < nc * 4 * 16; idx += kThreads) {
+    const int gs = idx >> 4, m = idx & 15;
+    const int kg = k0 + gs * 128;
+    const bool in = kg < p.K && m < p.M;
+    // Clamped address, unconditional loads, then zero what is out of range:
+    // no divergent branch around the loads.
+    const u4_t *src = reinterpret_cast<const u4_t *>(p.X + (in ? (int64_t)m * p.K + kg : 0));
+    u4_t v[16];
+#pragma unroll
+    for (int o = 0; o < 16; ++o) v[o] = src[o];
+    float c = 0.f;
+#pragma unroll
+    for (int o = 0; o < 16; ++o) {
+      const u4_t z = {0u, 0u, 0u, 0u};
+      const u4_t vv = in ? v[o] : z;
+      if (m < MTS) *reinterpret_cast<u4_t *>(xl + (gs * 16 + o) * MTS + m) = vv;
+      if constexpr (FMT == 1)
+        c += (x_to_float(uint16_t(vv.y), BF) + x_to_float(uint16_t(vv.y >> 16), BF)) +
+             (x_to_float(uint16_t(vv.w), BF) + x_to_float(uint16_t(vv.w >> 16), BF));
     }
+    corr[idx] = -c;
   }
-  if constexpr (FMT == 1) {
-    __syncthreads();
-    float *corr = reinterpret_cast<float *>(lds + p.off_corr);
-    for (int idx = threadIdx.x; idx < nc * 4 * 16; idx += kThreads) {
-      const int gs = idx >> 4, m = idx & 15;
-      float c = 0.f;
-      if (m < M)
-        for (int o = 0; o < 16; ++o) c += part[(gs * 16 + o) * M + m];
-      corr[idx] = c;
+}
+
+// Packed words and scales of R row tiles x one chunk (4 groups), for one lane.
+template <int FMT, int R>
+struct Unit {
+  static constexpr int WPU = FMT == 1 ? 4 : 8;
+  uint32_t w[R][WPU];
+  uint32_t s[R][2];  // 4 FP16 scales
+};
+
+// Loads are issued without per-lane branches (ragged tiles clamp their
+// addresses and zero the values afterwards): a divergent branch around a
+// load makes the compiler wait for every outstanding load at the join, which
+// would drain the prefetch ring.
+template <int FMT, int R>
+__device__ __forceinline__ void load_unit(const GemvParams &p, Unit<FMT, R> &u, int t0, int c, bool valid) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  constexpr int WPU = Unit<FMT, R>::WPU;
+  const int64_t unit = FMT == 1 ? 16 : 32;
+  const int Gc = uni(min(4, p.G - 4 * c));
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = uni(t0 + r);
+    if (!valid || t >= p.tiles) {  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < WPU; ++i) u.w[r][i] = 0;
+      u.s[r][0] = u.s[r][1] = 0;
+      continue;
+    }
+    const int RT = uni(min(16, p.N - 16 * t));
+    const uint8_t *blk = p.W + 16 * (int64_t)t * p.G * unit + (int64_t)RT * 4 * c * unit;
+    if (RT == 16 && Gc == 4 && (p.G & 3) == 0) {  // wave-uniform fast path
+      const u4_t v0 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk) + lane);
+      u.w[r][0] = v0.x; u.w[r][1] = v0.y; u.w[r][2] = v0.z; u.w[r][3] = v0.w;
+      if constexpr (FMT == 2) {
+        const u4_t v1 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk + 1024) + lane);
+        u.w[r][4] = v1.x; u.w[r][5] = v1.y; u.w[r][6] = v1.z; u.w[r][7] = v1.w;
+      }
+      const u2_t sv = *reinterpret_cast<const u2_t *>(p.Sc + (int64_t)(16 * t + j) * p.G + 4 * c);
+      u.s[r][0] = sv.x; u.s[r][1] = sv.y;
+    } else {
+      const bool row_ok = j < RT;
+      const int jj = min(j, RT - 1);
+      const uint32_t *base = reinterpret_cast<const uint32_t *>(blk);
+      const uint16_t *srow = p.Sc + (int64_t)(16 * t + jj) * p.G + 4 * c;
+      uint32_t h[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int gg = min(g, Gc - 1);
+        const bool ok = row_ok && g < Gc;
+        if constexpr (FMT == 1) {
+          const uint32_t w = base[(q * RT + jj) * Gc + gg];
+          u.w[r][g] = ok ? w : 0u;
+        } else {
+          const int hh = gg >> 1, Gh = min(2, Gc - 2 * hh);
+          const uint32_t *hb = base + RT * 16 * hh + ((q * RT + jj) * Gh + (gg - 2 * hh)) * 2;
+          const uint32_t w0 = hb[0], w1 = hb[1];
+          u.w[r][2 * g + 0] = ok ? w0 : 0u;
+          u.w[r][2 * g + 1] = ok ? w1 : 0u;
+        }
+        const uint32_t sv = srow[gg];
+        h[g] = ok ? sv : 0u;
+      }
+      u.s[r][0] = h[0] | (h[1] << 16);
+      u.s[r][1] = h[2] | (h[3] << 16);
     }
   }
 }
 
-// One wave: R row tiles starting at tile t0, chunk c (c_local inside the stage).
-template <int FMT, bool BF, int MT, int R>
-__device__ __forceinline__ void wave_chunk(const GemvParams &p, const char *lds, int t0, int c,
-                                           int c_local, float (&yacc)[R][4]) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15, q = lane >> 4;
-  const int Gc = min(4, p.G - 4 * c);
-  constexpr int WPG = FMT == 1 ? 1 : 2;  // lane words per group
-  uint32_t wb[R][4 * WPG];
-  uint16_t sc[R][4];
-  bool tile_ok[R];
-
-  const int64_t unit = FMT == 1 ? 16 : 32;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int t = t0 + r;
-    tile_ok[r] = t < p.tiles;
-#pragma unroll
-    for (int i = 0; i < 4 * WPG; ++i) wb[r][i] = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[r][i] = 0;
-    if (!tile_ok[r]) continue;
-    const int RT = min(16, p.N - 16 * t);
-    const int64_t blk = 16 * (int64_t)t * p.G * unit + (int64_t)RT * 4 * c * unit;
-    const int n = 16 * t + j;
-    if (RT == 16 && Gc == 4) {
-      if constexpr (FMT == 1) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(p.W + blk + 16 * lane);
-        wb[r][0] = v.x; wb[r][1] = v.y; wb[r][2] = v.z; wb[r][3] = v.w;
-      } else {
-        const uint4 v0 = *reinterpret_cast<const uint4 *>(p.W + blk + 16 * lane);
-        const uint4 v1 = *reinterpret_cast<const uint4 *>(p.W + blk + 16 * 64 + 16 * lane);
-        wb[r][0] = v0.x; wb[r][1] = v0.y; wb[r][2] = v0.z; wb[r][3] = v0.w;
-        wb[r][4] = v1.x; wb[r][5] = v1.y; wb[r][6] = v1.z; wb[r][7] = v1.w;
-      }
-    } else if (j < RT) {
-      const uint32_t *base = reinterpret_cast<const uint32_t *>(p.W + blk);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (g >= Gc) break;
-        if constexpr (FMT == 1) {
-          wb[r][g] = base[(q * RT + j) * Gc + g];
-        } else {
-          const int hh = g >> 1, Gh = min(2, Gc - 2 * hh);
-          const uint32_t *hb = base + RT * 16 * hh;
-          wb[r][2 * g + 0] = hb[((q * RT + j) * Gh + (g - 2 * hh)) * 2 + 0];
-          wb[r][2 * g + 1] = hb[((q * RT + j) * Gh + (g - 2 * hh)) * 2 + 1];
-        }
-      }
-    }
-    if (j < RT) {
-      const uint16_t *srow = p.Sc + (int64_t)n * p.G + 4 * c;
-      if (Gc == 4 && (p.G & 3) == 0) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(srow);
-        sc[r][0] = uint16_t(v.x); sc[r][1] = uint16_t(v.x >> 16);
-        sc[r][2] = uint16_t(v.y); sc[r][3] = uint16_t(v.y >> 16);
-      } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          if (g < Gc) sc[r][g] = srow[g];
-      }
-    }
-  }
-
-  // A-operand (x) addressing: lane (q, i) reads token i, k-octet 4u+q of group g.
-  const int i = j;
-  const bool xact = i < p.M;
-  const int lane_x = p.off_x + (q * p.M + i) * 16;
-  const float *corr = reinterpret_cast<const float *>(lds + p.off_corr);
-
+// x operand cells of step (g, uu) sit at a compile-time offset from the
+// lane's chunk base, so the LDS reads need no address arithmetic.
+template <int FMT, bool BF, int R, int E, int MTS>
+__device__ __forceinline__ void compute_unit(const GemvParams &p, const char *lds, const Unit<FMT, R> &u, int c_local,
+                                             int xbase, float (&yacc)[R][4]) {
+  const int q = (threadIdx.x & 63) >> 4;
+  const float *corr = reinterpret_cast<const float *>(lds + p.off_corr) + c_local * 64 + 4 * q;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    if (g >= Gc) break;
-    f4_t acc[R];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int step = ((c_local * 4 + g) * 16 + 4 * u) * p.M * 16;
-      const int addr = xact ? lane_x + step : 0;
-      const u4_t a = *reinterpret_cast<const u4_t *>(lds + addr);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (!tile_ok[r]) continue;
-        u4_t b;
-        if constexpr (FMT == 1) b = q1_operand<BF>(wb[r][g], u);
-        else b = tq2_operand(wb[r][2 * g + (u >> 1)], u);
-        acc[r] = u == 0 ? mfma16x16x32_zero<BF>(a, b) : mfma16x16x32<BF>(a, b, acc[r]);
+    // q1: the group's accumulator starts at -(sum of x fed as t + 1).
+    f4_t init = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FMT == 1) {
+      if constexpr (E == 1) {
+        init[0] = corr[g * 16];
+      } else {
+        const float4 cv = *reinterpret_cast<const float4 *>(corr + g * 16);
+        init = f4_t{cv.x, cv.y, cv.z, cv.w};
       }
     }
-    float cr[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (FMT == 1) {
-      const float4 cv = *reinterpret_cast<const float4 *>(corr + (c_local * 4 + g) * 16 + 4 * q);
-      cr[0] = cv.x; cr[1] = cv.y; cr[2] = cv.z; cr[3] = cv.w;
+    f4_t acc[R];
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      const u4_t a = *reinterpret_cast<const u4_t *>(lds + xbase + (g * 16 + 4 * uu) * MTS * 16);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        u4_t b;
+        if constexpr (FMT == 1) b = q1_operand<BF>(u.w[r][g], uu);
+        else b = tq2_operand(u.w[r][2 * g + (uu >> 1)], uu);
+        if constexpr (FMT == 1) acc[r] = mfma16x16x32<BF>(a, b, uu == 0 ? init : acc[r]);
+        else acc[r] = uu == 0 ? mfma16x16x32_zero<BF>(a, b) : mfma16x16x32<BF>(a, b, acc[r]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (!tile_ok[r]) continue;
-      const float s = half_to_float(sc[r][g]);
+      const float s = half_to_float(uint16_t(u.s[r][g >> 1] >> (16 * (g & 1))));
 #pragma unroll
-      for (int e = 0; e < (MT == 1 ? 1 : 4); ++e) yacc[r][e] = fmaf(s, acc[r][e] - cr[e], yacc[r][e]);
+      for (int e = 0; e < E; ++e) yacc[r][e] = fmaf(s, acc[r][e], yacc[r][e]);
     }
   }
 }
 
-template <int FMT, int MT, int R>
-__device__ __forceinline__ void store_tileset(const GemvParams &p, int t0, const float (&yacc)[R][4]) {
+template <int FMT, int R, int E>
+__device__ __forceinline__ void store_tiles(const GemvParams &p, int t0, const float (&yacc)[R][4]) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, q = lane >> 4;
   const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int n = 16 * (t0 + r) + j;
-    if (t0 + r >= p.tiles || n >= p.N) continue;
+    if (n >= p.N) continue;
 #pragma unroll
-    for (int e = 0; e < (MT == 1 ? 1 : 4); ++e) {
+    for (int e = 0; e < E; ++e) {
       const int m = 4 * q + e;
       if (m >= p.M) continue;
       const float v = yacc[r][e] * mul;
@@ -228,75 +233,139 @@ __device__ __forceinline__ void store_tileset(const GemvParams &p, int t0, const
   }
 }
 
-template <int FMT, bool BF, int MT, int R>
-__global__ void __launch_bounds__(kThreads) gemv_kernel(GemvParams p) {
-  extern __shared__ __align__(16) char lds[];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 4) reinterpret_cast<uint32_t *>(lds)[threadIdx.x] = 0;  // zero cell
+// Position of a wave in its flat sequence of units: tile set iteration it,
+// stage st, slot kl inside the stage.  Advanced incrementally (no divisions).
+struct Cursor {
+  int it, st, kl;
+};
 
-  const int S = p.S, P = kWaves / S;
-  const int pr = wave / S, s = wave - pr * S;
-
-  if (S == 1 && p.n_stages == 1) {
-    // x resident; every wave runs its own loop over tile sets.
-    stage_x<FMT, BF>(p, lds, 0, p.chunks);
-    __syncthreads();
-    for (int ts = blockIdx.x * kWaves + wave; ts < p.tilesets; ts += gridDim.x * kWaves) {
-      float yacc[R][4] = {};
-      for (int c = 0; c < p.chunks; ++c) wave_chunk<FMT, BF, MT, R>(p, lds, ts * R, c, c, yacc);
-      store_tileset<FMT, MT, R>(p, ts * R, yacc);
-    }
-    return;
-  }
-
-  const int rowblocks = (p.tilesets + P - 1) / P;
-  bool staged_once = false;
-  for (int rb = blockIdx.x; rb < rowblocks; rb += gridDim.x) {
-    const int ts = rb * P + pr;
-    const bool ts_ok = ts < p.tilesets;
-    float yacc[R][4] = {};
-    for (int st = 0; st < p.n_stages; ++st) {
-      const int c0 = st * p.SC;
-      const int nc = min(p.SC, p.chunks - c0);
-      if (p.n_stages > 1 || !staged_once) {
-        __syncthreads();
-        stage_x<FMT, BF>(p, lds, c0, nc);
-        __syncthreads();
-        staged_once = true;
-      }
-      if (ts_ok)
-        for (int cl = s; cl < nc; cl += S) wave_chunk<FMT, BF, MT, R>(p, lds, ts * R, c0 + cl, cl, yacc);
-    }
-    if (S == 1) {
-      if (ts_ok) store_tileset<FMT, MT, R>(p, ts * R, yacc);
-    } else {
-      float *red = reinterpret_cast<float *>(lds + p.off_red);
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red[((wave * R + r) * 4 + e) * 64 + lane] = yacc[r][e];
-      __syncthreads();
-      if (s == 0 && ts_ok) {
-        float tot[R][4];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float v = 0.f;
-            for (int s2 = 0; s2 < S; ++s2) v += red[(((pr * S + s2) * R + r) * 4 + e) * 64 + lane];
-            tot[r][e] = v;
-          }
-        store_tileset<FMT, MT, R>(p, ts * R, tot);
-      }
-      __syncthreads();
+__device__ __forceinline__ void advance(Cursor &c, int U, int n_stages) {
+  if (++c.kl == U) {
+    c.kl = 0;
+    if (++c.st == n_stages) {
+      c.st = 0;
+      ++c.it;
     }
   }
 }
 
-template <int FMT, bool BF, int MT, int R>
-hipError_t launch_t(const LaunchArgs &a) {
-  GemvParams p{};
+// Each wave walks a flat sequence of units (tile set, chunk) with a ring of
+// D units in flight: the loads of unit i + D - 1 are issued before unit i is
+// computed, across chunk, stage and tile-set boundaries.
+template <int FMT, bool BF, int MT, int R, int D>
+__global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
+  constexpr int E = MT == 1 ? 1 : 4;     // accumulator elements that can hold a token
+  constexpr int MTS = MT;                // token slots per x cell
+  extern __shared__ __align__(16) char lds[];
+  const int wave = uni(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  if constexpr (MTS < 16) {
+    for (int i = threadIdx.x; i < 64 * MTS; i += kThreads) reinterpret_cast<uint4 *>(lds)[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  const int S = uni(p.S), P = kWaves / S;
+  const int pr = uni(wave / S), s = uni(wave - pr * S);
+  const int U = uni(p.SC / S);          // unit slots per wave per stage
+  const int KT = uni(p.n_stages * U);   // unit slots per wave per tile set
+  const bool restage = p.n_stages > 1;
+  const bool lockstep = restage || S > 1;
+  const int rows_total = gridDim.x * P;  // wave-rows in the grid
+  // Tile set of iteration it: consecutive wave-rows of one workgroup are
+  // gridDim.x apart, so extra tile sets spread over all CUs.
+  const int my_row = pr * gridDim.x + blockIdx.x;
+  const int iters = lockstep ? (p.tilesets + rows_total - 1) / rows_total
+                             : (p.tilesets - my_row + rows_total - 1) / rows_total;
+  const int total = uni(iters * KT);
+  // Token slots past MTS read the zero region; slots in [M, MTS) hold zeros.
+  const bool xact = j < MTS;
+
+  auto tile0 = [&](const Cursor &c) { return (c.it * rows_total + my_row) * R; };
+  auto chunk = [&](const Cursor &c) { return c.st * p.SC + s + c.kl * S; };
+  auto is_valid = [&](const Cursor &c) {
+    return c.it * rows_total + my_row < p.tilesets && chunk(c) < p.chunks;
+  };
+
+  // First D - 1 units' loads go out before x is staged.
+  float yacc[R][4];
+  Unit<FMT, R> ring[D];
+  Cursor ld = {0, 0, 0};
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    load_unit<FMT, R>(p, ring[d], uni(tile0(ld)), uni(chunk(ld)), d < total && is_valid(ld));
+    advance(ld, U, p.n_stages);
+  }
+  if (!restage) {
+    stage_x<FMT, BF, MTS>(p, lds, 0, p.chunks);
+    __syncthreads();
+  }
+
+  Cursor cu = {0, 0, 0};
+  for (int i0 = 0; i0 < total; i0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = i0 + d;
+      if (i >= total) break;
+      load_unit<FMT, R>(p, ring[(d + D - 1) % D], uni(tile0(ld)), uni(chunk(ld)), i + D - 1 < total && is_valid(ld));
+      advance(ld, U, p.n_stages);
+
+      const int t0 = uni(tile0(cu));
+      const int k_first = cu.st == 0 && cu.kl == 0;
+      const int k_last = cu.st == p.n_stages - 1 && cu.kl == U - 1;
+      if (k_first) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yacc[r][e] = 0.f;
+      }
+      if (restage && cu.kl == 0) {
+        __syncthreads();
+        const int c0 = cu.st * p.SC;
+        stage_x<FMT, BF, MTS>(p, lds, c0, min(p.SC, p.chunks - c0));
+        __syncthreads();
+      }
+      if (is_valid(cu)) {
+        const int c_local = s + cu.kl * S;
+        const int xbase = xact ? p.off_x + (c_local * 64 * MTS + q * MTS + j) * 16 : 0;
+        compute_unit<FMT, BF, R, E, MTS>(p, lds, ring[d], c_local, xbase, yacc);
+      }
+      if (k_last) {
+        const bool ts_ok = t0 < p.tiles;
+        if (S == 1) {
+          if (ts_ok) store_tiles<FMT, R, E>(p, t0, yacc);
+        } else {
+          float *red = reinterpret_cast<float *>(lds + p.off_red);
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e) red[((wave * R + r) * E + e) * 64 + lane] = yacc[r][e];
+          __syncthreads();
+          if (s == 0 && ts_ok) {
+            float tot[R][4];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+              for (int e = 0; e < E; ++e) {
+                float v = 0.f;
+                for (int s2 = 0; s2 < S; ++s2) v += red[(((pr * S + s2) * R + r) * E + e) * 64 + lane];
+                tot[r][e] = v;
+              }
+            store_tiles<FMT, R, E>(p, t0, tot);
+          }
+          __syncthreads();
+        }
+      }
+      advance(cu, U, p.n_stages);
+    }
+  }
+}
+
+// Host-side choice of (R, S): the smallest per-wave work (the makespan:
+// tile sets per wave-row x R x chunks per wave), then fewer barriers.
+template <int FMT, bool BF, int MT, int R, int D>
+double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) {
+  constexpr int E = MT == 1 ? 1 : 4;
+  p = GemvParams{};
   const int64_t G = a.K / kGroup;
   p.W = a.W;
   p.Sc = reinterpret_cast<const uint16_t *>(a.W + plane_a_bytes(a.fmt, a.N, a.K));
@@ -307,35 +376,71 @@ hipError_t launch_t(const LaunchArgs &a) {
   p.chunks = int((G + 3) / 4);
   p.tilesets = (p.tiles + R - 1) / R;
   p.y_f16 = a.y_f16;
+  const int cus = num_cus();
+  const void *kern = reinterpret_cast<const void *>(&gemv_kernel<FMT, BF, MT, R, D>);
 
-  // K split: enough (tile set, split) pairs to fill 256 CUs x 8 waves.
-  int S = 1;
-  while (S < 8 && (int64_t)p.tilesets * S < 2048 && S * 2 <= p.chunks && MT * S * 2 <= 32) S *= 2;
-  // Chunks staged per stage: all of them if the LDS map fits in 64 KB, else
-  // the largest multiple of S that does.
-  int SC = (p.chunks + S - 1) / S * S;
-  while (SC > S && lds_map<FMT>(p.M, S, SC, R).total > 64 * 1024) SC -= S;
-  p.S = S;
-  p.SC = SC;
-  p.n_stages = (p.chunks + SC - 1) / SC;
-  const LdsMap m = lds_map<FMT>(p.M, S, SC, R);
-  p.off_corr = m.corr; p.off_x = m.x; p.off_part = m.part; p.off_red = m.red;
+  double best = 1e300;
+  GemvParams bp = p;
+  int bgrid = 1, blds = 0;
+  for (int S = 1; S <= 8; S *= 2) {
+    if (S > 1 && S > p.chunks) break;
+    GemvParams q = p;
+    // Stage all chunks when the LDS map fits in 64 KB, else stream stages of
+    // as many chunks as fit in 32 KB of x.
+    int SC = (p.chunks + S - 1) / S * S;
+    if (lds_map(MT, S, SC, R, E).total > 64 * 1024) {
+      if (MT * S * 1024 > 32 * 1024) continue;
+      SC = S;
+      while (SC + S <= p.chunks && MT * (SC + S) * 1024 <= 32 * 1024) SC += S;
+    }
+    q.S = S;
+    q.SC = SC;
+    q.n_stages = (p.chunks + SC - 1) / SC;
+    const LdsMap m = lds_map(MT, S, SC, R, E);
+    q.off_corr = m.corr; q.off_x = m.x; q.off_red = m.red;
+    const int P = kWaves / S;
+    const int per_cu = resident_blocks(kern, kThreads, m.total);
+    const int g = max(1, min((q.tilesets + P - 1) / P, cus * per_cu));
+    const int64_t rows = (int64_t)g * P;
+    // Makespan in units of (tile, chunk) work per wave, with a small charge
+    // for workgroup barriers (K split or streamed stages).
+    const double units = double((q.tilesets + rows - 1) / rows) * R * ((p.chunks + S - 1) / S);
+    const double cost = units * ((S > 1 || q.n_stages > 1) ? 1.05 : 1.0);
+    if (cost < best) {
+      best = cost;
+      bp = q;
+      bgrid = g;
+      blds = m.total;
+    }
+  }
+  p = bp;
+  grid = bgrid;
+  lds_bytes = blds;
+  // R = 1 reads the x operand from LDS once per MFMA instead of once per two.
+  return best * (R == 1 ? 1.1 : 1.0);
+}
 
-  const int P = kWaves / S;
-  int grid;
-  if (S == 1 && p.n_stages == 1) grid = (p.tilesets + kWaves - 1) / kWaves;
-  else grid = (p.tilesets + P - 1) / P;
-  const int per_cu = m.total <= 40 * 1024 ? 3 : (m.total <= 64 * 1024 ? 2 : 1);
-  grid = max(1, min(grid, 256 * per_cu));
-  hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, R>), dim3(grid), dim3(kThreads), m.total, a.stream, p);
+template <int FMT, bool BF, int MT>
+hipError_t launch_mt(const LaunchArgs &a) {
+  GemvParams p1, p2;
+  int g1, g2, l1, l2;
+  // Ring depth: three units in flight for q1 (1 KB per tile each), two for
+  // tq2 (2 KB per tile each) so that four waves per SIMD fit in registers.
+  constexpr int D = FMT == 1 ? 3 : 2;
+  const double c1 = make_plan<FMT, BF, MT, 1, D>(a, p1, g1, l1);
+  const double c2 = make_plan<FMT, BF, MT, 2, D>(a, p2, g2, l2);
+  if (c1 < c2)
+    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, 1, D>), dim3(g1), dim3(kThreads), l1, a.stream, p1);
+  else
+    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, 2, D>), dim3(g2), dim3(kThreads), l2, a.stream, p2);
   return hipGetLastError();
 }
 
 template <int FMT, bool BF>
-hipError_t launch_mt(const LaunchArgs &a) {
-  if (a.M <= 1) return launch_t<FMT, BF, 1, 2>(a);
-  if (a.M <= 4) return launch_t<FMT, BF, 4, 2>(a);
-  return launch_t<FMT, BF, 16, 2>(a);
+hipError_t launch_fmt(const LaunchArgs &a) {
+  if (a.M <= 1) return launch_mt<FMT, BF, 1>(a);
+  if (a.M <= 4) return launch_mt<FMT, BF, 4>(a);
+  return launch_mt<FMT, BF, 16>(a);
 }
 
 }  // namespace
@@ -348,8 +453,8 @@ hipError_t launch_gemv(const LaunchArgs &a) {
     b.X = a.X + m0 * a.K;
     b.Y = static_cast<char *>(a.Y) + m0 * a.N * (a.y_f16 ? 2 : 4);
     hipError_t e;
-    if (a.fmt == 1) e = a.x_bf16 ? launch_mt<1, true>(b) : launch_mt<1, false>(b);
-    else e = a.x_bf16 ? launch_mt<2, true>(b) : launch_mt<2, false>(b);
+    if (a.fmt == 1) e = a.x_bf16 ? launch_fmt<1, true>(b) : launch_fmt<1, false>(b);
+    else e = a.x_bf16 ? launch_fmt<2, true>(b) : launch_fmt<2, false>(b);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -21,4 +21,10 @@ hipError_t launch_gemv(const LaunchArgs &a);
 hipError_t launch_gemm(const LaunchArgs &a);
 hipError_t launch_fill_zero(void *Y, int64_t bytes, hipStream_t stream);
 
+// Compute units of the current device (cached per device, thread-safe).
+int num_cus();
+// Workgroups of `kernel` (block `threads`, `lds` dynamic LDS bytes) that one
+// compute unit holds at once; cached per (kernel, threads, lds, device).
+int resident_blocks(const void *kernel, int threads, int lds);
+
 }  // namespace lowbit
