@@ -48,31 +48,68 @@ __device__ __forceinline__ uint16_t load_scale(const GemmParams &p, int n, int g
   return uint16_t(b[0] | (uint16_t(b[1]) << 8));
 }
 
-// One weight group g: stage the activation tile, then 4 k-steps of MFMAs
-// into a fresh tile, then acc += s * tile.  Bop(u, nb) returns the B operand
-// (16 weight rows x 32 k) of n-block nb for k-step u.
-template <bool BF, class Bop>
-__device__ __forceinline__ void group_step(const GemmParams &p, uint16_t *xs, int g, int m0, int n0,
-                                           const int (&RT)[4], f4_t (&acc)[4][4], Bop bop) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int j = lane & 15, q = lane >> 4;
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < kBM * 16; idx += kThreads) {
-    const int r = idx >> 4, c16 = idx & 15;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (m0 + r < p.M) v = *reinterpret_cast<const uint4 *>(p.X + (int64_t)(m0 + r) * p.K + 128 * g + 8 * c16);
-    *reinterpret_cast<uint4 *>(xs + r * kXStride + 8 * c16) = v;
-  }
-  float sc[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int n = n0 + wn * 64 + 16 * nb + j;
-    sc[nb] = (j < RT[nb]) ? half_to_float(load_scale(p, n, g)) : 0.f;
-  }
-  __syncthreads();
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// The activation tile of one group (128 rows x 128 k) as 16-byte cells: each
+// thread holds 8 of the tile's 2048 cells in registers between the global
+// load and the LDS store, so the next group's loads overlap this group's MFMAs.
+struct XRegs {
+  u4_t v[8];
+};
+
+__device__ __forceinline__ void x_load(const GemmParams &p, XRegs &r, int m0, int g) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    const int row = idx >> 4, c16 = idx & 15;
+    const bool in = m0 + row < p.M && g < p.G;
+    const u4_t *src = reinterpret_cast<const u4_t *>(p.X + (in ? (int64_t)(m0 + row) * p.K + 128 * g + 8 * c16 : 0));
+    const u4_t v = *src;
+    const u4_t z = {0u, 0u, 0u, 0u};
+    r.v[i] = in ? v : z;
+  }
+}
+
+// Store the cells; for q1 also minus the sum over k % 4 in {2, 3} of every row
+// (16 consecutive lanes hold one row's 16 cells).
+template <int FMT, bool BF>
+__device__ __forceinline__ void x_store(const XRegs &r, uint16_t *xs, float *corr) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    const int row = idx >> 4, c16 = idx & 15;
+    *reinterpret_cast<u4_t *>(xs + row * kXStride + 8 * c16) = r.v[i];
+    if constexpr (FMT == 1) {
+      const u4_t v = r.v[i];
+      float c = (x_to_float(uint16_t(v.y), BF) + x_to_float(uint16_t(v.y >> 16), BF)) +
+                (x_to_float(uint16_t(v.w), BF) + x_to_float(uint16_t(v.w >> 16), BF));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) c += __shfl_xor(c, o, 16);
+      if (c16 == 0) corr[row] = -c;
+    }
+  }
+}
+
+// 4 k-steps of MFMAs for one group from LDS tile xs into fresh tiles (q1:
+// seeded with -corr of each row), then acc += s * tile.  Bop(u, nb) returns
+// the B operand (16 weight rows x 32 k) of n-block nb for k-step u.
+template <int FMT, bool BF, class Bop>
+__device__ __forceinline__ void group_mma(const uint16_t *xs, const float *corr, const float (&sc)[4],
+                                          f4_t (&acc)[4][4], Bop bop) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1;
+  const int j = lane & 15, q = lane >> 4;
   f4_t cg[4][4];
+  f4_t init[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    if constexpr (FMT == 1) {
+      const float4 c = *reinterpret_cast<const float4 *>(corr + wm * 64 + 16 * mb + 4 * q);
+      init[mb] = f4_t{c.x, c.y, c.z, c.w};
+    } else {
+      init[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     u4_t A[4], B[4];
@@ -84,8 +121,7 @@ __device__ __forceinline__ void group_step(const GemmParams &p, uint16_t *xs, in
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        cg[mb][nb] = u == 0 ? mfma16x16x32_zero<BF>(A[mb], B[nb]) : mfma16x16x32<BF>(A[mb], B[nb], cg[mb][nb]);
+      for (int nb = 0; nb < 4; ++nb) cg[mb][nb] = mfma16x16x32<BF>(A[mb], B[nb], u == 0 ? init[mb] : cg[mb][nb]);
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -95,16 +131,79 @@ __device__ __forceinline__ void group_step(const GemmParams &p, uint16_t *xs, in
       for (int e = 0; e < 4; ++e) acc[mb][nb][e] = fmaf(sc[nb], cg[mb][nb][e], acc[mb][nb][e]);
 }
 
+// Weight words of one chunk (4 groups) for this lane's 4 n-blocks, and their scales.
+template <int FMT>
+struct WChunk {
+  uint32_t w[4][FMT == 1 ? 4 : 8];
+  uint32_t s[4][2];
+};
+
+template <int FMT>
+__device__ __forceinline__ void w_load(const GemmParams &p, WChunk<FMT> &wc, const int (&tileT)[4],
+                                       const int (&RT)[4], int c) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  constexpr int WPU = FMT == 1 ? 4 : 8;
+  const int64_t unit = FMT == 1 ? 16 : 32;
+  const int Gc = uni(min(4, p.G - 4 * c));
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int R = RT[nb];
+    if (R == 0 || c >= (p.G + 3) / 4) {
+#pragma unroll
+      for (int i = 0; i < WPU; ++i) wc.w[nb][i] = 0;
+      wc.s[nb][0] = wc.s[nb][1] = 0;
+      continue;
+    }
+    const uint8_t *blk = p.W + 16 * (int64_t)tileT[nb] * p.G * unit + (int64_t)R * 4 * c * unit;
+    if (R == 16 && Gc == 4 && (p.G & 3) == 0) {
+      const u4_t v0 = *(reinterpret_cast<const u4_t *>(blk) + lane);
+      wc.w[nb][0] = v0.x; wc.w[nb][1] = v0.y; wc.w[nb][2] = v0.z; wc.w[nb][3] = v0.w;
+      if constexpr (FMT == 2) {
+        const u4_t v1 = *(reinterpret_cast<const u4_t *>(blk + 1024) + lane);
+        wc.w[nb][4] = v1.x; wc.w[nb][5] = v1.y; wc.w[nb][6] = v1.z; wc.w[nb][7] = v1.w;
+      }
+      const u2_t sv = *reinterpret_cast<const u2_t *>(p.Sc + ((int64_t)(16 * tileT[nb] + j) * p.G + 4 * c) * 2);
+      wc.s[nb][0] = sv.x; wc.s[nb][1] = sv.y;
+    } else {
+      const bool row_ok = j < R;
+      const int jj = min(j, R - 1);
+      const uint32_t *base = reinterpret_cast<const uint32_t *>(blk);
+      uint32_t h[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int g2 = min(gg, Gc - 1);
+        const bool ok = row_ok && gg < Gc;
+        if constexpr (FMT == 1) {
+          const uint32_t w = base[(q * R + jj) * Gc + g2];
+          wc.w[nb][gg] = ok ? w : 0u;
+        } else {
+          const int hh = g2 >> 1, Gh = min(2, Gc - 2 * hh);
+          const uint32_t *hb = base + R * 16 * hh + ((q * R + jj) * Gh + (g2 - 2 * hh)) * 2;
+          const uint32_t w0 = hb[0], w1 = hb[1];
+          wc.w[nb][2 * gg + 0] = ok ? w0 : 0u;
+          wc.w[nb][2 * gg + 1] = ok ? w1 : 0u;
+        }
+        const uint32_t sv = load_scale(p, 16 * tileT[nb] + jj, 4 * c + g2);
+        h[gg] = ok ? sv : 0u;
+      }
+      wc.s[nb][0] = h[0] | (h[1] << 16);
+      wc.s[nb][1] = h[2] | (h[3] << 16);
+    }
+  }
+}
+
 template <int FMT, bool BF>
 __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
-  __shared__ __align__(16) uint16_t xs[kBM * kXStride];
+  __shared__ __align__(16) uint16_t xs[2][kBM * kXStride];
+  __shared__ __align__(16) float corr[2][kBM];
   __shared__ uint16_t lut[256];
 
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
   const int m0 = tm * kBM, n0 = tn * kBN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wn = wave & 1;
   const int j = lane & 15, q = lane >> 4;
 
   if constexpr (FMT == 3) {
@@ -121,13 +220,13 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
     }
   }
 
-  // Row tiles (16 rows) of this wave's 4 n-blocks.
+  // Row tiles (16 rows) of this wave's 4 n-blocks (wave-uniform).
   int tileT[4], RT[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int n = n0 + wn * 64 + 16 * nb;
-    tileT[nb] = n / 16;
-    RT[nb] = n < p.N ? min(16, p.N - n) : 0;
+    tileT[nb] = uni(n / 16);
+    RT[nb] = uni(n < p.N ? min(16, p.N - n) : 0);
   }
 
   f4_t acc[4][4];
@@ -136,116 +235,118 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
 
+  XRegs xr;
+  x_load(p, xr, m0, 0);
+  x_store<FMT, BF>(xr, xs[0], corr[0]);
+  __syncthreads();
+
   if constexpr (FMT == 1 || FMT == 2) {
-    const int64_t unit = FMT == 1 ? 16 : 32;
     const int chunks = (p.G + 3) / 4;
+    WChunk<FMT> wa, wb;
+    w_load<FMT>(p, wa, tileT, RT, 0);
     for (int c = 0; c < chunks; ++c) {
-      const int Gc = min(4, p.G - 4 * c);
-      uint32_t wq[4][8];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) wq[nb][w] = 0;
-        if (RT[nb] == 0) continue;
-        const int64_t blk = 16 * (int64_t)tileT[nb] * p.G * unit + (int64_t)RT[nb] * 4 * c * unit;
-        if (RT[nb] == 16 && Gc == 4) {
-          const uint4 v0 = *reinterpret_cast<const uint4 *>(p.W + blk + 16 * lane);
-          wq[nb][0] = v0.x; wq[nb][1] = v0.y; wq[nb][2] = v0.z; wq[nb][3] = v0.w;
-          if constexpr (FMT == 2) {
-            const uint4 v1 = *reinterpret_cast<const uint4 *>(p.W + blk + 1024 + 16 * lane);
-            wq[nb][4] = v1.x; wq[nb][5] = v1.y; wq[nb][6] = v1.z; wq[nb][7] = v1.w;
-          }
-        } else if (j < RT[nb]) {
-          const uint32_t *base = reinterpret_cast<const uint32_t *>(p.W + blk);
-          const int R = RT[nb];
-#pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            if (gg >= Gc) break;
-            if constexpr (FMT == 1) {
-              wq[nb][gg] = base[(q * R + j) * Gc + gg];
-            } else {
-              const int hh = gg >> 1, Gh = min(2, Gc - 2 * hh);
-              const uint32_t *hb = base + R * 16 * hh;
-              wq[nb][2 * gg + 0] = hb[((q * R + j) * Gh + (gg - 2 * hh)) * 2 + 0];
-              wq[nb][2 * gg + 1] = hb[((q * R + j) * Gh + (gg - 2 * hh)) * 2 + 1];
-            }
-          }
-        }
-      }
+      w_load<FMT>(p, wb, tileT, RT, c + 1);  // next chunk in flight
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
-        if (gi >= Gc) break;
-        group_step<BF>(p, xs, 4 * c + gi, m0, n0, RT, acc, [&](int u, int nb) -> u4_t {
-          if constexpr (FMT == 1) return q1_operand_pm1<BF>(wq[nb][gi], u);
-          else return tq2_operand(wq[nb][2 * gi + (u >> 1)], u);
+        const int g = 4 * c + gi;
+        if (g >= p.G) break;
+        const int buf = g & 1;
+        if (g + 1 < p.G) x_load(p, xr, m0, g + 1);
+        float sc[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) sc[nb] = half_to_float(uint16_t(wa.s[nb][gi >> 1] >> (16 * (gi & 1))));
+        group_mma<FMT, BF>(xs[buf], corr[buf], sc, acc, [&](int u, int nb) -> u4_t {
+          if constexpr (FMT == 1) return q1_operand<BF>(wa.w[nb][gi], u);
+          else return tq2_operand(wa.w[nb][2 * gi + (u >> 1)], u);
         });
+        if (g + 1 < p.G) x_store<FMT, BF>(xr, xs[buf ^ 1], corr[buf ^ 1]);
+        __syncthreads();
       }
+      wa = wb;
     }
   } else {
-    for (int seg = 0; seg < p.s_full; ++seg) {
-      __syncthreads();  // the table is built before its first use
+    for (int seg = 0; seg * 5 < p.G; ++seg) {
+      const bool full = seg < p.s_full;
       uint32_t d5[4][16];
+      if (full) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-        if (j < RT[nb]) {
+        for (int nb = 0; nb < 4; ++nb) {
           const int R = RT[nb];
+          const bool row_ok = j < R;
+          const int jj = min(j, max(R - 1, 0));
           const uint8_t *sb = p.W + 16 * (int64_t)tileT[nb] * p.rowbytes + (int64_t)R * 128 * seg;
-          v0 = *reinterpret_cast<const uint4 *>(sb + (q * R + j) * 16);
-          v1 = *reinterpret_cast<const uint4 *>(sb + R * 64 + (q * R + j) * 16);
-        }
-        const uint32_t wds[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int pr = 0; pr < 4; ++pr) {
-            const int w0 = 8 * u + 2 * pr;  // lane byte of weight e = 2pr of step u
-            const uint32_t b0 = (wds[w0 >> 2] >> (8 * (w0 & 3))) & 0xFF;
-            const uint32_t b1 = (wds[(w0 + 1) >> 2] >> (8 * ((w0 + 1) & 3))) & 0xFF;
-            d5[nb][u * 4 + pr] = uint32_t(lut[b0]) | (uint32_t(lut[b1]) << 16);
+          u4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+          if (R > 0) {
+            v0 = *reinterpret_cast<const u4_t *>(sb + (q * R + jj) * 16);
+            v1 = *reinterpret_cast<const u4_t *>(sb + R * 64 + (q * R + jj) * 16);
           }
+          const uint32_t wds[8] = {row_ok ? v0.x : 0u, row_ok ? v0.y : 0u, row_ok ? v0.z : 0u, row_ok ? v0.w : 0u,
+                                   row_ok ? v1.x : 0u, row_ok ? v1.y : 0u, row_ok ? v1.z : 0u, row_ok ? v1.w : 0u};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+              const int w0 = 8 * u + 2 * pr;  // lane byte of weight e = 2pr of step u
+              const uint32_t b0 = (wds[w0 >> 2] >> (8 * (w0 & 3))) & 0xFF;
+              const uint32_t b1 = (wds[(w0 + 1) >> 2] >> (8 * ((w0 + 1) & 3))) & 0xFF;
+              d5[nb][u * 4 + pr] = uint32_t(lut[b0]) | (uint32_t(lut[b1]) << 16);
+            }
+        }
       }
+      for (int gs = 0; gs < 5; ++gs) {
+        const int g = 5 * seg + gs;
+        if (g >= p.G) break;
+        const int buf = g & 1;
+        if (g + 1 < p.G) x_load(p, xr, m0, g + 1);
+        float sc[4];
 #pragma unroll
-      for (int gs = 0; gs < 5; ++gs)
-        group_step<BF>(p, xs, 5 * seg + gs, m0, n0, RT, acc, [&](int u, int nb) -> u4_t {
-          u4_t b;
-          b.x = tq5_pair(d5[nb][u * 4 + 0], gs);
-          b.y = tq5_pair(d5[nb][u * 4 + 1], gs);
-          b.z = tq5_pair(d5[nb][u * 4 + 2], gs);
-          b.w = tq5_pair(d5[nb][u * 4 + 3], gs);
-          return b;
-        });
-    }
-    // Tail segment (K mod 640 trits), row-major bytes: offset kt -> byte kt % B, digit kt / B.
-    for (int g = 5 * p.s_full; g < p.G; ++g) {
-      group_step<BF>(p, xs, g, m0, n0, RT, acc, [&](int u, int nb) -> u4_t {
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          h[e] = 0;
-          if (j < RT[nb]) {
-            const int R = RT[nb];
-            const int kt = 128 * (g - 5 * p.s_full) + 32 * u + 8 * q + e;
-            const int b = kt % p.b_tail, dig = kt / p.b_tail;
-            const uint8_t *tb =
-                p.W + 16 * (int64_t)tileT[nb] * p.rowbytes + (int64_t)R * 128 * p.s_full + (int64_t)j * p.b_tail;
-            int v = tb[b];
-            for (int t = 0; t < dig; ++t) v /= 3;
-            const int d = v % 3;
-            h[e] = d == 1 ? 0u : (d == 2 ? 0x4000u : 0xC000u);
-          }
+        for (int nb = 0; nb < 4; ++nb) {
+          const int n = 16 * tileT[nb] + min(j, max(RT[nb] - 1, 0));
+          const float sv = RT[nb] > 0 ? half_to_float(load_scale(p, n, g)) : 0.f;
+          sc[nb] = j < RT[nb] ? sv : 0.f;
         }
-        u4_t b;
-        b.x = h[0] | (h[1] << 16);
-        b.y = h[2] | (h[3] << 16);
-        b.z = h[4] | (h[5] << 16);
-        b.w = h[6] | (h[7] << 16);
-        return b;
-      });
+        if (full) {
+          group_mma<FMT, BF>(xs[buf], corr[buf], sc, acc, [&](int u, int nb) -> u4_t {
+            u4_t b;
+            b.x = tq5_pair(d5[nb][u * 4 + 0], gs);
+            b.y = tq5_pair(d5[nb][u * 4 + 1], gs);
+            b.z = tq5_pair(d5[nb][u * 4 + 2], gs);
+            b.w = tq5_pair(d5[nb][u * 4 + 3], gs);
+            return b;
+          });
+        } else {
+          // Tail segment, row-major bytes: offset kt -> byte kt % B, digit kt / B.
+          group_mma<FMT, BF>(xs[buf], corr[buf], sc, acc, [&](int u, int nb) -> u4_t {
+            uint32_t h[8];
+            const int R = RT[nb];
+            const int jj = min(j, max(R - 1, 0));
+            const uint8_t *tb =
+                p.W + 16 * (int64_t)tileT[nb] * p.rowbytes + (int64_t)R * 128 * p.s_full + (int64_t)jj * p.b_tail;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int kt = 128 * (g - 5 * p.s_full) + 32 * u + 8 * q + e;
+              const int b = kt % p.b_tail, dig = kt / p.b_tail;
+              int v = R > 0 ? tb[b] : 121;
+              for (int t = 0; t < dig; ++t) v /= 3;
+              const int d = v % 3;
+              h[e] = (j >= R || d == 1) ? 0u : (d == 2 ? 0x4000u : 0xC000u);
+            }
+            u4_t b;
+            b.x = h[0] | (h[1] << 16);
+            b.y = h[2] | (h[3] << 16);
+            b.z = h[4] | (h[5] << 16);
+            b.w = h[6] | (h[7] << 16);
+            return b;
+          });
+        }
+        if (g + 1 < p.G) x_store<FMT, BF>(xr, xs[buf ^ 1], corr[buf ^ 1]);
+        __syncthreads();
+      }
     }
   }
 
   const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
+  const int wm = wave >> 1;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll

@@ -80,27 +80,34 @@ __device__ void stage_x(const GemvParams &p, char *lds, int c0, int nc) {
   const int k0 = c0 * 512;
   uint4 *xl = reinterpret_cast<uint4 *>(lds + p.off_x);
   float *corr = reinterpret_cast<float *>(lds + p.off_corr);
-  for (int idx = threadIdx.x; idx < nc * 4 * 16; idx += kThreads) {
-    const int gs = idx >> 4, m = idx & 15;
-    const int kg = k0 + gs * 128;
-    const bool in = kg < p.K && m < p.M;
-    // Clamped address, unconditional loads, then zero what is out of range:
-    // no divergent branch around the loads.
-    const u4_t *src = reinterpret_cast<const u4_t *>(p.X + (in ? (int64_t)m * p.K + kg : 0));
-    u4_t v[16];
+  // One thread per (token slot, k-octet); the 16 octets of a group sit in 16
+  // consecutive lanes, which add up the group's correction by shuffles.
+  const int cells = MTS * nc * 64;
+  for (int base = 0; base < cells; base += kThreads) {
+    const int idx = base + threadIdx.x;
+    const int m = idx / (nc * 64), oct = idx - m * (nc * 64);
+    const int k = k0 + oct * 8;
+    const bool live = idx < cells;
+    const bool in = live && k < p.K && m < p.M;
+    const u4_t *src = reinterpret_cast<const u4_t *>(p.X + (in ? (int64_t)m * p.K + k : 0));
+    u4_t v = *src;
+    const u4_t z = {0u, 0u, 0u, 0u};
+    v = in ? v : z;
+    if (live) *reinterpret_cast<u4_t *>(xl + oct * MTS + m) = v;
+    if constexpr (FMT == 1) {
+      float c = (x_to_float(uint16_t(v.y), BF) + x_to_float(uint16_t(v.y >> 16), BF)) +
+                (x_to_float(uint16_t(v.w), BF) + x_to_float(uint16_t(v.w >> 16), BF));
 #pragma unroll
-    for (int o = 0; o < 16; ++o) v[o] = src[o];
-    float c = 0.f;
-#pragma unroll
-    for (int o = 0; o < 16; ++o) {
-      const u4_t z = {0u, 0u, 0u, 0u};
-      const u4_t vv = in ? v[o] : z;
-      if (m < MTS) *reinterpret_cast<u4_t *>(xl + (gs * 16 + o) * MTS + m) = vv;
-      if constexpr (FMT == 1)
-        c += (x_to_float(uint16_t(vv.y), BF) + x_to_float(uint16_t(vv.y >> 16), BF)) +
-             (x_to_float(uint16_t(vv.w), BF) + x_to_float(uint16_t(vv.w >> 16), BF));
+      for (int o = 1; o < 16; o <<= 1) c += __shfl_xor(c, o, 16);
+      if (live && (oct & 15) == 0) corr[(oct >> 4) * 16 + m] = -c;
     }
-    corr[idx] = -c;
+  }
+  if constexpr (FMT == 1) {
+    // Token slots without a token get a zero correction.
+    for (int idx = threadIdx.x; idx < nc * 4 * (16 - MTS); idx += kThreads) {
+      const int gs = idx / (16 - MTS), m = MTS + idx % (16 - MTS);
+      corr[gs * 16 + m] = 0.f;
+    }
   }
 }
 
