@@ -28,6 +28,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+# Plain copy run once before timing so that a hardware-counter pass over this
+# same command can scale FETCH_SIZE / WRITE_SIZE by a kernel of known traffic.
+CALIB_COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_sweep.txt")
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 BLOCK = [(5120, 5120)] * 4 + [(17408, 5120), (17408, 5120), (5120, 17408)]
@@ -45,6 +49,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--print-source-digest", action="store_true")
     return ap.parse_args()
 
 
@@ -89,9 +94,12 @@ def gen_weights_gpu(torch, lb, fmt, layers, seed):
 
 def main():
     args = parse()
+    if args.print_source_digest:
+        print(_source_digest())
+        return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build's path runs on a single MI355X "
-              "(see the sharding notes in the design document); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the low-bit GEMV/GEMM path runs on a single MI355X "
+              "and has no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -154,6 +162,13 @@ def main():
         f, w, x, y, M, N, K = gemm_data[i]
         lb.gemm_raw(f, w.data_ptr(), x.data_ptr(), BF, y.data_ptr(), F32, M, N, K, sptr)
 
+    # Counter calibration: one plain device copy of CALIB_COPY_BYTES (untimed).
+    cal_src = torch.ones(CALIB_COPY_BYTES // 4, device=dev, dtype=torch.float32)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
     # ------------------------------------------------------------- timing
     parts = [("sweep", k) for k in SWEEP] + [("gemm", i) for i in range(len(GEMMS))]
     ev = {p: [] for p in parts}
@@ -202,8 +217,10 @@ def main():
     dom = max(SWEEP, key=lambda k: ms[("sweep", k)])
     dom_ms = ms[("sweep", dom)]
     achieved = sweep_bytes[dom] / (dom_ms * 1e-3) / 1e9
+    traffic, fetch = measured_traffic(dom)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "fetch_bytes_per_launch": fetch,
                 "kernel": f"gemv {dom[0]} M={dom[1]} (bf16 x, fp32 y)",
                 "avg_launch_us": round(dom_ms * 1e3 / len(layers), 3),
                 "bytes_per_launch": round(sweep_bytes[dom] / len(layers))}
@@ -230,6 +247,43 @@ def main():
         "roofline": roofline, "roofline_gemm": roofline_gemm, "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def _source_digest():
+    """sha256 over the kernel sources and the launch planner (any change to
+    them invalidates counters taken earlier)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "ternary_group_scaled_q1_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(dom):
+    """(traffic, fetch) in HBM bytes per launch of the dominant sweep from the
+    committed counter summary: FETCH_SIZE and WRITE_SIZE, each scaled by the
+    calibration copy.  traffic = fetch + write when both were measured; both
+    are None when there is no summary or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(l.split(":", 1) for l in f if ":" in l and not l.startswith(("#", "|", " ")))
+    except OSError:
+        return None, None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != _source_digest() or kv.get("sweep") != f"{dom[0]}_M{dom[1]}":
+        return None, None
+
+    def num(key):
+        try:
+            return int(float(kv[key]))
+        except (KeyError, ValueError):
+            return None
+
+    fetch, write = num("fetch_bytes_per_launch"), num("write_bytes_per_launch")
+    return (fetch + write if fetch is not None and write is not None else None), fetch
 
 
 def cpu_baseline(budget_s):
