@@ -91,6 +91,50 @@ __device__ __forceinline__ uint32_t tq5_pair(uint32_t d, int i) {
   return (d << (2 * i)) & 0xC000C000u;
 }
 
+// ---- Scaled fp8 x fp4 matrix path (v_mfma_scale_f32_16x16x128_f8f6f4) ----
+//
+// Lane layout of the 16x16x128 instruction (measured on gfx950):
+//  * B, fp4 e2m1: lane 16q + j holds column j at k = 32q + n for its nibble n
+//    (nibble n in dword n / 8, bits 4(n % 8) .. 4(n % 8) + 3);
+//  * A, fp8 e4m3: lane 16q + r holds row r at k = 16q + b for bytes b < 16 and
+//    at k = 64 + 16q + (b - 16) for bytes b >= 16;
+//  * the E8M0 scale of lane 16kb + r (byte 0) multiplies row r of A (column r
+//    of B) over k in [32kb, 32kb + 32);
+//  * D lane 16q + j, element e: row 4q + e, column j.
+// +-1 and +-2 are exact in fp4 e2m1, so a weight decodes to an exact operand.
+typedef int i8v_t __attribute__((ext_vector_type(8)));
+
+// A = x pieces (fp8), B = weights (fp4, scale 1), fresh fp32 accumulator.
+__device__ __forceinline__ f4_t mfma_f8f4(u4_t a0, u4_t a1, u4_t b, int sa) {
+  const i8v_t A = {int(a0.x), int(a0.y), int(a0.z), int(a0.w), int(a1.x), int(a1.y), int(a1.z), int(a1.w)};
+  const i8v_t B = {int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0};
+  const f4_t z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, z, 0, 4, 0, sa, 0, 0x7F7F7F7F);
+}
+
+// q1 word -> 32 fp4 weights: nibble i of dword d takes bit 4i + 3 - d;
+// bit 1 -> +1.0 (0x2), bit 0 -> -1.0 (0xA).
+__device__ __forceinline__ u4_t q1_fp4(uint32_t w) {
+  u4_t b;
+  b.x = (~w & 0x88888888u) | 0x22222222u;
+  b.y = (~(w << 1) & 0x88888888u) | 0x22222222u;
+  b.z = (~(w << 2) & 0x88888888u) | 0x22222222u;
+  b.w = (~(w << 3) & 0x88888888u) | 0x22222222u;
+  return b;
+}
+
+// tq2 words (two per lane and group) -> 32 fp4 values 2t: nibble i of dword d
+// takes the code at bits 4i + 2 - 2(d % 2) of word d / 2; ~c at nibble bits
+// 2..3 is 0xC (-2), 0x8 (-0) or 0x4 (+2) for c = 0, 1, 2.
+__device__ __forceinline__ u4_t tq2_fp4(uint32_t w0, uint32_t w1) {
+  u4_t b;
+  b.x = ~w0 & 0xCCCCCCCCu;
+  b.y = ~(w0 << 2) & 0xCCCCCCCCu;
+  b.z = ~w1 & 0xCCCCCCCCu;
+  b.w = ~(w1 << 2) & 0xCCCCCCCCu;
+  return b;
+}
+
 __device__ __forceinline__ float half_to_float(uint16_t h) {
   return float(__builtin_bit_cast(_Float16, h));
 }

@@ -16,6 +16,18 @@
 // that is scaled by the group's FP16 scale in fp32 and added to the running
 // sum (exact products, one fp32 rounding per group).
 //
+// Two product paths share the work split below:
+//  * bf16 x, up to 8 tokens: the weights decode to fp4 (e2m1) and each
+//    128-weight group is one scaled 16x16x128 fp8 x fp4 MFMA.  x enters as two
+//    exact fp8 (e4m3) pieces per value, x = S (hi + lo), with one power-of-two
+//    scale S per token and 32 values (the instruction's E8M0 operand scale):
+//    a bf16 value has 8 significant bits and each piece carries 4, so the
+//    split is exact unless a value sits more than 2^10 below the largest of
+//    its 32 (then the error is below 2^-17 of that largest value).  The A rows
+//    are (token, piece) pairs; the two pieces' products are added in fp32.
+//  * fp16 x, or more than 8 tokens: v_mfma_f32_16x16x32 on exact f16/bf16
+//    operands.
+//
 // Work split: a workgroup of 8 waves stages x in LDS as [k/8][token][8]
 // 16-byte cells, all of K at once when it fits (then the stage is loaded
 // once per workgroup) or S chunks at a time.  The waves form P = 8/S
@@ -68,7 +80,109 @@ inline LdsMap lds_map(int MTS, int S, int SC, int R, int E) {
   return m;
 }
 
+// fp8 x fp4 path: per group, 2*MP A rows of kRowBytes (128 bytes of pieces
+// in lane order + 16 bytes that spread the rows over the LDS banks), then
+// MP*4 E8M0 scale bytes per group.
+constexpr int kRowBytes = 144;
+
+inline LdsMap lds_map_fp4(int MP, int S, int SC, int R, int E) {
+  LdsMap m;
+  const int groups = 4 * SC;
+  m.corr = 0;
+  m.x = 0;
+  int o = groups * 2 * MP * kRowBytes;
+  m.corr = o;  // E8M0 scale bytes
+  o += (groups * MP * 4 + 15) / 16 * 16;
+  m.red = o;
+  if (S > 1) o += kWaves * R * E * 64 * 4;
+  m.total = o;
+  return m;
+}
+
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Which in-group weight (8u + e: k = 32u + 8q + e for lane quarter q) feeds
+// fp4 nibble n of a lane's operand (the inverses of q1_fp4 / tq2_fp4 over the
+// bit positions of device layout v1).
+__device__ constexpr int fp4_src(int fmt, int n) {
+  const int d = n / 8, i = n % 8;
+  if (fmt == 1) {
+    const int pbit = 4 * i + 3 - d;
+    const int rem = 15 - pbit % 16;
+    return 8 * (rem / 4) + (pbit / 16) + 2 * (rem % 2) + 4 * ((rem / 2) % 2);
+  }
+  const int pos = 4 * i + 2 - 2 * (d % 2);
+  const int rem = 14 - pos % 16;
+  return 8 * (2 * (d / 2) + rem / 8) + (pos / 16) + 2 * ((rem % 8) / 2);
+}
+
+// Stage chunks [c0, c0 + nc) of x for the fp8 x fp4 path.  One thread per
+// (token slot m, group, lane quarter q): the 32 values of that quarter
+// (k = 32u + 8q + e) are the 32 k of one E8M0 block of the B operand, so one
+// scale S = 2^(E - 127) covers them.  E puts the block's largest magnitude in
+// [128, 256) (below the fp8 maximum 448, so no piece can overflow); hi =
+// fp8(x / S) and lo = fp8(x / S - hi), both rounded to nearest even.  A block
+// holding inf or nan gets the nan scale 0xFF.  Tokens m >= M and groups past
+// K stage as zeros.
+template <int FMT, int MP>
+__device__ void stage_fp4(const GemvParams &p, char *lds, int c0, int nc) {
+  const int g0 = 4 * c0;
+  const int items = MP * 4 * nc * 4;
+  for (int it = threadIdx.x; it < items; it += kThreads) {
+    const int q = it & 3, rest = it >> 2;
+    const int gl = rest % (4 * nc), m = rest / (4 * nc);
+    const bool in = m < p.M && g0 + gl < p.G;
+    const uint16_t *src = p.X + (in ? (int64_t)m * p.K + 128 * (g0 + gl) + 8 * q : 0);
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u4_t o = *reinterpret_cast<const u4_t *>(src + 32 * u);
+      v[4 * u + 0] = in ? o.x : 0u;
+      v[4 * u + 1] = in ? o.y : 0u;
+      v[4 * u + 2] = in ? o.z : 0u;
+      v[4 * u + 3] = in ? o.w : 0u;
+    }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = max(mx, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+    const int ef = int(mx >> 7);  // exponent field of the largest magnitude
+    const int sb = ef == 255 ? 255 : max(ef - 7, 0);
+    const float mul = __builtin_bit_cast(float, uint32_t(254 - min(sb, 253)) << 23);  // 2^(127 - sb)
+    int hi[8], lo[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float f[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int sidx = fp4_src(FMT, 4 * w + b);  // 8u + e
+        const uint32_t word = v[sidx / 2];
+        f[b] = __builtin_bit_cast(float, (sidx & 1) ? (word & 0xFFFF0000u) : (word << 16)) * mul;
+      }
+      hi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      hi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], hi[w], true);
+      const float r0 = f[0] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 0);
+      const float r1 = f[1] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 1);
+      const float r2 = f[2] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 2);
+      const float r3 = f[3] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 3);
+      lo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+      lo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, lo[w], true);
+    }
+    // Nibble n of the B lane quarter q sits at hardware k = 32q + n; A holds
+    // k < 64 in bytes 0..15 and k >= 64 in bytes 16..31 of lane quarter
+    // (k % 64) / 16.
+    char *row = lds + p.off_x + (gl * 2 * MP + 2 * m) * kRowBytes;
+    const int qa = 2 * (q & 1), half = 16 * (q >> 1);
+    const u4_t h0 = {uint32_t(hi[0]), uint32_t(hi[1]), uint32_t(hi[2]), uint32_t(hi[3])};
+    const u4_t h1 = {uint32_t(hi[4]), uint32_t(hi[5]), uint32_t(hi[6]), uint32_t(hi[7])};
+    const u4_t l0 = {uint32_t(lo[0]), uint32_t(lo[1]), uint32_t(lo[2]), uint32_t(lo[3])};
+    const u4_t l1 = {uint32_t(lo[4]), uint32_t(lo[5]), uint32_t(lo[6]), uint32_t(lo[7])};
+    *reinterpret_cast<u4_t *>(row + qa * 32 + half) = h0;
+    *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = h1;
+    *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = l0;
+    *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = l1;
+    reinterpret_cast<uint8_t *>(lds + p.off_corr)[(gl * MP + m) * 4 + q] = uint8_t(sb);
+  }
+}
 
 // Stage chunks [c0, c0 + nc) of x: cell (oct, m) holds x[m][k0 + 8 oct .. + 8] at
 // byte off_x + (oct * MTS + m) * 16 (zeros past K and for m >= M).  One thread
@@ -240,6 +354,59 @@ __device__ __forceinline__ void store_tiles(const GemvParams &p, int t0, const f
   }
 }
 
+// fp8 x fp4 path, one unit (R tiles x 4 groups).  Lane 16qa + r reads A row
+// r (token r / 2, piece r % 2) of each group; rows past 2*MP are zero.
+template <int FMT, int MP, int R, int E>
+__device__ __forceinline__ void compute_fp4(const GemvParams &p, const char *lds, const Unit<FMT, R> &u, int c_local,
+                                            float (&yacc)[R][4]) {
+  const int lane = threadIdx.x & 63, qa = lane >> 4, r = lane & 15;
+  const bool arow = r < 2 * MP;
+  const int rr = arow ? r : 0;
+  const char *xa = lds + p.off_x + (c_local * 4 * 2 * MP + rr) * kRowBytes + qa * 32;
+  const uint8_t *sa = reinterpret_cast<const uint8_t *>(lds + p.off_corr) + (c_local * 4 * MP + (rr >> 1)) * 4 + qa;
+  const u4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    u4_t a0 = *reinterpret_cast<const u4_t *>(xa + g * 2 * MP * kRowBytes);
+    u4_t a1 = *reinterpret_cast<const u4_t *>(xa + g * 2 * MP * kRowBytes + 16);
+    a0 = arow ? a0 : z;
+    a1 = arow ? a1 : z;
+    const int sc = sa[g * MP * 4];
+#pragma unroll
+    for (int r2 = 0; r2 < R; ++r2) {
+      u4_t b;
+      if constexpr (FMT == 1) b = q1_fp4(u.w[r2][g]);
+      else b = tq2_fp4(u.w[r2][2 * g], u.w[r2][2 * g + 1]);
+      const f4_t d = mfma_f8f4(a0, a1, b, sc);
+      const float s = half_to_float(uint16_t(u.s[r2][g >> 1] >> (16 * (g & 1))));
+#pragma unroll
+      for (int e = 0; e < E; ++e) yacc[r2][e] = fmaf(s, d[e], yacc[r2][e]);
+    }
+  }
+}
+
+// Accumulator element e of lane 16qa + j is A row 4qa + e: token 2qa + e / 2,
+// piece e % 2.
+template <int FMT, int R, int E>
+__device__ __forceinline__ void store_fp4(const GemvParams &p, int t0, const float (&yacc)[R][4]) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, qa = lane >> 4;
+  const float mul = FMT == 1 ? 1.f : 0.5f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = 16 * (t0 + r) + j;
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int tt = 0; tt < E / 2; ++tt) {
+      const int m = 2 * qa + tt;
+      if (m >= p.M) continue;
+      const float v = (yacc[r][2 * tt] + yacc[r][2 * tt + 1]) * mul;
+      if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
+      else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+    }
+  }
+}
+
 // Position of a wave in its flat sequence of units: tile set iteration it,
 // stage st, slot kl inside the stage.  Advanced incrementally (no divisions).
 struct Cursor {
@@ -259,15 +426,17 @@ __device__ __forceinline__ void advance(Cursor &c, int U, int n_stages) {
 // Each wave walks a flat sequence of units (tile set, chunk) with a ring of
 // D units in flight: the loads of unit i + D - 1 are issued before unit i is
 // computed, across chunk, stage and tile-set boundaries.
-template <int FMT, bool BF, int MT, int R, int D>
+// FP4 selects the fp8 x fp4 path (MT = token slots MP, at most 8).
+template <int FMT, bool BF, int MT, int R, int D, bool FP4>
 __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
-  constexpr int E = MT == 1 ? 1 : 4;     // accumulator elements that can hold a token
+  // Accumulator elements that can hold a token (fp4: A rows, two per token).
+  constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
   constexpr int MTS = MT;                // token slots per x cell
   extern __shared__ __align__(16) char lds[];
   const int wave = uni(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, q = lane >> 4;
-  if constexpr (MTS < 16) {
+  if constexpr (!FP4 && MTS < 16) {
     for (int i = threadIdx.x; i < 64 * MTS; i += kThreads) reinterpret_cast<uint4 *>(lds)[i] = make_uint4(0, 0, 0, 0);
   }
 
@@ -303,7 +472,8 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
     advance(ld, U, p.n_stages);
   }
   if (!restage) {
-    stage_x<FMT, BF, MTS>(p, lds, 0, p.chunks);
+    if constexpr (FP4) stage_fp4<FMT, MT>(p, lds, 0, p.chunks);
+    else stage_x<FMT, BF, MTS>(p, lds, 0, p.chunks);
     __syncthreads();
   }
 
@@ -328,18 +498,26 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
       if (restage && cu.kl == 0) {
         __syncthreads();
         const int c0 = cu.st * p.SC;
-        stage_x<FMT, BF, MTS>(p, lds, c0, min(p.SC, p.chunks - c0));
+        if constexpr (FP4) stage_fp4<FMT, MT>(p, lds, c0, min(p.SC, p.chunks - c0));
+        else stage_x<FMT, BF, MTS>(p, lds, c0, min(p.SC, p.chunks - c0));
         __syncthreads();
       }
       if (is_valid(cu)) {
         const int c_local = s + cu.kl * S;
-        const int xbase = xact ? p.off_x + (c_local * 64 * MTS + q * MTS + j) * 16 : 0;
-        compute_unit<FMT, BF, R, E, MTS>(p, lds, ring[d], c_local, xbase, yacc);
+        if constexpr (FP4) {
+          compute_fp4<FMT, MT, R, E>(p, lds, ring[d], c_local, yacc);
+        } else {
+          const int xbase = xact ? p.off_x + (c_local * 64 * MTS + q * MTS + j) * 16 : 0;
+          compute_unit<FMT, BF, R, E, MTS>(p, lds, ring[d], c_local, xbase, yacc);
+        }
       }
       if (k_last) {
         const bool ts_ok = t0 < p.tiles;
         if (S == 1) {
-          if (ts_ok) store_tiles<FMT, R, E>(p, t0, yacc);
+          if (ts_ok) {
+            if constexpr (FP4) store_fp4<FMT, R, E>(p, t0, yacc);
+            else store_tiles<FMT, R, E>(p, t0, yacc);
+          }
         } else {
           float *red = reinterpret_cast<float *>(lds + p.off_red);
 #pragma unroll
@@ -357,7 +535,8 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
                 for (int s2 = 0; s2 < S; ++s2) v += red[(((pr * S + s2) * R + r) * E + e) * 64 + lane];
                 tot[r][e] = v;
               }
-            store_tiles<FMT, R, E>(p, t0, tot);
+            if constexpr (FP4) store_fp4<FMT, R, E>(p, t0, tot);
+            else store_tiles<FMT, R, E>(p, t0, tot);
           }
           __syncthreads();
         }
@@ -369,9 +548,9 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
 
 // Host-side choice of (R, S): the smallest per-wave work (the makespan:
 // tile sets per wave-row x R x chunks per wave), then fewer barriers.
-template <int FMT, bool BF, int MT, int R, int D>
+template <int FMT, bool BF, int MT, int R, int D, bool FP4>
 double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) {
-  constexpr int E = MT == 1 ? 1 : 4;
+  constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
   p = GemvParams{};
   const int64_t G = a.K / kGroup;
   p.W = a.W;
@@ -384,7 +563,10 @@ double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) 
   p.tilesets = (p.tiles + R - 1) / R;
   p.y_f16 = a.y_f16;
   const int cus = num_cus();
-  const void *kern = reinterpret_cast<const void *>(&gemv_kernel<FMT, BF, MT, R, D>);
+  const void *kern = reinterpret_cast<const void *>(&gemv_kernel<FMT, BF, MT, R, D, FP4>);
+  auto map = [&](int S, int SC) { return FP4 ? lds_map_fp4(MT, S, SC, R, E) : lds_map(MT, S, SC, R, E); };
+  // x bytes a stage of SC chunks occupies.
+  auto xbytes = [&](int SC) { return FP4 ? SC * 4 * (2 * MT * kRowBytes + 4 * MT) : MT * SC * 1024; };
 
   double best = 1e300;
   GemvParams bp = p;
@@ -395,15 +577,15 @@ double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) 
     // Stage all chunks when the LDS map fits in 64 KB, else stream stages of
     // as many chunks as fit in 32 KB of x.
     int SC = (p.chunks + S - 1) / S * S;
-    if (lds_map(MT, S, SC, R, E).total > 64 * 1024) {
-      if (MT * S * 1024 > 32 * 1024) continue;
+    if (map(S, SC).total > 64 * 1024) {
+      if (xbytes(S) > 32 * 1024) continue;
       SC = S;
-      while (SC + S <= p.chunks && MT * (SC + S) * 1024 <= 32 * 1024) SC += S;
+      while (SC + S <= p.chunks && xbytes(SC + S) <= 32 * 1024) SC += S;
     }
     q.S = S;
     q.SC = SC;
     q.n_stages = (p.chunks + SC - 1) / SC;
-    const LdsMap m = lds_map(MT, S, SC, R, E);
+    const LdsMap m = map(S, SC);
     q.off_corr = m.corr; q.off_x = m.x; q.off_red = m.red;
     const int P = kWaves / S;
     const int per_cu = resident_blocks(kern, kThreads, m.total);
@@ -423,31 +605,44 @@ double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) 
   p = bp;
   grid = bgrid;
   lds_bytes = blds;
-  // R = 1 reads the x operand from LDS once per MFMA instead of once per two.
+  // One row tile per unit reads the x operand from LDS once per MFMA instead
+  // of once per R.
   return best * (R == 1 ? 1.1 : 1.0);
 }
 
-template <int FMT, bool BF, int MT>
+template <int FMT, bool BF, int MT, bool FP4, int RA, int RB>
 hipError_t launch_mt(const LaunchArgs &a) {
   GemvParams p1, p2;
   int g1, g2, l1, l2;
   // Ring depth: three units in flight for q1 (1 KB per tile each), two for
-  // tq2 (2 KB per tile each) so that four waves per SIMD fit in registers.
-  constexpr int D = FMT == 1 ? 3 : 2;
-  const double c1 = make_plan<FMT, BF, MT, 1, D>(a, p1, g1, l1);
-  const double c2 = make_plan<FMT, BF, MT, 2, D>(a, p2, g2, l2);
+  // tq2 (2 KB per tile each) and for four-tile units, so that four waves per
+  // SIMD fit in registers.
+  constexpr int DA = (FMT == 1 && RA < 4) ? 3 : 2;
+  constexpr int DB = (FMT == 1 && RB < 4) ? 3 : 2;
+  const double c1 = make_plan<FMT, BF, MT, RA, DA, FP4>(a, p1, g1, l1);
+  const double c2 = make_plan<FMT, BF, MT, RB, DB, FP4>(a, p2, g2, l2);
   if (c1 < c2)
-    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, 1, D>), dim3(g1), dim3(kThreads), l1, a.stream, p1);
+    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, RA, DA, FP4>), dim3(g1), dim3(kThreads), l1, a.stream, p1);
   else
-    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, 2, D>), dim3(g2), dim3(kThreads), l2, a.stream, p2);
+    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, RB, DB, FP4>), dim3(g2), dim3(kThreads), l2, a.stream, p2);
   return hipGetLastError();
 }
 
 template <int FMT, bool BF>
 hipError_t launch_fmt(const LaunchArgs &a) {
-  if (a.M <= 1) return launch_mt<FMT, BF, 1>(a);
-  if (a.M <= 4) return launch_mt<FMT, BF, 4>(a);
-  return launch_mt<FMT, BF, 16>(a);
+  if constexpr (BF) {
+    // fp8 x fp4 path: exact fp8 pieces of bf16 x, up to 8 tokens.
+    constexpr int RB = FMT == 1 ? 4 : 3;
+    if (a.M <= 1) return launch_mt<FMT, BF, 1, true, 2, RB>(a);
+    if (a.M <= 2) return launch_mt<FMT, BF, 2, true, 2, RB>(a);
+    if (a.M <= 4) return launch_mt<FMT, BF, 4, true, 2, RB>(a);
+    if (a.M <= 8) return launch_mt<FMT, BF, 8, true, 2, RB>(a);
+    return launch_mt<FMT, BF, 16, false, 1, 2>(a);
+  } else {
+    if (a.M <= 1) return launch_mt<FMT, BF, 1, false, 1, 2>(a);
+    if (a.M <= 4) return launch_mt<FMT, BF, 4, false, 1, 2>(a);
+    return launch_mt<FMT, BF, 16, false, 1, 2>(a);
+  }
 }
 
 }  // namespace

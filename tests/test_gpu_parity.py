@@ -206,3 +206,49 @@ def test_workload_config1_all_outputs():
     x = synth.draw_x(0, 1, 0, 1, K, "f16")
     y = gu.run("gemv", "q1", gu.w_tensor(lb.pack("q1", codes, sc)), x, "f16", "f32", N, K)
     gu.check(y, codes, sc, x, "f16", "config 1")
+
+
+# ------------------------------------------ decode sweep shapes (27B-class) ----
+SWEEP_SHAPES = [(5120, 5120), (17408, 5120), (5120, 17408)]
+
+
+@pytest.mark.parametrize("fmt", ["q1", "tq2"])
+@pytest.mark.parametrize("shape", SWEEP_SHAPES)
+@pytest.mark.parametrize("M", [1, 16])
+def test_workload_sweep_shapes(fmt, shape, M):
+    N, K = shape
+    print(f"{fmt} gemv sweep shape N={N} K={K} M={M}", flush=True)
+    _sampled(fmt, N, K, M, "bf16", "gemv", 5, SWEEP_SHAPES.index(shape), None if fmt == "q1" else 0.3)
+
+
+def test_workload_sweep_lm_head_q1():
+    print("q1 gemv N=151936 K=5120 M=1", flush=True)
+    _sampled("q1", 151936, 5120, 1, "bf16", "gemv", 5, 3, None, rows=32)
+
+
+# ------------------------------------------------ bf16 x over a wide range ----
+@pytest.mark.parametrize("fmt", ["q1", "tq2"])
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
+def test_bf16_x_wide_dynamic_range(fmt, M):
+    """bf16 activations whose magnitudes spread over 2^-40 .. 2^8 inside every
+    32-value block, plus whole blocks of tiny values next to large ones: every
+    element must stay within the bound."""
+    g = np.random.default_rng(300 + M)
+    N, K = 96, 2048
+    codes = _codes(g, fmt, N, K)
+    sc = synth.scales_absnormal(g, N, K // 128)
+    mag = np.exp2(g.uniform(-40, 8, size=(M, K)))
+    xf = mag * np.where(g.random((M, K)) < 0.5, -1.0, 1.0)
+    xf[:, 256:384] *= 2.0 ** -60          # one group of tiny values
+    xf[:, 512:520] = 0.0                  # a run of zeros
+    x = synth.f64_to_bf16_bits(xf)
+    blob = gu.w_tensor(lb.pack(fmt, codes, sc))
+    for ydt in ("f32", "f16"):
+        y = gu.run("gemv", fmt, blob, x, "bf16", ydt, N, K)
+        if ydt == "f16":
+            y_ref, a_ref = ref.product(codes, sc, x, "bf16")
+            keep = np.abs(y_ref) < 6e4  # fp16 output range
+            y_ref_ok, a_ok = y_ref[keep], a_ref[keep]
+            assert np.all(np.abs(y[keep] - y_ref_ok) <= ref.RTOL * a_ok + ref.ATOL + np.abs(y_ref_ok) * 2.0 ** -11)
+        else:
+            gu.check(y, codes, sc, x, "bf16", f"wide range {fmt} M={M}")
