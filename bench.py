@@ -125,6 +125,9 @@ def main():
           for m in (1, 16) for K in (5120, 17408)}
     ys = {(m, N): torch.empty((m, N), device=dev, dtype=torch.float32)
           for m in (1, 16) for N in (5120, 17408, 151936)}
+    # One caller-owned GEMV workspace, reused by every launch of a sweep.
+    ws_bytes = max(lb.gemv_workspace_bytes(f, m, N, K) for f in ("q1", "tq2") for m in (1, 16) for (N, K) in layers)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def sweep(fmt, m):
         buf, offs = weights[fmt]
@@ -132,7 +135,7 @@ def main():
         f = lb.FORMATS[fmt]
         for (N, K), off in zip(layers, offs):
             lb.gemv_raw(f, base + off, xs[(m, K)].data_ptr(), BF, ys[(m, N)].data_ptr(), F32, m, N, K,
-                        torch.cuda.current_stream(dev).cuda_stream)
+                        torch.cuda.current_stream(dev).cuda_stream, ws.data_ptr(), ws_bytes)
 
     sweep_bytes = {}
     for fmt, m in SWEEP:

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 1
+#define LOWBIT_ABI_VERSION 2
 
 typedef enum { LOWBIT_Q1_G128 = 1, LOWBIT_TQ2_G128 = 2, LOWBIT_TQ5_G128 = 3 } lowbit_format;
 typedef enum { LOWBIT_F16 = 1, LOWBIT_BF16 = 2, LOWBIT_F32 = 3 } lowbit_dtype;
@@ -100,15 +100,32 @@ int pack_tq5_g128(const int8_t *codes, const uint16_t *scales, int64_t N, int64_
 int unpack_lowbit(int fmt, const void *packed, int64_t packed_bytes, int64_t N, int64_t K,
                   int8_t *codes_out, uint16_t *scales_out);
 
-/* Decode GEMV: Y = X W^T for small batches (tuned for M <= 16; any M works).
+/* Workspace that lets gemv_lowbit take its fastest path for this problem
+ * (0 = the fastest path needs none).  With bf16 activations the decode
+ * product may cut K into ranges handled by different workgroups; their fp32
+ * partial sums live here, after 32 KiB of arrival counters at its start.  The
+ * size does not depend on the device; fp16 activations never use it.
+ * Returns a negative status on a bad format or shape. */
+int64_t gemv_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
+
+/* Decode GEMV: Y = X W^T for small batches (tuned for M <= 16; any M works;
+ * more than 16 tokens run as consecutive 16-token launches).
  *   Wp: device, packed blob of this (fmt, N, K), 16-byte aligned
  *   X:  device, M x K, x_dtype LOWBIT_F16 or LOWBIT_BF16, 16-byte aligned
  *   Y:  device, M x N, y_dtype LOWBIT_F32 or LOWBIT_F16
+ *   workspace: caller-owned device memory, 16-byte aligned, or NULL.  It
+ *   must be zero-filled before its first use (it holds arrival counters that
+ *   every call leaves at zero again); calls that may run concurrently need
+ *   separate workspaces.  With at least gemv_workspace_bytes_lowbit() bytes
+ *   the call may split K across workgroups; with less, or NULL, it takes a
+ *   path that needs none.  Results obey the same bound and are deterministic
+ *   for a given workspace size either way.
  *   hip_stream: hipStream_t to launch on (NULL = default stream); the call is
  *   asynchronous with respect to the host.
  * M*N == 0 returns LOWBIT_OK without launching; K == 0 writes Y = 0.       */
 int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype,
-                int64_t M, int64_t N, int64_t K, void *hip_stream);
+                int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
+                void *hip_stream);
 
 /* Workspace gemm_lowbit needs for this problem (0 = none). */
 int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);

@@ -13,5 +13,5 @@ arguments to it (ctypes), with torch providing device memory and streams.
 """
 from ._lib import (  # noqa: F401
     DT_BF16, DT_F16, DT_F32, FORMATS, GROUP, LIB_PATH, LowbitError, abi_version, gemm, gemm_raw,
-    gemm_workspace_bytes, gemv, gemv_raw, load, pack, packed_bytes, strerror, unpack,
+    gemm_workspace_bytes, gemv, gemv_raw, gemv_workspace_bytes, load, pack, packed_bytes, strerror, unpack,
 )

@@ -52,7 +52,8 @@ def load() -> ctypes.CDLL:
         "pack_tq2_g128": (i32, [vp, vp, i64, i64, vp, i64]),
         "pack_tq5_g128": (i32, [vp, vp, i64, i64, vp, i64]),
         "unpack_lowbit": (i32, [i32, vp, i64, i64, i64, vp, vp]),
-        "gemv_lowbit": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp]),
+        "gemv_workspace_bytes_lowbit": (i64, [i32, i64, i64, i64]),
+        "gemv_lowbit": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp, i64, vp]),
         "gemm_workspace_bytes_lowbit": (i64, [i32, i64, i64, i64]),
         "gemm_lowbit": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp, i64, vp]),
     }
@@ -157,14 +158,31 @@ def _prep(fmt, w, x, N, K, out_dtype, out):
     return f, x, M, out
 
 
-def gemv(fmt, w, x, N: int, K: int, out_dtype=None, out=None, stream=None):
-    """y[M,N] = x[M,K] @ W^T on the GPU (decode path, M <= 16 preferred)."""
+def gemv_workspace_bytes(fmt, M: int, N: int, K: int) -> int:
+    n = load().gemv_workspace_bytes_lowbit(_fmt(fmt), M, N, K)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def gemv(fmt, w, x, N: int, K: int, out_dtype=None, out=None, workspace=None, stream=None):
+    """y[M,N] = x[M,K] @ W^T on the GPU (decode path, M <= 16 preferred).
+
+    workspace: a zero-filled uint8 device tensor of at least
+    gemv_workspace_bytes() bytes, reused across calls on one stream (a fresh
+    zeroed one is allocated here when None and needed); workspace=False runs
+    the path that needs none."""
     torch = _torch()
     out_dtype = out_dtype or torch.float32
     f, x, M, out = _prep(fmt, w, x, N, K, out_dtype, out)
+    if workspace is None:
+        need = gemv_workspace_bytes(f, M, N, K)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device) if need else False
+    ws_ptr = workspace.data_ptr() if workspace is not False else None
+    ws_n = workspace.numel() if workspace is not False else 0
     s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
     _check(load().gemv_lowbit(f, w.data_ptr(), x.data_ptr(), _x_dtype(x), out.data_ptr(), _y_dtype(out.dtype),
-                              M, N, K, s))
+                              M, N, K, ws_ptr, ws_n, s))
     return out
 
 
@@ -192,9 +210,10 @@ def gemm(fmt, w, x, N: int, K: int, out_dtype=None, out=None, workspace=None, st
 
 
 def gemv_raw(fmt: int, w_ptr: int, x_ptr: int, x_dtype: int, y_ptr: int, y_dtype: int, M: int, N: int, K: int,
-             stream_ptr: int) -> None:
+             stream_ptr: int, ws_ptr: int = 0, ws_bytes: int = 0) -> None:
     """Pointer-level call (no tensor checks) for tight timing loops."""
-    _check(load().gemv_lowbit(fmt, w_ptr, x_ptr, x_dtype, y_ptr, y_dtype, M, N, K, stream_ptr))
+    _check(load().gemv_lowbit(fmt, w_ptr, x_ptr, x_dtype, y_ptr, y_dtype, M, N, K, ws_ptr or None, ws_bytes,
+                              stream_ptr))
 
 
 def gemm_raw(fmt: int, w_ptr: int, x_ptr: int, x_dtype: int, y_ptr: int, y_dtype: int, M: int, N: int, K: int,

@@ -33,8 +33,10 @@ int check_product(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, 
 }
 
 int run(bool gemm, int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M, int64_t N,
-        int64_t K, void *stream) {
+        int64_t K, void *ws, int64_t ws_bytes, void *stream) {
   LaunchArgs a;
+  a.ws = ws;
+  a.ws_bytes = ws ? ws_bytes : 0;
   a.fmt = fmt;
   a.W = static_cast<const uint8_t *>(Wp);
   a.X = static_cast<const uint16_t *>(X);
@@ -75,11 +77,20 @@ const char *lowbit_strerror(int status) {
   return "unknown status";
 }
 
+int64_t gemv_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (fmt < LOWBIT_Q1_G128 || fmt > LOWBIT_TQ5_G128) return LOWBIT_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0 || K % kGroup) return LOWBIT_ERR_SHAPE;
+  if (M == 0 || N == 0 || K == 0) return 0;
+  return gemv_workspace_bytes(fmt, M, N, K);
+}
+
 int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M, int64_t N,
-                int64_t K, void *hip_stream) {
+                int64_t K, void *workspace, int64_t workspace_bytes, void *hip_stream) {
   const int st = check_product(fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K);
   if (st != LOWBIT_OK || M == 0 || N == 0) return st;
-  return run(false, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, hip_stream);
+  if (workspace_bytes < 0) return LOWBIT_ERR_SIZE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 15)) return LOWBIT_ERR_ALIGN;
+  return run(false, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, workspace, workspace_bytes, hip_stream);
 }
 
 int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K) {
@@ -95,7 +106,7 @@ int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, in
   const int64_t need = gemm_workspace_bytes_lowbit(fmt, M, N, K);
   if (workspace_bytes < need) return LOWBIT_ERR_SIZE;
   if (need > 0 && !workspace) return LOWBIT_ERR_NULL;
-  return run(true, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, hip_stream);
+  return run(true, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, workspace, workspace_bytes, hip_stream);
 }
 
 }  // extern "C"

@@ -135,6 +135,93 @@ __device__ __forceinline__ u4_t tq2_fp4(uint32_t w0, uint32_t w1) {
   return b;
 }
 
+// Which in-group weight (8u + e: k = 32u + 8q + e for lane quarter q) feeds
+// fp4 nibble n of a lane's operand (the inverses of q1_fp4 / tq2_fp4 over the
+// bit positions of device layout v1).
+__device__ constexpr int fp4_src(int fmt, int n) {
+  const int d = n / 8, i = n % 8;
+  if (fmt == 1) {
+    const int pbit = 4 * i + 3 - d;
+    const int rem = 15 - pbit % 16;
+    return 8 * (rem / 4) + (pbit / 16) + 2 * (rem % 2) + 4 * ((rem / 2) % 2);
+  }
+  const int pos = 4 * i + 2 - 2 * (d % 2);
+  const int rem = 14 - pos % 16;
+  return 8 * (2 * (d / 2) + rem / 8) + (pos / 16) + 2 * ((rem % 8) / 2);
+}
+
+// The 32 bf16 values of one lane quarter q of a group (k = 32u + 8q + e) as
+// two fp8 pieces in nibble order: h0/l0 hold nibbles 0..15 and h1/l1 nibbles
+// 16..31 (the A operand's hardware k 32q + n), sb the E8M0 scale.
+struct XQuarter {
+  u4_t h0, h1, l0, l1;
+  uint8_t sb;
+};
+
+// Those 32 values are the 32 k of one E8M0 block of the B operand, so one
+// scale S = 2^(sb - 127) covers them.  sb puts the block's largest magnitude
+// in [128, 256) (below the fp8 maximum 448, so no piece can overflow); hi =
+// fp8(x / S) and lo = fp8(x / S - hi), both rounded to nearest even.  A bf16
+// value has 8 significant bits and each piece 4, so x = S (hi + lo) exactly
+// unless x lies more than 2^10 below the block's largest value (then the
+// error is below 2^-17 of it).  A block holding inf or nan gets the nan
+// scale 0xFF.  x[u] holds the 8 values x[m][128 g + 32 u + 8 q .. + 8].
+template <int FMT>
+__device__ __forceinline__ void split_x_regs(const u4_t (&x)[4], XQuarter &o) {
+  uint32_t v[16];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    v[4 * u + 0] = x[u].x;
+    v[4 * u + 1] = x[u].y;
+    v[4 * u + 2] = x[u].z;
+    v[4 * u + 3] = x[u].w;
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = max(mx, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+  const int ef = int(mx >> 7);  // exponent field of the largest magnitude
+  const int sb = ef == 255 ? 255 : max(ef - 7, 0);
+  const float mul = __builtin_bit_cast(float, uint32_t(254 - min(sb, 253)) << 23);  // 2^(127 - sb)
+  int hi[8], lo[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float f[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int sidx = fp4_src(FMT, 4 * w + b);  // 8u + e
+      const uint32_t word = v[sidx / 2];
+      f[b] = __builtin_bit_cast(float, (sidx & 1) ? (word & 0xFFFF0000u) : (word << 16)) * mul;
+    }
+    hi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    hi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], hi[w], true);
+    const float r0 = f[0] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 0);
+    const float r1 = f[1] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 1);
+    const float r2 = f[2] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 2);
+    const float r3 = f[3] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 3);
+    lo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+    lo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, lo[w], true);
+  }
+  o.h0 = u4_t{uint32_t(hi[0]), uint32_t(hi[1]), uint32_t(hi[2]), uint32_t(hi[3])};
+  o.h1 = u4_t{uint32_t(hi[4]), uint32_t(hi[5]), uint32_t(hi[6]), uint32_t(hi[7])};
+  o.l0 = u4_t{uint32_t(lo[0]), uint32_t(lo[1]), uint32_t(lo[2]), uint32_t(lo[3])};
+  o.l1 = u4_t{uint32_t(lo[4]), uint32_t(lo[5]), uint32_t(lo[6]), uint32_t(lo[7])};
+  o.sb = uint8_t(sb);
+}
+
+// The same from memory: src points at x[m][128 g + 8 q]; in == false gives
+// zeros (src must still be a readable address).
+template <int FMT>
+__device__ __forceinline__ void split_x_quarter(const uint16_t *src, bool in, XQuarter &o) {
+  u4_t x[4];
+  const u4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const u4_t v = *reinterpret_cast<const u4_t *>(src + 32 * u);
+    x[u] = in ? v : z;
+  }
+  split_x_regs<FMT>(x, o);
+}
+
 __device__ __forceinline__ float half_to_float(uint16_t h) {
   return float(__builtin_bit_cast(_Float16, h));
 }

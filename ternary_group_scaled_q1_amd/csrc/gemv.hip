@@ -36,6 +36,7 @@
 // a fixed order, so results are deterministic.  All control flow that
 // decides loads, MFMAs and barriers is wave-uniform.
 #include "device.hpp"
+#include "gemv_common.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
 
@@ -80,10 +81,8 @@ inline LdsMap lds_map(int MTS, int S, int SC, int R, int E) {
   return m;
 }
 
-// fp8 x fp4 path: per group, 2*MP A rows of kRowBytes (128 bytes of pieces
-// in lane order + 16 bytes that spread the rows over the LDS banks), then
-// MP*4 E8M0 scale bytes per group.
-constexpr int kRowBytes = 144;
+// fp8 x fp4 path: per group, 2*MP A rows of kRowBytes (gemv_common.hpp),
+// then MP*4 E8M0 scale bytes per group.
 
 inline LdsMap lds_map_fp4(int MP, int S, int SC, int R, int E) {
   LdsMap m;
@@ -99,31 +98,13 @@ inline LdsMap lds_map_fp4(int MP, int S, int SC, int R, int E) {
   return m;
 }
 
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Which in-group weight (8u + e: k = 32u + 8q + e for lane quarter q) feeds
-// fp4 nibble n of a lane's operand (the inverses of q1_fp4 / tq2_fp4 over the
-// bit positions of device layout v1).
-__device__ constexpr int fp4_src(int fmt, int n) {
-  const int d = n / 8, i = n % 8;
-  if (fmt == 1) {
-    const int pbit = 4 * i + 3 - d;
-    const int rem = 15 - pbit % 16;
-    return 8 * (rem / 4) + (pbit / 16) + 2 * (rem % 2) + 4 * ((rem / 2) % 2);
-  }
-  const int pos = 4 * i + 2 - 2 * (d % 2);
-  const int rem = 14 - pos % 16;
-  return 8 * (2 * (d / 2) + rem / 8) + (pos / 16) + 2 * ((rem % 8) / 2);
-}
-
-// Stage chunks [c0, c0 + nc) of x for the fp8 x fp4 path.  One thread per
-// (token slot m, group, lane quarter q): the 32 values of that quarter
-// (k = 32u + 8q + e) are the 32 k of one E8M0 block of the B operand, so one
-// scale S = 2^(E - 127) covers them.  E puts the block's largest magnitude in
-// [128, 256) (below the fp8 maximum 448, so no piece can overflow); hi =
-// fp8(x / S) and lo = fp8(x / S - hi), both rounded to nearest even.  A block
-// holding inf or nan gets the nan scale 0xFF.  Tokens m >= M and groups past
-// K stage as zeros.
+// Stage chunks [c0, c0 + nc) of x for the fp8 x fp4 path: one thread per
+// (token slot m, group, lane quarter q) splits that quarter's 32 values
+// (split_x_quarter) into A rows 2m (hi) and 2m + 1 (lo) of the group and
+// its E8M0 scale byte.  The quarter's values sit at hardware k 32q + n; the
+// A operand holds k < 64 in bytes 0..15 and k >= 64 in bytes 16..31 of lane
+// quarter (k % 64) / 16, so nibbles 0..15 go to lane quarter 2(q % 2) and
+// 16..31 to 2(q % 2) + 1.  Tokens m >= M and groups past K stage as zeros.
 template <int FMT, int MP>
 __device__ void stage_fp4(const GemvParams &p, char *lds, int c0, int nc) {
   const int g0 = 4 * c0;
@@ -133,54 +114,15 @@ __device__ void stage_fp4(const GemvParams &p, char *lds, int c0, int nc) {
     const int gl = rest % (4 * nc), m = rest / (4 * nc);
     const bool in = m < p.M && g0 + gl < p.G;
     const uint16_t *src = p.X + (in ? (int64_t)m * p.K + 128 * (g0 + gl) + 8 * q : 0);
-    uint32_t v[16];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u4_t o = *reinterpret_cast<const u4_t *>(src + 32 * u);
-      v[4 * u + 0] = in ? o.x : 0u;
-      v[4 * u + 1] = in ? o.y : 0u;
-      v[4 * u + 2] = in ? o.z : 0u;
-      v[4 * u + 3] = in ? o.w : 0u;
-    }
-    uint32_t mx = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = max(mx, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
-    const int ef = int(mx >> 7);  // exponent field of the largest magnitude
-    const int sb = ef == 255 ? 255 : max(ef - 7, 0);
-    const float mul = __builtin_bit_cast(float, uint32_t(254 - min(sb, 253)) << 23);  // 2^(127 - sb)
-    int hi[8], lo[8];
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      float f[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int sidx = fp4_src(FMT, 4 * w + b);  // 8u + e
-        const uint32_t word = v[sidx / 2];
-        f[b] = __builtin_bit_cast(float, (sidx & 1) ? (word & 0xFFFF0000u) : (word << 16)) * mul;
-      }
-      hi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-      hi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], hi[w], true);
-      const float r0 = f[0] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 0);
-      const float r1 = f[1] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 1);
-      const float r2 = f[2] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 2);
-      const float r3 = f[3] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 3);
-      lo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
-      lo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, lo[w], true);
-    }
-    // Nibble n of the B lane quarter q sits at hardware k = 32q + n; A holds
-    // k < 64 in bytes 0..15 and k >= 64 in bytes 16..31 of lane quarter
-    // (k % 64) / 16.
+    XQuarter xq;
+    split_x_quarter<FMT>(src, in, xq);
     char *row = lds + p.off_x + (gl * 2 * MP + 2 * m) * kRowBytes;
     const int qa = 2 * (q & 1), half = 16 * (q >> 1);
-    const u4_t h0 = {uint32_t(hi[0]), uint32_t(hi[1]), uint32_t(hi[2]), uint32_t(hi[3])};
-    const u4_t h1 = {uint32_t(hi[4]), uint32_t(hi[5]), uint32_t(hi[6]), uint32_t(hi[7])};
-    const u4_t l0 = {uint32_t(lo[0]), uint32_t(lo[1]), uint32_t(lo[2]), uint32_t(lo[3])};
-    const u4_t l1 = {uint32_t(lo[4]), uint32_t(lo[5]), uint32_t(lo[6]), uint32_t(lo[7])};
-    *reinterpret_cast<u4_t *>(row + qa * 32 + half) = h0;
-    *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = h1;
-    *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = l0;
-    *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = l1;
-    reinterpret_cast<uint8_t *>(lds + p.off_corr)[(gl * MP + m) * 4 + q] = uint8_t(sb);
+    *reinterpret_cast<u4_t *>(row + qa * 32 + half) = xq.h0;
+    *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = xq.h1;
+    *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = xq.l0;
+    *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = xq.l1;
+    reinterpret_cast<uint8_t *>(lds + p.off_corr)[(gl * MP + m) * 4 + q] = xq.sb;
   }
 }
 
@@ -221,74 +163,6 @@ __device__ void stage_x(const GemvParams &p, char *lds, int c0, int nc) {
     for (int idx = threadIdx.x; idx < nc * 4 * (16 - MTS); idx += kThreads) {
       const int gs = idx / (16 - MTS), m = MTS + idx % (16 - MTS);
       corr[gs * 16 + m] = 0.f;
-    }
-  }
-}
-
-// Packed words and scales of R row tiles x one chunk (4 groups), for one lane.
-template <int FMT, int R>
-struct Unit {
-  static constexpr int WPU = FMT == 1 ? 4 : 8;
-  uint32_t w[R][WPU];
-  uint32_t s[R][2];  // 4 FP16 scales
-};
-
-// Loads are issued without per-lane branches (ragged tiles clamp their
-// addresses and zero the values afterwards): a divergent branch around a
-// load makes the compiler wait for every outstanding load at the join, which
-// would drain the prefetch ring.
-template <int FMT, int R>
-__device__ __forceinline__ void load_unit(const GemvParams &p, Unit<FMT, R> &u, int t0, int c, bool valid) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15, q = lane >> 4;
-  constexpr int WPU = Unit<FMT, R>::WPU;
-  const int64_t unit = FMT == 1 ? 16 : 32;
-  const int Gc = uni(min(4, p.G - 4 * c));
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int t = uni(t0 + r);
-    if (!valid || t >= p.tiles) {  // wave-uniform
-#pragma unroll
-      for (int i = 0; i < WPU; ++i) u.w[r][i] = 0;
-      u.s[r][0] = u.s[r][1] = 0;
-      continue;
-    }
-    const int RT = uni(min(16, p.N - 16 * t));
-    const uint8_t *blk = p.W + 16 * (int64_t)t * p.G * unit + (int64_t)RT * 4 * c * unit;
-    if (RT == 16 && Gc == 4 && (p.G & 3) == 0) {  // wave-uniform fast path
-      const u4_t v0 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk) + lane);
-      u.w[r][0] = v0.x; u.w[r][1] = v0.y; u.w[r][2] = v0.z; u.w[r][3] = v0.w;
-      if constexpr (FMT == 2) {
-        const u4_t v1 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk + 1024) + lane);
-        u.w[r][4] = v1.x; u.w[r][5] = v1.y; u.w[r][6] = v1.z; u.w[r][7] = v1.w;
-      }
-      const u2_t sv = *reinterpret_cast<const u2_t *>(p.Sc + (int64_t)(16 * t + j) * p.G + 4 * c);
-      u.s[r][0] = sv.x; u.s[r][1] = sv.y;
-    } else {
-      const bool row_ok = j < RT;
-      const int jj = min(j, RT - 1);
-      const uint32_t *base = reinterpret_cast<const uint32_t *>(blk);
-      const uint16_t *srow = p.Sc + (int64_t)(16 * t + jj) * p.G + 4 * c;
-      uint32_t h[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int gg = min(g, Gc - 1);
-        const bool ok = row_ok && g < Gc;
-        if constexpr (FMT == 1) {
-          const uint32_t w = base[(q * RT + jj) * Gc + gg];
-          u.w[r][g] = ok ? w : 0u;
-        } else {
-          const int hh = gg >> 1, Gh = min(2, Gc - 2 * hh);
-          const uint32_t *hb = base + RT * 16 * hh + ((q * RT + jj) * Gh + (gg - 2 * hh)) * 2;
-          const uint32_t w0 = hb[0], w1 = hb[1];
-          u.w[r][2 * g + 0] = ok ? w0 : 0u;
-          u.w[r][2 * g + 1] = ok ? w1 : 0u;
-        }
-        const uint32_t sv = srow[gg];
-        h[g] = ok ? sv : 0u;
-      }
-      u.s[r][0] = h[0] | (h[1] << 16);
-      u.s[r][1] = h[2] | (h[3] << 16);
     }
   }
 }
@@ -628,24 +502,42 @@ hipError_t launch_mt(const LaunchArgs &a) {
   return hipGetLastError();
 }
 
+// Path choice for bf16 x, from timings of the decode shapes on MI355X:
+//  * one token, or small x: the workgroup-staged kernel above (x of the
+//    whole K fits in LDS at once, no second kernel stage);
+//  * more tokens with a long K, or 9..16 tokens: the 2-D split (row blocks x
+//    K ranges, x converted once per block, gemv_split.hip), which needs the
+//    caller's workspace to split K across workgroups;
+//  * 9..16 tokens on a small matrix: x loaded straight into registers
+//    (gemv_wide.hip).
 template <int FMT, bool BF>
 hipError_t launch_fmt(const LaunchArgs &a) {
   if constexpr (BF) {
-    // fp8 x fp4 path: exact fp8 pieces of bf16 x, up to 8 tokens.
     constexpr int RB = FMT == 1 ? 4 : 3;
+    const bool ws_ok = a.ws && a.ws_bytes >= gemv_split_workspace_bytes(a.M, a.N, a.K);
+    if (a.M > 8) {
+      if (a.N <= 8192 && a.K <= 8192) return launch_gemv_wide(a);
+      if (ws_ok || a.N >= 65536) return launch_gemv_split(a);
+      return launch_gemv_wide(a);
+    }
+    const bool split = ws_ok && a.M >= 2 && (a.K >= 8192 || (a.M >= 4 && a.N < 65536));
+    if (split) return launch_gemv_split(a);
     if (a.M <= 1) return launch_mt<FMT, BF, 1, true, 2, RB>(a);
     if (a.M <= 2) return launch_mt<FMT, BF, 2, true, 2, RB>(a);
     if (a.M <= 4) return launch_mt<FMT, BF, 4, true, 2, RB>(a);
-    if (a.M <= 8) return launch_mt<FMT, BF, 8, true, 2, RB>(a);
-    return launch_mt<FMT, BF, 16, false, 1, 2>(a);
+    return launch_mt<FMT, BF, 8, true, 2, RB>(a);
   } else {
     if (a.M <= 1) return launch_mt<FMT, BF, 1, false, 1, 2>(a);
     if (a.M <= 4) return launch_mt<FMT, BF, 4, false, 1, 2>(a);
-    return launch_mt<FMT, BF, 16, false, 1, 2>(a);
+    return launch_gemv_wide(a);
   }
 }
 
 }  // namespace
+
+int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+  return fmt == 3 ? 0 : gemv_split_workspace_bytes(M, N, K);
+}
 
 hipError_t launch_gemv(const LaunchArgs &a) {
   // Token blocks of at most 16 rows share one pass over the weights.

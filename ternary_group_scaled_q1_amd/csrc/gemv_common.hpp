@@ -1,0 +1,86 @@
+// Pieces shared by the GEMV kernels: wave-uniform values, the per-lane unit
+// of packed weights (R row tiles x one chunk of 4 groups in device layout v1)
+// and its branch-free load.
+#pragma once
+#include "device.hpp"
+#include "layout.hpp"
+
+namespace lowbit {
+namespace {
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// One A row of a group in the fp8 x fp4 path's LDS staging: 128 bytes of
+// pieces in lane order plus 16 bytes that spread the rows over the LDS banks.
+constexpr int kRowBytes = 144;
+
+// Packed words and scales of R row tiles x one chunk (4 groups), for one lane.
+template <int FMT, int R>
+struct Unit {
+  static constexpr int WPU = FMT == 1 ? 4 : 8;
+  uint32_t w[R][WPU];
+  uint32_t s[R][2];  // 4 FP16 scales
+};
+
+// Loads are issued without per-lane branches (ragged tiles clamp their
+// addresses and zero the values afterwards): a divergent branch around a
+// load makes the compiler wait for every outstanding load at the join, which
+// would drain the prefetch ring.  P provides W, Sc, N, G and tiles.
+template <int FMT, int R, class P>
+__device__ __forceinline__ void load_unit(const P &p, Unit<FMT, R> &u, int t0, int c, bool valid) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  constexpr int WPU = Unit<FMT, R>::WPU;
+  const int64_t unit = FMT == 1 ? 16 : 32;
+  const int Gc = uni(min(4, p.G - 4 * c));
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = uni(t0 + r);
+    if (!valid || t >= p.tiles) {  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < WPU; ++i) u.w[r][i] = 0;
+      u.s[r][0] = u.s[r][1] = 0;
+      continue;
+    }
+    const int RT = uni(min(16, p.N - 16 * t));
+    const uint8_t *blk = p.W + 16 * (int64_t)t * p.G * unit + (int64_t)RT * 4 * c * unit;
+    if (RT == 16 && Gc == 4 && (p.G & 3) == 0) {  // wave-uniform fast path
+      const u4_t v0 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk) + lane);
+      u.w[r][0] = v0.x; u.w[r][1] = v0.y; u.w[r][2] = v0.z; u.w[r][3] = v0.w;
+      if constexpr (FMT == 2) {
+        const u4_t v1 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk + 1024) + lane);
+        u.w[r][4] = v1.x; u.w[r][5] = v1.y; u.w[r][6] = v1.z; u.w[r][7] = v1.w;
+      }
+      const u2_t sv = *reinterpret_cast<const u2_t *>(p.Sc + (int64_t)(16 * t + j) * p.G + 4 * c);
+      u.s[r][0] = sv.x; u.s[r][1] = sv.y;
+    } else {
+      const bool row_ok = j < RT;
+      const int jj = min(j, RT - 1);
+      const uint32_t *base = reinterpret_cast<const uint32_t *>(blk);
+      const uint16_t *srow = p.Sc + (int64_t)(16 * t + jj) * p.G + 4 * c;
+      uint32_t h[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int gg = min(g, Gc - 1);
+        const bool ok = row_ok && g < Gc;
+        if constexpr (FMT == 1) {
+          const uint32_t w = base[(q * RT + jj) * Gc + gg];
+          u.w[r][g] = ok ? w : 0u;
+        } else {
+          const int hh = gg >> 1, Gh = min(2, Gc - 2 * hh);
+          const uint32_t *hb = base + RT * 16 * hh + ((q * RT + jj) * Gh + (gg - 2 * hh)) * 2;
+          const uint32_t w0 = hb[0], w1 = hb[1];
+          u.w[r][2 * g + 0] = ok ? w0 : 0u;
+          u.w[r][2 * g + 1] = ok ? w1 : 0u;
+        }
+        const uint32_t sv = srow[gg];
+        h[g] = ok ? sv : 0u;
+      }
+      u.s[r][0] = h[0] | (h[1] << 16);
+      u.s[r][1] = h[2] | (h[3] << 16);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace lowbit

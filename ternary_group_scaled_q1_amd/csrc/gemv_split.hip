@@ -1,0 +1,400 @@
+// Decode GEMV on the fp8 x fp4 matrix instructions with a 2-D work split:
+// Y[m][n] = sum_k X[m][k] t[n][k] s[n][k/128], bf16 x, up to 16 tokens.
+//
+// A workgroup owns a row block (8 waves x R row tiles of 16 rows) and one
+// K range of the matrix.  It converts the x of its K range once into LDS as
+// exact fp8 pieces with per-32 E8M0 scales (split_x_quarter in device.hpp),
+// in passes of GP groups that are double buffered: while the waves multiply
+// pass p, the raw bf16 x of pass p + 1 is already in registers and is
+// converted into the other buffer.  Every x value staged is then used by the
+// 8R row tiles of the block, so the activations cross the L2 once per block
+// instead of once per tile (16 tokens of x are as large as the weights that
+// use them).
+//
+// Small matrices have too few row blocks to fill the chip, so their K is cut
+// into KS ranges handled by different workgroups.  Each writes its fp32
+// partial sums to the caller's workspace and increments the block's arrival
+// counter; the last of the KS workgroups adds the KS partials in range
+// order, which makes the result independent of which finished last, writes
+// Y and resets the counter to 0.  The XCDs' L2 caches are not coherent with
+// each other, and an agent-scope fence would write back and invalidate a
+// whole L2 per workgroup, so the partials instead travel as agent-scope
+// atomic stores and loads (emitted with the sc1 bit: they go to and come
+// from the device's coherence point); each thread waits for its stores to
+// complete and the workgroup synchronises before one thread increments the
+// counter, and the last workgroup reads only after it saw the count.
+//
+// Per (row tile, group) the weights decode to fp4 (q1: +-1, tq2: 2t) with a
+// shift and one bitwise op per 8 weights, one scaled 16x16x128 MFMA per
+// block of 8 tokens takes x as A rows (token, piece), and the group's FP16
+// scale is applied to the fresh fp32 tile (exact products), as on the
+// aberweb.com page, section 4.1: the signs are decoded inside the kernel and
+// no dense weight tensor exists.
+#include "device.hpp"
+#include "gemv_common.hpp"
+#include "kernels.hpp"
+#include "layout.hpp"
+
+namespace lowbit {
+
+namespace {
+
+constexpr int kSWaves = 8;
+constexpr int kSThreads = 64 * kSWaves;
+
+struct SplitParams {
+  const uint8_t *W;    // plane A
+  const uint16_t *Sc;  // plane B: FP16 scales [N][G]
+  const uint16_t *X;   // [M][K]
+  void *Y;             // [M][N]
+  float *part;         // [KS][M][N] partial sums (KS > 1)
+  unsigned *count;     // [row_blocks] arrival counters, 0 between calls
+  int M, N, K, G, tiles;
+  int GK;          // groups per K range (a multiple of 4 when KS > 1)
+  int KS;          // K ranges
+  int GP;          // groups per staging pass (a multiple of 4)
+  int row_blocks;  // ceil(tiles / (8 R))
+  int y_f16;
+  int buf_bytes;   // LDS bytes of one staging buffer
+};
+
+// LDS of one staging buffer: GP groups x 2*MP A rows, then GP*MP*4 scale bytes.
+__host__ __device__ constexpr int split_buf_bytes(int MP, int GP) {
+  return (GP * 2 * MP * kRowBytes + GP * MP * 4 + 15) / 16 * 16;
+}
+
+// Raw x of one (token, group, lane quarter) item, held between its load and
+// its conversion.
+struct RawQ {
+  u4_t v[4];
+};
+
+template <int MP>
+__device__ __forceinline__ void load_raw(const SplitParams &p, RawQ &r, int g0, int np_groups, int item, bool &live) {
+  const int q = item & 3, rest = item >> 2;
+  const int gl = rest % p.GP, m = rest / p.GP;
+  live = item < MP * p.GP * 4;
+  const bool in = live && m < p.M && gl < np_groups;
+  const uint16_t *src = p.X + (in ? (int64_t)m * p.K + 128 * (g0 + gl) + 8 * q : 0);
+  const u4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const u4_t x = *reinterpret_cast<const u4_t *>(src + 32 * u);
+    r.v[u] = in ? x : z;
+  }
+}
+
+template <int FMT, int MP>
+__device__ __forceinline__ void convert_raw(const SplitParams &p, const RawQ &r, char *buf, int item) {
+  const int q = item & 3, rest = item >> 2;
+  const int gl = rest % p.GP, m = rest / p.GP;
+  XQuarter xq;
+  split_x_regs<FMT>(r.v, xq);
+  char *row = buf + (gl * 2 * MP + 2 * m) * kRowBytes;
+  const int qa = 2 * (q & 1), half = 16 * (q >> 1);
+  *reinterpret_cast<u4_t *>(row + qa * 32 + half) = xq.h0;
+  *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = xq.h1;
+  *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = xq.l0;
+  *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = xq.l1;
+  reinterpret_cast<uint8_t *>(buf + p.GP * 2 * MP * kRowBytes)[(gl * MP + m) * 4 + q] = xq.sb;
+}
+
+// One chunk (4 groups at buffer group offset gb) for R tiles.  Lane 16qa + r
+// of token block tb reads A row 16 tb + r (token 8 tb + r / 2, piece r % 2).
+template <int FMT, int MP, int R, int TB>
+__device__ __forceinline__ void compute_chunk(const SplitParams &p, const char *buf, const Unit<FMT, R> &u, int gb,
+                                              int ng, float (&yacc)[R][TB][4]) {
+  constexpr int ROWS = 2 * MP < 16 ? 2 * MP : 16;  // A rows per token block
+  const int lane = threadIdx.x & 63, qa = lane >> 4, r = lane & 15;
+  const bool arow = r < ROWS;
+  const int rr = arow ? r : 0;
+  const u4_t z = {0u, 0u, 0u, 0u};
+  const uint8_t *scb = reinterpret_cast<const uint8_t *>(buf + p.GP * 2 * MP * kRowBytes);
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    if (gi >= ng) break;  // wave-uniform: groups past K in the last chunk
+    const int gl = gb + gi;
+    u4_t a0[TB], a1[TB];
+    int sa[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const char *xa = buf + (gl * 2 * MP + 16 * tb + rr) * kRowBytes + qa * 32;
+      const u4_t v0 = *reinterpret_cast<const u4_t *>(xa);
+      const u4_t v1 = *reinterpret_cast<const u4_t *>(xa + 16);
+      a0[tb] = arow ? v0 : z;
+      a1[tb] = arow ? v1 : z;
+      sa[tb] = scb[(gl * MP + 8 * tb + (rr >> 1)) * 4 + qa];
+    }
+#pragma unroll
+    for (int r2 = 0; r2 < R; ++r2) {
+      u4_t b;
+      if constexpr (FMT == 1) b = q1_fp4(u.w[r2][gi]);
+      else b = tq2_fp4(u.w[r2][2 * gi], u.w[r2][2 * gi + 1]);
+      const float s = half_to_float(uint16_t(u.s[r2][gi >> 1] >> (16 * (gi & 1))));
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const f4_t d = mfma_f8f4(a0[tb], a1[tb], b, sa[tb]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yacc[r2][tb][e] = fmaf(s, d[e], yacc[r2][tb][e]);
+      }
+    }
+  }
+}
+
+// Accumulator element e of lane 16qa + j, token block tb, is A row 4qa + e:
+// token 8 tb + 2 qa + e / 2, piece e % 2.  The two pieces add here.
+template <int R, int TB>
+__device__ __forceinline__ void token_sums(const float (&yacc)[R][TB][4], float (&y)[R][TB][2]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      y[r][tb][0] = yacc[r][tb][0] + yacc[r][tb][1];
+      y[r][tb][1] = yacc[r][tb][2] + yacc[r][tb][3];
+    }
+}
+
+template <int FMT, int MP, int R>
+__global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p) {
+  constexpr int TB = MP > 8 ? 2 : 1;
+  extern __shared__ __align__(16) char lds[];
+  __shared__ int last_flag;
+  const int wave = uni(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ks = blockIdx.x % p.KS, rb = blockIdx.x / p.KS;
+  const int g0 = ks * p.GK;
+  const int ng = uni(min(p.GK, p.G - g0));  // groups of this K range
+  const int nchunks = (ng + 3) / 4;
+  const int c0 = g0 / 4;
+  const int t0 = uni(rb * 8 * R + wave * R);
+  const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
+
+  // Weights: two chunks in flight, in two named units.
+  Unit<FMT, R> u0, u1;
+  load_unit<FMT, R>(p, u0, t0, c0, true);
+  if (nchunks > 1) load_unit<FMT, R>(p, u1, t0, c0 + 1, true);
+
+  // x: pass 0 staged now; the raw x of pass 1 goes out before pass 0 is used.
+  const int npass = (ng + p.GP - 1) / p.GP;
+  RawQ raw;
+  bool live;
+  load_raw<MP>(p, raw, g0, min(p.GP, ng), threadIdx.x, live);
+  if (live) convert_raw<FMT, MP>(p, raw, lds, threadIdx.x);
+  __syncthreads();
+
+  float yacc[R][TB][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yacc[r][tb][e] = 0.f;
+
+  int c = 0;  // chunk index inside the K range
+  for (int ps = 0; ps < npass; ++ps) {
+    const int pg0 = ps * p.GP;  // first group of this pass (range-relative)
+    const int png = min(p.GP, ng - pg0);
+    char *cur = lds + (ps & 1) * p.buf_bytes;
+    char *nxt = lds + ((ps + 1) & 1) * p.buf_bytes;
+    const bool more = ps + 1 < npass;
+    if (more) load_raw<MP>(p, raw, g0 + pg0 + p.GP, min(p.GP, ng - pg0 - p.GP), threadIdx.x, live);
+    // Chunks of this pass (GP is a multiple of 4, so passes hold whole chunks).
+    for (int cc = 0; cc < (png + 3) / 4; cc += 2) {
+      compute_chunk<FMT, MP, R, TB>(p, cur, u0, 4 * cc, min(4, png - 4 * cc), yacc);
+      if (c + 2 < nchunks) load_unit<FMT, R>(p, u0, t0, c0 + c + 2, true);
+      ++c;
+      if (cc + 1 >= (png + 3) / 4) {
+        // Odd chunk count in this pass: the next pass starts on u1.
+        Unit<FMT, R> t = u0;
+        u0 = u1;
+        u1 = t;
+        break;
+      }
+      compute_chunk<FMT, MP, R, TB>(p, cur, u1, 4 * (cc + 1), min(4, png - 4 * (cc + 1)), yacc);
+      if (c + 2 < nchunks) load_unit<FMT, R>(p, u1, t0, c0 + c + 2, true);
+      ++c;
+    }
+    if (more && live) convert_raw<FMT, MP>(p, raw, nxt, threadIdx.x);
+    __syncthreads();
+  }
+
+  float ys[R][TB][2];
+  token_sums<R, TB>(yacc, ys);
+  const int j = lane & 15, qa = lane >> 4;
+  if (p.KS == 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int n = 16 * (t0 + r) + j;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int m = 8 * tb + 2 * qa + tt;
+          if (m >= p.M) continue;
+          const float v = ys[r][tb][tt] * mul;
+          if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
+          else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+        }
+    }
+    return;
+  }
+
+  // K split across workgroups: publish this range's partial sums.
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = 16 * (t0 + r) + j;
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int m = 8 * tb + 2 * qa + tt;
+        if (m >= p.M) continue;
+        __hip_atomic_store(p.part + ((int64_t)ks * p.M + m) * p.N + n, ys[r][tb][tt], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_flag = __hip_atomic_fetch_add(p.count + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                unsigned(p.KS - 1);
+  __syncthreads();
+  if (!last_flag) return;
+  // Last workgroup of the block: Y = sum over ranges in range order.
+  const int n0 = rb * 8 * R * 16;
+  const int rows = min(8 * R * 16, p.N - n0);
+  for (int idx = threadIdx.x; idx < p.M * rows; idx += kSThreads) {
+    const int m = idx / rows, n = n0 + idx % rows;
+    float v = 0.f;
+    for (int k2 = 0; k2 < p.KS; ++k2)
+      v += __hip_atomic_load(p.part + ((int64_t)k2 * p.M + m) * p.N + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v *= mul;
+    if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
+    else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(p.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Largest pass (groups, a multiple of 4) whose x fits in one item per thread
+// and whose two buffers fit in 64 KB of LDS.
+inline int pass_groups(int MP, int G) {
+  int gp = 4;
+  while (gp + 4 <= 128 && MP * (gp + 4) * 4 <= kSThreads && 2 * split_buf_bytes(MP, gp + 4) <= 64 * 1024) gp += 4;
+  const int g4 = (G + 3) / 4 * 4;
+  return gp < g4 ? gp : g4;
+}
+
+// Workspace: kMaxCounters arrival counters at offset 0 (a fixed place, so
+// that calls of any shape sharing one workspace find them zero), then the
+// partial sums.  K is cut into at most kMaxKS ranges, and only while the
+// partials of all ranges stay within kMaxPartBytes (large matrices fill the
+// chip with row blocks alone, and their partials would cost as much traffic
+// as the weights) and the row blocks have counters.
+constexpr int kMaxKS = 16;
+constexpr int64_t kMaxPartBytes = 8 << 20;
+constexpr int kMaxCounters = 8192;
+constexpr int64_t kPartOffset = kMaxCounters * 4;
+
+int64_t split_ws_bytes(int64_t M, int64_t N, int KS) {
+  return KS <= 1 ? 0 : kPartOffset + (int64_t)KS * M * N * 4;
+}
+
+struct SplitPlan {
+  SplitParams p;
+  int grid = 0;
+  int lds = 0;
+  double cost = 1e300;
+};
+
+// Per-wave work of the busiest workgroup slot, in (tile, group) units, with
+// charges for staging x, for workgroup start-up and for the partial sums.
+template <int FMT, int MP, int R>
+void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
+  SplitParams p{};
+  p.W = a.W;
+  p.Sc = reinterpret_cast<const uint16_t *>(a.W + plane_a_bytes(a.fmt, a.N, a.K));
+  p.X = a.X;
+  p.Y = a.Y;
+  p.M = int(a.M); p.N = int(a.N); p.K = int(a.K); p.G = int(a.K / kGroup);
+  p.tiles = int((a.N + 15) / 16);
+  p.y_f16 = a.y_f16;
+  p.row_blocks = (p.tiles + 8 * R - 1) / (8 * R);
+  p.GP = pass_groups(MP, p.G);
+  p.buf_bytes = split_buf_bytes(MP, p.GP);
+  const int lds = 2 * p.buf_bytes;
+  const void *kern = reinterpret_cast<const void *>(&gemv_split_kernel<FMT, MP, R>);
+  const int slots = num_cus() * resident_blocks(kern, kSThreads, lds);
+  for (int GK = 4; GK < p.G + 4; GK += 4) {
+    const int gk = GK < p.G ? GK : p.G;
+    const int KS = (p.G + gk - 1) / gk;
+    if (KS > kMaxKS) continue;
+    if (KS > 1 && (gk % 4 || (int64_t)KS * a.M * a.N * 4 > kMaxPartBytes || p.row_blocks > kMaxCounters ||
+                   split_ws_bytes(a.M, a.N, KS) > ws_bytes))
+      continue;
+    const int64_t wgs = (int64_t)p.row_blocks * KS;
+    const double rounds = double((wgs + slots - 1) / slots);
+    const double stage = 8.0 * ((gk + p.GP - 1) / p.GP);        // per pass: convert + barrier
+    const double work = double(R) * gk * (MP > 8 ? 2.0 : 1.0);   // MFMA sets per wave
+    const double reduce = KS > 1 ? 6.0 + 0.02 * KS * MP * R : 0.0;
+    const double cost = rounds * (work + stage + 12.0 + reduce);
+    if (cost < best.cost) {
+      best.cost = cost;
+      best.p = p;
+      best.p.GK = gk;
+      best.p.KS = KS;
+      best.grid = int(wgs);
+      best.lds = lds;
+    }
+    if (KS == 1) break;
+  }
+}
+
+template <int FMT, int MP>
+hipError_t launch_split_mp(const LaunchArgs &a) {
+  SplitPlan b1, b2, b4;
+  plan_split<FMT, MP, 1>(a, a.ws_bytes, b1);
+  plan_split<FMT, MP, 2>(a, a.ws_bytes, b2);
+  plan_split<FMT, MP, 4>(a, a.ws_bytes, b4);
+  int R = 1;
+  SplitPlan *b = &b1;
+  if (b2.cost < b->cost) { b = &b2; R = 2; }
+  if (b4.cost < b->cost) { b = &b4; R = 4; }
+  if (b->p.KS > 1) {
+    b->p.count = static_cast<unsigned *>(a.ws);
+    b->p.part = reinterpret_cast<float *>(static_cast<char *>(a.ws) + kPartOffset);
+  }
+  if (R == 1) hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
+  else if (R == 2) hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
+  else hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_split_fmt(const LaunchArgs &a) {
+  if (a.M <= 1) return launch_split_mp<FMT, 1>(a);
+  if (a.M <= 2) return launch_split_mp<FMT, 2>(a);
+  if (a.M <= 4) return launch_split_mp<FMT, 4>(a);
+  if (a.M <= 8) return launch_split_mp<FMT, 8>(a);
+  return launch_split_mp<FMT, 16>(a);
+}
+
+}  // namespace
+
+int64_t gemv_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  // The counters plus the largest partial-sum area any plan may use
+  // (16-token launches).
+  const int64_t m = M < 16 ? M : 16;
+  int64_t ks = kMaxPartBytes / (m * N * 4);
+  if (ks > kMaxKS) ks = kMaxKS;
+  if (ks > K / kGroup) ks = K / kGroup;
+  if (ks < 2 || ((N + 15) / 16 + 7) / 8 > kMaxCounters) return 0;
+  return split_ws_bytes(m, N, int(ks));
+}
+
+hipError_t launch_gemv_split(const LaunchArgs &a) {
+  return a.fmt == 1 ? launch_split_fmt<1>(a) : launch_split_fmt<2>(a);
+}
+
+}  // namespace lowbit

@@ -1,0 +1,288 @@
+// Decode GEMV for 9..16 tokens: Y[m][n] = sum_k X[m][k] t[n][k] s[n][k/128].
+//
+// With 16 tokens the activations of one K range are as large as the weights
+// that use them (16 x 5120 bf16 = 160 KB), too large to stage in LDS once per
+// workgroup.  Here every wave loads the A operand of each MFMA straight from
+// memory into registers: lane 16q + j reads the 16 bytes x[j][k0 + 8q .. +8]
+// of the k-step, which the L2 (and the CU's L1 when neighbouring waves walk
+// the same groups) serves to all waves that share the K range.  No LDS
+// staging and no barriers, except one at the end when waves that split K add
+// their partial sums.
+//
+// Unit of work: R row tiles (16 rows each) x one group of 128 weights.  Per
+// unit a lane holds its tiles' packed words of that group (q1: 4 bytes, tq2:
+// 8 bytes per tile), their FP16 scales and 4 x 16 bytes of x; a ring of D
+// units keeps the loads of the next units in flight while one is computed.
+// The weights decode to exact +-1 (q1) or 2t (tq2) f16/bf16 operands with one
+// shift and one bitwise op per pair (device.hpp), four k-steps of
+// v_mfma_f32_16x16x32 fill a fresh fp32 tile per (tile, group), and the
+// group's FP16 scale is applied to it in fp32 (exact products, one rounding
+// per group), as on the aberweb.com page, section 4.1: the signs are decoded
+// inside the kernel and no dense weight tensor exists.
+#include "device.hpp"
+#include "kernels.hpp"
+#include "layout.hpp"
+
+namespace lowbit {
+
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+
+struct WideParams {
+  const uint8_t *W;    // plane A
+  const uint16_t *Sc;  // plane B: FP16 scales [N][G]
+  const uint16_t *X;   // [M][K]
+  void *Y;             // [M][N]
+  int M, N, K, G;
+  int tiles, tilesets;
+  int S;    // waves of a wave-row splitting the groups
+  int GS;   // groups per wave (ceil(G / S))
+  int y_f16;
+};
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int FMT, int R>
+struct WUnit {
+  static constexpr int WPG = FMT == 1 ? 1 : 2;  // packed words per lane per tile and group
+  uint32_t w[R][WPG];
+  uint32_t s[R];   // FP16 scale bits
+  u4_t x[4];       // A operand of the four k-steps
+};
+
+// Loads of one unit, without per-lane branches around them (a divergent
+// branch around a load makes the compiler drain every load in flight at the
+// join).  Ragged tiles clamp their addresses and zero the values afterwards;
+// token rows >= M read row 0 and are zeroed.
+template <int FMT, int R>
+__device__ __forceinline__ void load_wunit(const WideParams &p, WUnit<FMT, R> &u, int t0, int g, bool valid) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  const u4_t z = {0u, 0u, 0u, 0u};
+  if (!valid) {  // wave-uniform
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int i = 0; i < WUnit<FMT, R>::WPG; ++i) u.w[r][i] = 0;
+      u.s[r] = 0;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) u.x[s] = z;
+    return;
+  }
+  const bool tok = j < p.M;
+  const uint16_t *xr = p.X + (tok ? (int64_t)j * p.K : 0) + 128 * g + 8 * q;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const u4_t v = *reinterpret_cast<const u4_t *>(xr + 32 * s);
+    u.x[s] = tok ? v : z;
+  }
+  const int c = g >> 2, gc = g & 3;
+  const int Gc = uni(min(4, p.G - 4 * c));
+  const int64_t unit = FMT == 1 ? 16 : 32;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = uni(t0 + r);
+    if (t >= p.tiles) {  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < WUnit<FMT, R>::WPG; ++i) u.w[r][i] = 0;
+      u.s[r] = 0;
+      continue;
+    }
+    const int RT = uni(min(16, p.N - 16 * t));
+    const bool row_ok = j < RT;
+    const int jj = min(j, RT - 1);
+    const uint32_t *blk =
+        reinterpret_cast<const uint32_t *>(p.W + 16 * (int64_t)t * p.G * unit + (int64_t)RT * 4 * c * unit);
+    if constexpr (FMT == 1) {
+      const uint32_t w = __builtin_nontemporal_load(blk + (q * RT + jj) * Gc + gc);
+      u.w[r][0] = row_ok ? w : 0u;
+    } else {
+      const int hh = gc >> 1, Gh = min(2, Gc - 2 * hh);
+      const u2_t w = __builtin_nontemporal_load(
+          reinterpret_cast<const u2_t *>(blk + RT * 16 * hh + ((q * RT + jj) * Gh + (gc - 2 * hh)) * 2));
+      u.w[r][0] = row_ok ? w.x : 0u;
+      u.w[r][1] = row_ok ? w.y : 0u;
+    }
+    const uint32_t sv = p.Sc[(int64_t)(16 * t + jj) * p.G + g];
+    u.s[r] = row_ok ? sv : 0u;
+  }
+}
+
+template <int FMT, bool BF, int R>
+__device__ __forceinline__ void compute_wunit(const WUnit<FMT, R> &u, float (&yacc)[R][4]) {
+  f4_t acc[R];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      u4_t b;
+      if constexpr (FMT == 1) b = q1_operand_pm1<BF>(u.w[r][0], s);
+      else b = tq2_operand(u.w[r][s >> 1], s);
+      acc[r] = s == 0 ? mfma16x16x32_zero<BF>(u.x[s], b) : mfma16x16x32<BF>(u.x[s], b, acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float sc = half_to_float(uint16_t(u.s[r]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) yacc[r][e] = fmaf(sc, acc[r][e], yacc[r][e]);
+  }
+}
+
+template <int FMT, int R>
+__device__ __forceinline__ void store_wide(const WideParams &p, int t0, const float (&yacc)[R][4]) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = 16 * (t0 + r) + j;
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * q + e;
+      if (m >= p.M) continue;
+      const float v = yacc[r][e] * mul;
+      if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
+      else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+    }
+  }
+}
+
+// The 8 waves of a workgroup form P = 8 / S wave-rows; wave s of a wave-row
+// takes groups [s GS, (s + 1) GS) of each of its tile sets.  Wave-row i of
+// workgroup b handles tile sets b + gridDim.x (i + P it), it = 0, 1, ...
+// Every wave walks the same number of units (missing ones are skipped
+// without loads), so the per-tile-set barrier of the K split is reached by
+// all waves.
+template <int FMT, bool BF, int R, int D>
+__global__ void __launch_bounds__(kThreads, 2) gemv_wide_kernel(WideParams p) {
+  __shared__ float red[kWaves * R * 4 * 64];
+  const int wave = uni(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int S = uni(p.S), P = kWaves / S;
+  const int pr = uni(wave / S), s = uni(wave - pr * S);
+  const int rows_total = gridDim.x * P;
+  const int my_row = pr * gridDim.x + blockIdx.x;
+  const int iters = (p.tilesets + rows_total - 1) / rows_total;
+  const int GS = uni(p.GS);
+  const int total = uni(iters * GS);
+  const int g_begin = s * GS;
+
+  auto tile0 = [&](int i) { return ((i / GS) * rows_total + my_row) * R; };
+  auto group = [&](int i) { return g_begin + i % GS; };
+  auto valid = [&](int i) { return (i / GS) * rows_total + my_row < p.tilesets && group(i) < p.G; };
+
+  WUnit<FMT, R> ring[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) load_wunit<FMT, R>(p, ring[d], uni(tile0(d)), uni(group(d)), d < total && valid(d));
+
+  float yacc[R][4];
+  for (int i0 = 0; i0 < total; i0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = i0 + d;
+      if (i >= total) break;
+      const int nx = i + D - 1;
+      load_wunit<FMT, R>(p, ring[(d + D - 1) % D], uni(tile0(nx)), uni(group(nx)), nx < total && valid(nx));
+      const int k = i % GS;
+      if (k == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yacc[r][e] = 0.f;
+      }
+      if (valid(i)) compute_wunit<FMT, BF, R>(ring[d], yacc);
+      if (k == GS - 1) {
+        const int t0 = uni(tile0(i));
+        const bool ts_ok = (i / GS) * rows_total + my_row < p.tilesets;
+        if (S == 1) {
+          if (ts_ok) store_wide<FMT, R>(p, t0, yacc);
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[((wave * R + r) * 4 + e) * 64 + lane] = yacc[r][e];
+          __syncthreads();
+          if (s == 0 && ts_ok) {
+            float tot[R][4];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float v = 0.f;
+                for (int s2 = 0; s2 < S; ++s2) v += red[(((pr * S + s2) * R + r) * 4 + e) * 64 + lane];
+                tot[r][e] = v;
+              }
+            store_wide<FMT, R>(p, t0, tot);
+          }
+          __syncthreads();
+        }
+      }
+    }
+  }
+}
+
+// Plan: the (S, grid) with the smallest per-wave work (tile sets per
+// wave-row x R x groups per wave), with a small charge for the K-split
+// barrier.
+template <class Kern>
+double plan_wide(const LaunchArgs &a, int R, Kern kernel, WideParams &p, int &grid) {
+  p = WideParams{};
+  p.W = a.W;
+  p.Sc = reinterpret_cast<const uint16_t *>(a.W + plane_a_bytes(a.fmt, a.N, a.K));
+  p.X = a.X;
+  p.Y = a.Y;
+  p.M = int(a.M); p.N = int(a.N); p.K = int(a.K); p.G = int(a.K / kGroup);
+  p.tiles = int((a.N + 15) / 16);
+  p.tilesets = (p.tiles + R - 1) / R;
+  p.y_f16 = a.y_f16;
+  const int slots = num_cus() * resident_blocks(reinterpret_cast<const void *>(kernel), kThreads, 0);
+  double best = 1e300;
+  WideParams bp = p;
+  int bgrid = 1;
+  for (int S = 1; S <= 8; S *= 2) {
+    if (S > 1 && S > p.G) break;
+    const int P = kWaves / S;
+    const int g = max(1, min((p.tilesets + P - 1) / P, slots));
+    const int64_t rows = (int64_t)g * P;
+    const int GS = (p.G + S - 1) / S;
+    const double cost = double((p.tilesets + rows - 1) / rows) * R * GS * (S > 1 ? 1.05 : 1.0);
+    if (cost < best) {
+      best = cost;
+      bp = p;
+      bp.S = S;
+      bp.GS = GS;
+      bgrid = g;
+    }
+  }
+  p = bp;
+  grid = bgrid;
+  return best;
+}
+
+template <int FMT, bool BF>
+hipError_t launch_wide_t(const LaunchArgs &a) {
+  constexpr int D = 3;
+  WideParams p1, p2;
+  int g1, g2;
+  const double c1 = plan_wide(a, 2, &gemv_wide_kernel<FMT, BF, 2, D>, p1, g1);
+  const double c2 = plan_wide(a, 4, &gemv_wide_kernel<FMT, BF, 4, D>, p2, g2);
+  if (c1 <= c2 * 1.1)
+    hipLaunchKernelGGL((gemv_wide_kernel<FMT, BF, 2, D>), dim3(g1), dim3(kThreads), 0, a.stream, p1);
+  else
+    hipLaunchKernelGGL((gemv_wide_kernel<FMT, BF, 4, D>), dim3(g2), dim3(kThreads), 0, a.stream, p2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_wide(const LaunchArgs &a) {
+  if (a.fmt == 1) return a.x_bf16 ? launch_wide_t<1, true>(a) : launch_wide_t<1, false>(a);
+  return a.x_bf16 ? launch_wide_t<2, true>(a) : launch_wide_t<2, false>(a);
+}
+
+}  // namespace lowbit

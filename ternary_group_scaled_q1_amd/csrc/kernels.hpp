@@ -13,11 +13,20 @@ struct LaunchArgs {
   bool x_bf16;            // activation dtype
   bool y_f16;             // output dtype (false: fp32)
   int64_t M, N, K;
+  void *ws;          // caller-owned device workspace (may be NULL)
+  int64_t ws_bytes;  // its size in bytes
   hipStream_t stream;
 };
 
 // Each returns a hipError_t of the launch (hipSuccess when nothing to do).
 hipError_t launch_gemv(const LaunchArgs &a);
+// GEMV for 9..16 tokens (x operands loaded straight into registers).
+hipError_t launch_gemv_wide(const LaunchArgs &a);
+// Workspace bytes that let launch_gemv take its fastest path for M tokens.
+int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
+// GEMV on fp8 x fp4 instructions with row blocks x K ranges (bf16 x, M <= 16).
+hipError_t launch_gemv_split(const LaunchArgs &a);
+int64_t gemv_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const LaunchArgs &a);
 hipError_t launch_fill_zero(void *Y, int64_t bytes, hipStream_t stream);
 

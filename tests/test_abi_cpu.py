@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(lb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert lb.abi_version() == 1
+    assert lb.abi_version() == 2
 
 
 def test_strerror_covers_all_codes():
@@ -115,16 +115,41 @@ def test_unpack_rejects_invalid_codes():
 def test_device_calls_validate_before_launch():
     """Bad arguments are rejected before anything touches a GPU."""
     L = lb.load()
-    assert L.gemv_lowbit(7, 16, 16, 1, 16, 3, 1, 1, 128, None) == -2            # fmt
-    assert L.gemv_lowbit(1, 16, 16, 3, 16, 3, 1, 1, 128, None) == -7            # x f32
-    assert L.gemv_lowbit(1, 16, 16, 1, 16, 2, 1, 1, 128, None) == -7            # y bf16
-    assert L.gemv_lowbit(1, 16, 16, 1, 16, 3, 1, 1, 100, None) == -3            # K % 128
-    assert L.gemv_lowbit(1, None, 16, 1, 16, 3, 1, 1, 128, None) == -1          # W NULL
-    assert L.gemv_lowbit(1, 8, 16, 1, 16, 3, 1, 1, 128, None) == -6             # W misaligned
-    assert L.gemv_lowbit(1, 16, 16, 1, 18, 3, 1, 1, 128, None) == -6            # Y misaligned (f32)
-    assert L.gemv_lowbit(1, None, None, 1, None, 3, 0, 5, 128, None) == 0       # M == 0: no-op
+    assert L.gemv_lowbit(7, 16, 16, 1, 16, 3, 1, 1, 128, None, 0, None) == -2            # fmt
+    assert L.gemv_lowbit(1, 16, 16, 3, 16, 3, 1, 1, 128, None, 0, None) == -7            # x f32
+    assert L.gemv_lowbit(1, 16, 16, 1, 16, 2, 1, 1, 128, None, 0, None) == -7            # y bf16
+    assert L.gemv_lowbit(1, 16, 16, 1, 16, 3, 1, 1, 100, None, 0, None) == -3            # K % 128
+    assert L.gemv_lowbit(1, None, 16, 1, 16, 3, 1, 1, 128, None, 0, None) == -1          # W NULL
+    assert L.gemv_lowbit(1, 8, 16, 1, 16, 3, 1, 1, 128, None, 0, None) == -6             # W misaligned
+    assert L.gemv_lowbit(1, 16, 16, 1, 18, 3, 1, 1, 128, None, 0, None) == -6            # Y misaligned (f32)
+    assert L.gemv_lowbit(1, None, None, 1, None, 3, 0, 5, 128, None, 0, None) == 0       # M == 0: no-op
     assert L.gemm_lowbit(1, 16, 16, 1, 16, 3, 1, 1, 128, None, -1, None) == -5  # workspace size
     assert L.gemm_workspace_bytes_lowbit(1, 512, 17408, 5120) >= 0
+    assert L.gemv_lowbit(1, 16, 16, 1, 16, 3, 1, 1, 128, 24, 4096, None) == -6           # workspace misaligned
+    assert L.gemv_lowbit(1, 16, 16, 1, 16, 3, 1, 1, 128, None, -1, None) == -5           # workspace size
+
+
+def test_gemv_workspace_sizes():
+    """32 KiB of arrival counters, then the partial sums of at most 16 K
+    ranges and 8 MiB (16-token launches); none when fewer than two ranges fit;
+    tq5 (it runs on the GEMM kernel) needs none; shape errors reported."""
+    L = lb.load()
+
+    def rule(M, N, K):
+        m = min(M, 16)
+        ks = min(16, (8 << 20) // (m * N * 4), K // 128)
+        return 0 if ks < 2 else 32768 + ks * m * N * 4
+
+    for M, N, K in [(1, 5120, 5120), (16, 5120, 5120), (16, 17408, 5120), (16, 151936, 5120), (8, 5120, 17408),
+                    (40, 256, 1024), (1, 256, 128)]:
+        assert L.gemv_workspace_bytes_lowbit(1, M, N, K) == rule(M, N, K), (M, N, K)
+        assert L.gemv_workspace_bytes_lowbit(2, M, N, K) == rule(M, N, K), (M, N, K)
+    assert L.gemv_workspace_bytes_lowbit(1, 16, 5120, 5120) == 32768 + 16 * 16 * 5120 * 4
+    assert L.gemv_workspace_bytes_lowbit(1, 16, 151936, 5120) == 0
+    assert L.gemv_workspace_bytes_lowbit(3, 16, 5120, 17408) == 0
+    assert L.gemv_workspace_bytes_lowbit(1, 16, 5120, 100) == -3
+    assert L.gemv_workspace_bytes_lowbit(9, 16, 5120, 128) == -2
+    assert lb.gemv_workspace_bytes("q1", 16, 5120, 5120) == rule(16, 5120, 5120)
 
 
 def test_single_hip_runtime_in_process():

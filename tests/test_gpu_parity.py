@@ -140,7 +140,7 @@ def test_degenerate_sizes():
     L = lb.load()
     # M == 0 or N == 0: OK, nothing launched or written
     y = t.full((1, 4), 7.0, device="cuda")
-    assert L.gemv_lowbit(1, None, None, 1, y.data_ptr(), 3, 0, 4, 128, None) == 0
+    assert L.gemv_lowbit(1, None, None, 1, y.data_ptr(), 3, 0, 4, 128, None, 0, None) == 0
     assert L.gemm_lowbit(1, None, None, 1, y.data_ptr(), 3, 1, 0, 128, None, 0, None) == 0
     t.cuda.synchronize()
     assert (y == 7.0).all()
@@ -149,7 +149,7 @@ def test_degenerate_sizes():
         y = t.full((3, 5), 7.0, device="cuda")
         w = t.zeros(16, dtype=t.uint8, device="cuda")
         x = t.zeros((3, 0), dtype=t.float16, device="cuda")
-        st = (L.gemv_lowbit(1, w.data_ptr(), w.data_ptr(), 1, y.data_ptr(), 3, 3, 5, 0, None) if fn == "gemv"
+        st = (L.gemv_lowbit(1, w.data_ptr(), w.data_ptr(), 1, y.data_ptr(), 3, 3, 5, 0, None, 0, None) if fn == "gemv"
               else L.gemm_lowbit(1, w.data_ptr(), w.data_ptr(), 1, y.data_ptr(), 3, 3, 5, 0, None, 0, None))
         assert st == 0
         t.cuda.synchronize()
@@ -158,7 +158,7 @@ def test_degenerate_sizes():
     w = t.zeros(1024, dtype=t.uint8, device="cuda")
     x = t.zeros((1, 128), dtype=t.float16, device="cuda")
     y = t.zeros(64, dtype=t.float32, device="cuda")
-    assert L.gemv_lowbit(1, w.data_ptr() + 8, x.data_ptr(), 1, y.data_ptr(), 3, 1, 1, 128, None) == -6
+    assert L.gemv_lowbit(1, w.data_ptr() + 8, x.data_ptr(), 1, y.data_ptr(), 3, 1, 1, 128, None, 0, None) == -6
 
 
 # ------------------------------------------------ full workload shapes ----
@@ -252,3 +252,52 @@ def test_bf16_x_wide_dynamic_range(fmt, M):
             assert np.all(np.abs(y[keep] - y_ref_ok) <= ref.RTOL * a_ok + ref.ATOL + np.abs(y_ref_ok) * 2.0 ** -11)
         else:
             gu.check(y, codes, sc, x, "bf16", f"wide range {fmt} M={M}")
+
+
+def test_shared_workspace_across_shapes():
+    """One zero-filled workspace serves calls of different shapes and token
+    counts in a row (the split-K counters live at a fixed place and every call
+    leaves them zero): every result within the bound, and a second pass over
+    the same calls bitwise identical to the first."""
+    t = gu.torch()
+    g = np.random.default_rng(400)
+    cases = [("q1", 17, 130, 5120), ("tq2", 16, 5120, 1024), ("q1", 1, 4100, 2048), ("tq2", 9, 300, 17408),
+             ("q1", 16, 1000, 640), ("tq2", 3, 64, 5120)]
+    need = max(lb.gemv_workspace_bytes(f, M, N, K) for f, M, N, K in cases)
+    assert need > 0
+    ws = t.zeros(need, dtype=t.uint8, device="cuda")
+    data = []
+    for fmt, M, N, K in cases:
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        x = synth.x_normal(g, M, K, "bf16")
+        data.append((fmt, M, N, K, codes, sc, x, gu.w_tensor(lb.pack(fmt, codes, sc)), gu.x_tensor(x, "bf16")))
+    outs = []
+    for rep in range(2):
+        for fmt, M, N, K, codes, sc, x, w, xd in data:
+            print(f"shared workspace pass {rep}: {fmt} M={M} N={N} K={K}", flush=True)
+            y = lb.gemv(fmt, w, xd, N, K, workspace=ws)
+            t.cuda.synchronize()
+            yv = y.cpu().numpy().astype(np.float64)
+            if rep == 0:
+                gu.check(yv, codes, sc, x, "bf16", f"shared ws {fmt} M={M} N={N} K={K}")
+                outs.append(yv)
+            else:
+                assert np.array_equal(yv, outs[len(outs) - len(data) + data.index(next(d for d in data if d[0] == fmt and d[1] == M and d[2] == N and d[3] == K))])
+    assert not ws[:32768].any(), "split-K counters must be left at zero"
+
+
+@pytest.mark.parametrize("fmt", ["q1", "tq2"])
+def test_gemv_without_workspace(fmt):
+    """With no workspace the decode product takes the paths that need none
+    (workgroup-staged, or x straight into registers); same bound."""
+    g = np.random.default_rng(500)
+    for N, K, M in GEMV_SHAPES + [(5120, 17408, 4), (700, 12288, 16)]:
+        print(f"gemv {fmt} no workspace N={N} K={K} M={M}", flush=True)
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        x = synth.x_normal(g, M, K, "bf16")
+        blob = gu.w_tensor(lb.pack(fmt, codes, sc))
+        y = lb.gemv(fmt, blob, gu.x_tensor(x, "bf16"), N, K, workspace=False)
+        gu.torch().cuda.synchronize()
+        gu.check(y.cpu().numpy().astype(np.float64), codes, sc, x, "bf16", f"no ws {fmt} N={N} K={K} M={M}")
