@@ -161,9 +161,12 @@ def main():
         gemm_data.append((lb.FORMATS[fmt], w, x, y, M, N, K))
         del codes, sc
 
+    gws_bytes = max(lb.gemm_workspace_bytes(fmt, M, N, K) for (fmt, M, N, K, _) in GEMMS)
+    gws = torch.zeros(max(gws_bytes, 16), dtype=torch.uint8, device=dev)
+
     def run_gemm(i):
         f, w, x, y, M, N, K = gemm_data[i]
-        lb.gemm_raw(f, w.data_ptr(), x.data_ptr(), BF, y.data_ptr(), F32, M, N, K, sptr)
+        lb.gemm_raw(f, w.data_ptr(), x.data_ptr(), BF, y.data_ptr(), F32, M, N, K, sptr, gws.data_ptr(), gws_bytes)
 
     # Counter calibration: one plain device copy of CALIB_COPY_BYTES (untimed).
     cal_src = torch.ones(CALIB_COPY_BYTES // 4, device=dev, dtype=torch.float32)

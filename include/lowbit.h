@@ -127,12 +127,21 @@ int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, in
                 int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
                 void *hip_stream);
 
-/* Workspace gemm_lowbit needs for this problem (0 = none). */
+/* Workspace that lets gemm_lowbit balance its work over the whole chip: the
+ * (tile, 128-weight group) work items are cut into one contiguous range per
+ * workgroup slot, and tiles split between two ranges are summed through this
+ * memory (64 KiB of arrival counters, then two 128 x 128 fp32 pieces per
+ * slot).  Depends on the device's compute-unit count (256 assumed when no
+ * device is visible).  Returns a negative status on a bad format or shape. */
 int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* Prefill GEMM: Y = X W^T for large batches (M = prompt tokens).  Same
- * arguments and rules as gemv_lowbit, plus a caller-owned device workspace of
- * at least gemm_workspace_bytes_lowbit() bytes (may be NULL when that is 0). */
+ * arguments and rules as gemv_lowbit, including the workspace: caller-owned,
+ * 16-byte aligned, zero-filled before its first use (every call leaves its
+ * counters zero again), one per concurrently running call.  With at least
+ * gemm_workspace_bytes_lowbit() bytes the work is balanced across the chip;
+ * with less, or NULL, each workgroup takes whole tiles.  Results are
+ * deterministic for a given workspace size either way. */
 int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype,
                 int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
                 void *hip_stream);

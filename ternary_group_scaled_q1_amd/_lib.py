@@ -194,15 +194,20 @@ def gemm_workspace_bytes(fmt, M: int, N: int, K: int) -> int:
 
 
 def gemm(fmt, w, x, N: int, K: int, out_dtype=None, out=None, workspace=None, stream=None):
-    """y[M,N] = x[M,K] @ W^T on the GPU (prefill path)."""
+    """y[M,N] = x[M,K] @ W^T on the GPU (prefill path).
+
+    workspace: a zero-filled uint8 device tensor of at least
+    gemm_workspace_bytes() bytes, reused across calls on one stream (a fresh
+    zeroed one is allocated here when None); workspace=False runs whole tiles
+    per workgroup, which needs none."""
     torch = _torch()
     out_dtype = out_dtype or torch.float32
     f, x, M, out = _prep(fmt, w, x, N, K, out_dtype, out)
-    need = gemm_workspace_bytes(f, M, N, K)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_n = workspace.numel() if workspace is not None else 0
+    if workspace is None:
+        need = gemm_workspace_bytes(f, M, N, K)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device) if need else False
+    ws_ptr = workspace.data_ptr() if workspace is not False else None
+    ws_n = workspace.numel() if workspace is not False else 0
     s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
     _check(load().gemm_lowbit(f, w.data_ptr(), x.data_ptr(), _x_dtype(x), out.data_ptr(), _y_dtype(out.dtype),
                               M, N, K, ws_ptr, ws_n, s))

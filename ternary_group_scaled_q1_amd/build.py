@@ -31,6 +31,11 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
+# Per-source extra flags: the GEMM keeps its MFMA accumulators in VGPRs (the
+# per-group fp32 scale epilogue then needs no moves out of AGPRs).
+EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False, jobs: int = 4) -> str:
     hipcc = _hipcc()
     tmp = tempfile.mkdtemp(prefix="lowbit_build_")
@@ -39,7 +44,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            cmd = [hipcc, *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

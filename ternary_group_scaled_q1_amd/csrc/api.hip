@@ -96,16 +96,16 @@ int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, in
 int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K) {
   if (fmt < LOWBIT_Q1_G128 || fmt > LOWBIT_TQ5_G128) return LOWBIT_ERR_ENUM;
   if (M < 0 || N < 0 || K < 0 || K % kGroup) return LOWBIT_ERR_SHAPE;
-  return 0;
+  if (M == 0 || N == 0 || K == 0) return 0;
+  return gemm_workspace_bytes(M, N, K);
 }
 
 int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M, int64_t N,
                 int64_t K, void *workspace, int64_t workspace_bytes, void *hip_stream) {
   const int st = check_product(fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K);
   if (st != LOWBIT_OK || M == 0 || N == 0) return st;
-  const int64_t need = gemm_workspace_bytes_lowbit(fmt, M, N, K);
-  if (workspace_bytes < need) return LOWBIT_ERR_SIZE;
-  if (need > 0 && !workspace) return LOWBIT_ERR_NULL;
+  if (workspace_bytes < 0) return LOWBIT_ERR_SIZE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 15)) return LOWBIT_ERR_ALIGN;
   return run(true, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, workspace, workspace_bytes, hip_stream);
 }
 

@@ -1,24 +1,40 @@
 // Prefill GEMM  Y[m][n] = sum_k X[m][k] t[n][k] s[n][k/128]  for large M.
 //
 // Prompt processing is compute-bound (aberweb.com page, summary section 3),
-// so this path is a dense contraction on the matrix cores: the activation
-// tile (128 tokens x 128 k, one weight group) is staged in LDS, each wave
-// decodes its own weight operands straight from the packed bits in registers
-// into exact +-1 / 0 f16/bf16 halves and issues v_mfma_f32_16x16x32.  The
-// FP16 scale is applied once per group in fp32: each group accumulates into
-// a fresh tile that is then added as s * tile (products exact, the scale is
-// never rounded to bf16).
+// so this path is a dense contraction on the matrix cores: each wave decodes
+// its own weight operands straight from the packed bits in registers into
+// exact +-1 / 0 f16/bf16 halves and issues v_mfma_f32_16x16x32 against
+// activation tiles staged in LDS.  The FP16 scale is applied once per group
+// in fp32: each group accumulates into a fresh tile that is then added as
+// s * tile (products exact, the scale is never rounded to bf16).
 //
 // Workgroup = 4 waves = 128 x 128 outputs; wave (wm, wn) owns 64 x 64 =
-// 4 x 4 MFMA tiles, so every decoded weight operand feeds 4 MFMAs.  The 1-D
-// block id is remapped so that each XCD walks a contiguous run of tiles that
-// share activation rows (their L2 holds them).
+// 4 x 4 MFMA tiles, so every decoded weight operand feeds 4 MFMAs.
+//
+// Activations: a ring of three LDS stages, each one group of the tile (128
+// tokens x 128 k, 32 KB) in the order the MFMA reads it: 1 KB blocks, one
+// per (16-row block, k-step), with lane 16q + j's 16 bytes at 16 * lane.
+// Direct global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
+// land at 16 * lane from the block base) fill stage (i + 2) while stage i is
+// multiplied; every wave issues exactly 8 of them per group, so waiting
+// until at most 8 loads are outstanding means the stage needed next has
+// arrived.
+//
+// Work split (stream-K): the (tile, group) items, tiles ordered token tile
+// fastest, are cut into one contiguous range per workgroup slot of the chip.
+// A tile whose groups a range covers entirely is stored directly; the pieces
+// of a split tile go to the caller's workspace as agent-scope atomic stores,
+// one arrival counter per tile (zero between calls) tells the last of its
+// workgroups, which adds the pieces in K order (so the result does not
+// depend on arrival order), writes Y and resets the counter.  Without a
+// workspace every workgroup takes whole tiles.
 //
 // Ternary base-3 bytes (5 trits per byte) are decoded with a 243-entry LDS
 // table giving the five (sign, non-zero) bit pairs of a byte at bits
 // 15-2i / 14-2i; a shift by 2i and a mask then give the operand half 2t of
 // trit i.  In a full 640-trit segment byte b carries trit i of group i at
-// offset b, so one table lookup serves five groups.
+// offset b, so one table lookup serves five groups; the bytes of the next
+// segment are loaded two groups before it starts.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
@@ -29,15 +45,24 @@ namespace {
 
 constexpr int kBM = 128, kBN = 128;
 constexpr int kThreads = 256;
-constexpr int kXStride = 136;  // halves per LDS activation row (128 + 8 pad)
+constexpr int kStages = 3;
+constexpr int kStageBytes = kBM * 128 * 2;  // one group of the activation tile
+constexpr int kPieceFloats = 4 * 64 * 64;   // one 128 x 128 fp32 tile, lane order
+constexpr int64_t kCounterBytes = 64 << 10;  // arrival counters (up to 16384 tiles)
+constexpr int kRawBytes = 16 << 10;          // tq5 raw segment bytes per stage
+constexpr int kScaleStage = 4 * 256;         // staged FP16 scales per stage
 
 struct GemmParams {
   const uint8_t *W;
   const uint8_t *Sc;  // plane B (may be only 2-byte aligned for tq5)
   const uint16_t *X;
   void *Y;
+  float *part;      // [slot][2] pieces of split tiles (stream-K)
+  unsigned *count;  // [tiles] arrival counters
   int M, N, K, G;
   int tiles_m, tiles_n;
+  int64_t items;  // tiles * G
+  int per;        // items per workgroup
   int y_f16;
   // tq5 geometry
   int s_full, L_tail, b_tail, rowbytes;
@@ -50,78 +75,94 @@ __device__ __forceinline__ uint16_t load_scale(const GemmParams &p, int n, int g
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// The activation tile of one group (128 rows x 128 k) as 16-byte cells: each
-// thread holds 8 of the tile's 2048 cells in registers between the global
-// load and the LDS store, so the next group's loads overlap this group's MFMAs.
-struct XRegs {
-  u4_t v[8];
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct TileCols {
+  int tileT[4], RT[4];
 };
 
-__device__ __forceinline__ void x_load(const GemmParams &p, XRegs &r, int m0, int g) {
+__device__ __forceinline__ TileCols tile_cols(const GemmParams &p, int nt) {
+  const int wn = uni(threadIdx.x >> 6) & 1;
+  TileCols c;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
-    const int row = idx >> 4, c16 = idx & 15;
-    const bool in = m0 + row < p.M && g < p.G;
-    const u4_t *src = reinterpret_cast<const u4_t *>(p.X + (in ? (int64_t)(m0 + row) * p.K + 128 * g + 8 * c16 : 0));
-    const u4_t v = *src;
-    const u4_t z = {0u, 0u, 0u, 0u};
-    r.v[i] = in ? v : z;
+  for (int nb = 0; nb < 4; ++nb) {
+    const int n = nt * kBN + wn * 64 + 16 * nb;
+    c.tileT[nb] = uni(n / 16);
+    c.RT[nb] = uni(n < p.N ? min(16, p.N - n) : 0);
   }
+  return c;
 }
 
-// Store the cells; for q1 also minus the sum over k % 4 in {2, 3} of every row
-// (16 consecutive lanes hold one row's 16 cells).
-template <int FMT, bool BF>
-__device__ __forceinline__ void x_store(const XRegs &r, uint16_t *xs, float *corr) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
-    const int row = idx >> 4, c16 = idx & 15;
-    *reinterpret_cast<u4_t *>(xs + row * kXStride + 8 * c16) = r.v[i];
-    if constexpr (FMT == 1) {
-      const u4_t v = r.v[i];
-      float c = (x_to_float(uint16_t(v.y), BF) + x_to_float(uint16_t(v.y >> 16), BF)) +
-                (x_to_float(uint16_t(v.w), BF) + x_to_float(uint16_t(v.w >> 16), BF));
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) c += __shfl_xor(c, o, 16);
-      if (c16 == 0) corr[row] = -c;
-    }
-  }
+// Row tile and rows of n-block nb of column half wn of column tile nt, by
+// arithmetic (a runtime index into a per-thread array would put it in
+// scratch memory).  Blocks past N get tile 0 with one row: an in-bounds
+// address whose loads feed only unstored columns.
+struct ColBlock {
+  int T, R, RR;
+};
+
+__device__ __forceinline__ ColBlock col_block(const GemmParams &p, int nt, int wn, int nb) {
+  const int n = nt * kBN + wn * 64 + 16 * nb;
+  ColBlock c;
+  c.R = n < p.N ? min(16, p.N - n) : 0;
+  c.T = c.R > 0 ? n / 16 : 0;
+  c.RR = c.R > 0 ? c.R : 1;
+  return c;
 }
 
-// 4 k-steps of MFMAs for one group from LDS tile xs into fresh tiles (q1:
-// seeded with -corr of each row), then acc += s * tile.  Bop(u, nb) returns
-// the B operand (16 weight rows x 32 k) of n-block nb for k-step u.
-template <int FMT, bool BF, class Bop>
-__device__ __forceinline__ void group_mma(const uint16_t *xs, const float *corr, const float (&sc)[4],
-                                          f4_t (&acc)[4][4], Bop bop) {
+// Per-item weight staging (in the same LDS ring as the activations): the
+// packed words of the tile's 128 columns -- [wn][nb][word][lane] x 4 bytes,
+// one word per lane for q1, two for tq2 -- and their FP16 scales at
+// [wave][lane] x 4 bytes (a 2-byte global-to-LDS load writes its lane's
+// value zero-extended at 4 * lane; lane l carries the scale of row l % 16 of
+// n-block 2 wm + (l / 16) % 2).  Wave (wm, wn) loads
+// n-blocks 2wm, 2wm + 1 of its column half.  Weight rows past N (ragged last
+// tile, n-blocks past N) read a clamped, in-bounds address and keep whatever
+// they load: they only feed output columns that are never stored.
+template <int FMT>
+constexpr int w_words() { return FMT == 2 ? 2 : (FMT == 1 ? 1 : 0); }
+
+template <int FMT>
+constexpr int w_stage_bytes() {
+  return 2 * 4 * w_words<FMT>() * 256 + kScaleStage + (FMT == 3 ? kRawBytes : 0);
+}
+
+template <int FMT>
+__device__ __forceinline__ float w_scale(const char *wst, int nb) {
+  const int wn = (threadIdx.x >> 6) & 1, j = threadIdx.x & 15;
+  const int wave = (nb >> 1) * 2 + wn;
+  const uint16_t h = *reinterpret_cast<const uint16_t *>(wst + 2 * 4 * w_words<FMT>() * 256 + wave * 256 +
+                                                         ((nb & 1) * 16 + j) * 4);
+  return half_to_float(h);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t w_word(const char *wst, int nb, int h) {
+  const int wn = (threadIdx.x >> 6) & 1, lane = threadIdx.x & 63;
+  return *reinterpret_cast<const uint32_t *>(wst + ((wn * 4 + nb) * w_words<FMT>() + h) * 256 + lane * 4);
+}
+
+// 4 k-steps of MFMAs for one group from stage st into fresh tiles, then
+// acc += s * tile.  Bop(u, nb) returns the B operand (16 weight rows x 32 k)
+// of n-block nb for k-step u.
+template <bool BF, class Bop>
+__device__ __forceinline__ void group_mma(const char *st, const float (&sc)[4], f4_t (&acc)[4][4], Bop bop) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1;
-  const int j = lane & 15, q = lane >> 4;
   f4_t cg[4][4];
-  f4_t init[4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    if constexpr (FMT == 1) {
-      const float4 c = *reinterpret_cast<const float4 *>(corr + wm * 64 + 16 * mb + 4 * q);
-      init[mb] = f4_t{c.x, c.y, c.z, c.w};
-    } else {
-      init[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     u4_t A[4], B[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      A[mb] = *reinterpret_cast<const u4_t *>(xs + (wm * 64 + 16 * mb + j) * kXStride + 32 * u + 8 * q);
+      A[mb] = *reinterpret_cast<const u4_t *>(st + ((wm * 4 + mb) * 4 + u) * 1024 + lane * 16);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) B[nb] = bop(u, nb);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) cg[mb][nb] = mfma16x16x32<BF>(A[mb], B[nb], u == 0 ? init[mb] : cg[mb][nb]);
+      for (int nb = 0; nb < 4; ++nb)
+        cg[mb][nb] = u == 0 ? mfma16x16x32_zero<BF>(A[mb], B[nb]) : mfma16x16x32<BF>(A[mb], B[nb], cg[mb][nb]);
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -131,79 +172,159 @@ __device__ __forceinline__ void group_mma(const uint16_t *xs, const float *corr,
       for (int e = 0; e < 4; ++e) acc[mb][nb][e] = fmaf(sc[nb], cg[mb][nb][e], acc[mb][nb][e]);
 }
 
-// Weight words of one chunk (4 groups) for this lane's 4 n-blocks, and their scales.
 template <int FMT>
-struct WChunk {
-  uint32_t w[4][FMT == 1 ? 4 : 8];
-  uint32_t s[4][2];
+__device__ __forceinline__ void store_tile(const GemmParams &p, int mt, int nt, const f4_t (&acc)[4][4]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int j = lane & 15, q = lane >> 4;
+  const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = nt * kBN + wn * 64 + 16 * nb + j;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = mt * kBM + wm * 64 + 16 * mb + 4 * q + e;
+        if (m >= p.M) continue;
+        const float v = acc[mb][nb][e] * mul;
+        if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
+        else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+      }
+    }
+}
+
+// tq5: the raw bytes of the full segment holding each item, staged per item
+// in the weight stage (after the scales): layout [wn][nb][half][lane] x 16
+// bytes (32 bytes per lane and n-block, 16 KB); wave (wm, wn) fills n-blocks
+// 2wm, 2wm + 1.  Items of the tail segment (and matrices without a full
+// segment) load a harmless in-bounds block of x instead.
+
+// (sign, non-zero) pairs of the segment for the wave's 4 n-blocks, from the
+// staged raw bytes through the 243-entry table.
+__device__ __forceinline__ void tq5_decode(const char *slot, const uint16_t *lut, uint32_t (&d5)[4][16]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn = wave & 1;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const u4_t a = *reinterpret_cast<const u4_t *>(slot + ((wn * 4 + nb) * 2 + 0) * 1024 + lane * 16);
+    const u4_t b = *reinterpret_cast<const u4_t *>(slot + ((wn * 4 + nb) * 2 + 1) * 1024 + lane * 16);
+    const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const int w0 = 8 * u + 2 * pr;  // lane byte of weight e = 2pr of step u
+        const uint32_t b0 = (wds[w0 >> 2] >> (8 * (w0 & 3))) & 0xFF;
+        const uint32_t b1 = (wds[(w0 + 1) >> 2] >> (8 * ((w0 + 1) & 3))) & 0xFF;
+        d5[nb][u * 4 + pr] = uint32_t(lut[b0]) | (uint32_t(lut[b1]) << 16);
+      }
+  }
+}
+
+// The stream of items this workgroup loads: position (tile, group) and the
+// lane addresses that depend only on the tile, refreshed when the tile
+// changes, so that issuing an item's loads is a few adds per load.
+template <int FMT>
+struct Feed {
+  int tile, g, mt, nt;
+  const uint16_t *xrow[2];    // activation rows of blocks 8w..8w+3 / 8w+4..8w+7 (+ 8q)
+  const uint8_t *tbase[2];    // n-blocks 2wm, 2wm+1: tile block start (+ lane part for tq5)
+  int woff[2], RR[2];         // lane word index q*RR + jj, rows of the block (>= 1)
+  const uint8_t *scrow;       // this lane's scale row
+  const uint8_t *xfill;       // tq5: an in-bounds activation block for segments without raw bytes
 };
 
 template <int FMT>
-__device__ __forceinline__ void w_load(const GemmParams &p, WChunk<FMT> &wc, const int (&tileT)[4],
-                                       const int (&RT)[4], int c) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void feed_tile(const GemmParams &p, Feed<FMT> &f) {
+  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
   const int j = lane & 15, q = lane >> 4;
-  constexpr int WPU = FMT == 1 ? 4 : 8;
-  const int64_t unit = FMT == 1 ? 16 : 32;
-  const int Gc = uni(min(4, p.G - 4 * c));
+  f.mt = f.tile % p.tiles_m;
+  f.nt = f.tile / p.tiles_m;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int R = RT[nb];
-    if (R == 0 || c >= (p.G + 3) / 4) {
+  for (int h = 0; h < 2; ++h)
+    f.xrow[h] = p.X + (int64_t)min(f.mt * kBM + 16 * (2 * wave + h) + j, p.M - 1) * p.K + 8 * q;
 #pragma unroll
-      for (int i = 0; i < WPU; ++i) wc.w[nb][i] = 0;
-      wc.s[nb][0] = wc.s[nb][1] = 0;
-      continue;
-    }
-    const uint8_t *blk = p.W + 16 * (int64_t)tileT[nb] * p.G * unit + (int64_t)R * 4 * c * unit;
-    if (R == 16 && Gc == 4 && (p.G & 3) == 0) {
-      const u4_t v0 = *(reinterpret_cast<const u4_t *>(blk) + lane);
-      wc.w[nb][0] = v0.x; wc.w[nb][1] = v0.y; wc.w[nb][2] = v0.z; wc.w[nb][3] = v0.w;
-      if constexpr (FMT == 2) {
-        const u4_t v1 = *(reinterpret_cast<const u4_t *>(blk + 1024) + lane);
-        wc.w[nb][4] = v1.x; wc.w[nb][5] = v1.y; wc.w[nb][6] = v1.z; wc.w[nb][7] = v1.w;
+  for (int i = 0; i < 2; ++i) {
+    const ColBlock cb = col_block(p, f.nt, wn, 2 * wm + i);
+    const int jj = min(j, cb.RR - 1);
+    f.RR[i] = cb.RR;
+    f.woff[i] = q * cb.RR + jj;
+    if constexpr (FMT == 3) f.tbase[i] = p.W + 16 * (int64_t)cb.T * p.rowbytes + (q * cb.RR + jj) * 16;
+    else f.tbase[i] = p.W + 16 * (int64_t)cb.T * p.G * (FMT == 1 ? 16 : 32);
+  }
+  const ColBlock cs = col_block(p, f.nt, wn, 2 * wm + ((lane >> 4) & 1));
+  f.scrow = p.Sc + (int64_t)(16 * cs.T + min(j, cs.RR - 1)) * p.G * 2;
+  f.xfill = reinterpret_cast<const uint8_t *>(p.X + (int64_t)min(f.mt * kBM + j, p.M - 1) * p.K + 8 * q);
+}
+
+template <int FMT>
+__device__ __forceinline__ void feed_next(const GemmParams &p, Feed<FMT> &f) {
+  if (++f.g == p.G) {
+    f.g = 0;
+    ++f.tile;
+    feed_tile<FMT>(p, f);
+  }
+}
+
+// All loads of item f into activation stage xst and weight stage wst:
+// weights first, then the 8 activation loads of the wave.
+template <int FMT>
+__device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> &f, char *xst, char *wst) {
+  const int wave = uni(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = f.g;
+  if constexpr (FMT != 3) {
+    const int c = g >> 2, gc = g & 3;
+    const int Gc = min(4, p.G - 4 * c);
+    constexpr int unit = FMT == 1 ? 16 : 32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int nb = 2 * wm + i;
+      const uint32_t *blk = reinterpret_cast<const uint32_t *>(f.tbase[i] + (int64_t)f.RR[i] * 4 * c * unit);
+      if constexpr (FMT == 1) {
+        __builtin_amdgcn_global_load_lds((const void *)(blk + f.woff[i] * Gc + gc), (lds_void *)(wst + (wn * 4 + nb) * 256),
+                                         4, 0, 0);
+      } else {
+        const int hh = gc >> 1, Gh = min(2, Gc - 2 * hh);
+        const uint32_t *w = blk + f.RR[i] * 16 * hh + (f.woff[i] * Gh + (gc - 2 * hh)) * 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          __builtin_amdgcn_global_load_lds((const void *)(w + h), (lds_void *)(wst + ((wn * 4 + nb) * 2 + h) * 256), 4,
+                                           0, 0);
       }
-      const u2_t sv = *reinterpret_cast<const u2_t *>(p.Sc + ((int64_t)(16 * tileT[nb] + j) * p.G + 4 * c) * 2);
-      wc.s[nb][0] = sv.x; wc.s[nb][1] = sv.y;
-    } else {
-      const bool row_ok = j < R;
-      const int jj = min(j, R - 1);
-      const uint32_t *base = reinterpret_cast<const uint32_t *>(blk);
-      uint32_t h[4];
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int g2 = min(gg, Gc - 1);
-        const bool ok = row_ok && gg < Gc;
-        if constexpr (FMT == 1) {
-          const uint32_t w = base[(q * R + jj) * Gc + g2];
-          wc.w[nb][gg] = ok ? w : 0u;
-        } else {
-          const int hh = g2 >> 1, Gh = min(2, Gc - 2 * hh);
-          const uint32_t *hb = base + R * 16 * hh + ((q * R + jj) * Gh + (g2 - 2 * hh)) * 2;
-          const uint32_t w0 = hb[0], w1 = hb[1];
-          wc.w[nb][2 * gg + 0] = ok ? w0 : 0u;
-          wc.w[nb][2 * gg + 1] = ok ? w1 : 0u;
-        }
-        const uint32_t sv = load_scale(p, 16 * tileT[nb] + jj, 4 * c + g2);
-        h[gg] = ok ? sv : 0u;
-      }
-      wc.s[nb][0] = h[0] | (h[1] << 16);
-      wc.s[nb][1] = h[2] | (h[3] << 16);
     }
   }
+  __builtin_amdgcn_global_load_lds((const void *)(f.scrow + 2 * g),
+                                   (lds_void *)(wst + 2 * 4 * w_words<FMT>() * 256 + wave * 256), 2, 0, 0);
+  if constexpr (FMT == 3) {
+    const int seg = g / 5;
+    const bool full = seg < p.s_full;
+    char *slot = wst + kScaleStage;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int nb = 2 * wm + i;
+      const uint8_t *sb = f.tbase[i] + (int64_t)f.RR[i] * 128 * seg;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        __builtin_amdgcn_global_load_lds((const void *)(full ? sb + h * f.RR[i] * 64 : f.xfill),
+                                         (lds_void *)(slot + ((wn * 4 + nb) * 2 + h) * 1024), 16, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds((const void *)(f.xrow[i >> 2] + 128 * g + 32 * (i & 3)),
+                                     (lds_void *)(xst + (wave * 8 + i) * 1024), 16, 0, 0);
 }
 
 template <int FMT, bool BF>
 __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
-  __shared__ __align__(16) uint16_t xs[2][kBM * kXStride];
-  __shared__ __align__(16) float corr[2][kBM];
+  extern __shared__ __align__(16) char xs[];  // kStages x (activations, then weights)
   __shared__ uint16_t lut[256];
-
-  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  __shared__ int last_flag;
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wn = wave & 1;
   const int j = lane & 15, q = lane >> 4;
 
   if constexpr (FMT == 3) {
@@ -220,149 +341,169 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
     }
   }
 
-  // Row tiles (16 rows) of this wave's 4 n-blocks (wave-uniform).
-  int tileT[4], RT[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int n = n0 + wn * 64 + 16 * nb;
-    tileT[nb] = uni(n / 16);
-    RT[nb] = uni(n < p.N ? min(16, p.N - n) : 0);
-  }
+  const int64_t i0 = (int64_t)blockIdx.x * p.per;
+  const int64_t i1 = min(i0 + p.per, p.items);
+  if (i0 >= i1) return;  // workgroup-uniform
+  const int n = int(i1 - i0);
+  const int G = p.G;
+  const int first_tile = int(i0 / G);
 
   f4_t acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
+  TileCols tc = tile_cols(p, first_tile / p.tiles_m);
+  int g_begin = int(i0 % G);
+  int cur_tile = first_tile, cur_g = g_begin;  // item it
 
-  XRegs xr;
-  x_load(p, xr, m0, 0);
-  x_store<FMT, BF>(xr, xs[0], corr[0]);
-  __syncthreads();
+  // tq5: decoded pairs of the current segment.
+  uint32_t d5[4][16];
+  char *wring = xs + kStages * kStageBytes;  // weight stages (kStages x w_stage_bytes)
+  constexpr int kW = w_stage_bytes<FMT>();
 
-  if constexpr (FMT == 1 || FMT == 2) {
-    const int chunks = (p.G + 3) / 4;
-    WChunk<FMT> wa, wb;
-    w_load<FMT>(p, wa, tileT, RT, 0);
-    for (int c = 0; c < chunks; ++c) {
-      w_load<FMT>(p, wb, tileT, RT, c + 1);  // next chunk in flight
+  // Items 0 and 1 in flight; the feed then points at item 2 (it stops at
+  // the last item, whose loads are repeated into otherwise unused stages).
+  Feed<FMT> feed;
+  feed.tile = first_tile;
+  feed.g = g_begin;
+  feed_tile<FMT>(p, feed);
+  feed_issue<FMT>(p, feed, xs, wring);
+  int feed_it = 0;
+  if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
+  feed_issue<FMT>(p, feed, xs + kStageBytes, wring + kW);
+  if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
+
+  auto step = [&](int it, int slot) {
+    const int tile = cur_tile, g = cur_g;
+    if (++cur_g == G) { cur_g = 0; ++cur_tile; }
+    const int mt = tile % p.tiles_m, nt = tile / p.tiles_m;
+    const bool first = it == 0 || g == 0;
+    const bool last = it == n - 1 || g == G - 1;
+    if (first) {
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const int g = 4 * c + gi;
-        if (g >= p.G) break;
-        const int buf = g & 1;
-        if (g + 1 < p.G) x_load(p, xr, m0, g + 1);
-        float sc[4];
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) sc[nb] = half_to_float(uint16_t(wa.s[nb][gi >> 1] >> (16 * (gi & 1))));
-        group_mma<FMT, BF>(xs[buf], corr[buf], sc, acc, [&](int u, int nb) -> u4_t {
-          if constexpr (FMT == 1) return q1_operand<BF>(wa.w[nb][gi], u);
-          else return tq2_operand(wa.w[nb][2 * gi + (u >> 1)], u);
+        for (int b = 0; b < 4; ++b) acc[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
+      tc = tile_cols(p, nt);
+      g_begin = g;
+    }
+    // Stage `slot` holds item it once at most the 8 activation loads of item
+    // it + 1 are outstanding (the last item waits for all).
+    if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
+    // A plain barrier: __syncthreads() would also wait for every global load
+    // in flight.  LDS here is written only by the staging loads waited for
+    // above, and this wave's reads of the stage refilled below were consumed
+    // by its MFMAs of the previous item.
+    __builtin_amdgcn_s_barrier();
+    feed_issue<FMT>(p, feed, xs + ((slot + 2) % kStages) * kStageBytes, wring + ((slot + 2) % kStages) * kW);
+    if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
+    const char *st = xs + slot * kStageBytes;
+    const char *wst = wring + slot * kW;
+    float sc[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) sc[nb] = w_scale<FMT>(wst, nb);
+    if constexpr (FMT != 3) {
+      uint32_t wd[4][2];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int h = 0; h < w_words<FMT>(); ++h) wd[nb][h] = w_word<FMT>(wst, nb, h);
+      group_mma<BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
+        if constexpr (FMT == 1) return q1_operand_pm1<BF>(wd[nb][0], u);
+        else return tq2_operand(wd[nb][u >> 1], u);
+      });
+    } else {
+      const int seg = g / 5, gs = g % 5;
+      if (seg < p.s_full) {
+        if (gs == 0 || first) tq5_decode(wst + kScaleStage, lut, d5);
+        group_mma<BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
+          u4_t b;
+          b.x = tq5_pair(d5[nb][u * 4 + 0], gs);
+          b.y = tq5_pair(d5[nb][u * 4 + 1], gs);
+          b.z = tq5_pair(d5[nb][u * 4 + 2], gs);
+          b.w = tq5_pair(d5[nb][u * 4 + 3], gs);
+          return b;
         });
-        if (g + 1 < p.G) x_store<FMT, BF>(xr, xs[buf ^ 1], corr[buf ^ 1]);
-        __syncthreads();
-      }
-      wa = wb;
-    }
-  } else {
-    for (int seg = 0; seg * 5 < p.G; ++seg) {
-      const bool full = seg < p.s_full;
-      uint32_t d5[4][16];
-      if (full) {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int R = RT[nb];
-          const bool row_ok = j < R;
+      } else {
+        // Tail segment, row-major bytes: offset kt -> byte kt % B, digit kt / B.
+        group_mma<BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
+          uint32_t h[8];
+          const int R = tc.RT[nb];
           const int jj = min(j, max(R - 1, 0));
-          const uint8_t *sb = p.W + 16 * (int64_t)tileT[nb] * p.rowbytes + (int64_t)R * 128 * seg;
-          u4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-          if (R > 0) {
-            v0 = *reinterpret_cast<const u4_t *>(sb + (q * R + jj) * 16);
-            v1 = *reinterpret_cast<const u4_t *>(sb + R * 64 + (q * R + jj) * 16);
+          const int T = R > 0 ? tc.tileT[nb] : 0;
+          const int RR = R > 0 ? R : 1;
+          const uint8_t *tb = p.W + 16 * (int64_t)T * p.rowbytes + (int64_t)RR * 128 * p.s_full + (int64_t)jj * p.b_tail;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kt = 128 * (g - 5 * p.s_full) + 32 * u + 8 * q + e;
+            const int b = kt % p.b_tail, dig = kt / p.b_tail;
+            int v = tb[b];
+            for (int t = 0; t < dig; ++t) v /= 3;
+            const int d = v % 3;
+            h[e] = d == 1 ? 0u : (d == 2 ? 0x4000u : 0xC000u);
           }
-          const uint32_t wds[8] = {row_ok ? v0.x : 0u, row_ok ? v0.y : 0u, row_ok ? v0.z : 0u, row_ok ? v0.w : 0u,
-                                   row_ok ? v1.x : 0u, row_ok ? v1.y : 0u, row_ok ? v1.z : 0u, row_ok ? v1.w : 0u};
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int pr = 0; pr < 4; ++pr) {
-              const int w0 = 8 * u + 2 * pr;  // lane byte of weight e = 2pr of step u
-              const uint32_t b0 = (wds[w0 >> 2] >> (8 * (w0 & 3))) & 0xFF;
-              const uint32_t b1 = (wds[(w0 + 1) >> 2] >> (8 * ((w0 + 1) & 3))) & 0xFF;
-              d5[nb][u * 4 + pr] = uint32_t(lut[b0]) | (uint32_t(lut[b1]) << 16);
-            }
-        }
-      }
-      for (int gs = 0; gs < 5; ++gs) {
-        const int g = 5 * seg + gs;
-        if (g >= p.G) break;
-        const int buf = g & 1;
-        if (g + 1 < p.G) x_load(p, xr, m0, g + 1);
-        float sc[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int n = 16 * tileT[nb] + min(j, max(RT[nb] - 1, 0));
-          const float sv = RT[nb] > 0 ? half_to_float(load_scale(p, n, g)) : 0.f;
-          sc[nb] = j < RT[nb] ? sv : 0.f;
-        }
-        if (full) {
-          group_mma<FMT, BF>(xs[buf], corr[buf], sc, acc, [&](int u, int nb) -> u4_t {
-            u4_t b;
-            b.x = tq5_pair(d5[nb][u * 4 + 0], gs);
-            b.y = tq5_pair(d5[nb][u * 4 + 1], gs);
-            b.z = tq5_pair(d5[nb][u * 4 + 2], gs);
-            b.w = tq5_pair(d5[nb][u * 4 + 3], gs);
-            return b;
-          });
-        } else {
-          // Tail segment, row-major bytes: offset kt -> byte kt % B, digit kt / B.
-          group_mma<FMT, BF>(xs[buf], corr[buf], sc, acc, [&](int u, int nb) -> u4_t {
-            uint32_t h[8];
-            const int R = RT[nb];
-            const int jj = min(j, max(R - 1, 0));
-            const uint8_t *tb =
-                p.W + 16 * (int64_t)tileT[nb] * p.rowbytes + (int64_t)R * 128 * p.s_full + (int64_t)jj * p.b_tail;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int kt = 128 * (g - 5 * p.s_full) + 32 * u + 8 * q + e;
-              const int b = kt % p.b_tail, dig = kt / p.b_tail;
-              int v = R > 0 ? tb[b] : 121;
-              for (int t = 0; t < dig; ++t) v /= 3;
-              const int d = v % 3;
-              h[e] = (j >= R || d == 1) ? 0u : (d == 2 ? 0x4000u : 0xC000u);
-            }
-            u4_t b;
-            b.x = h[0] | (h[1] << 16);
-            b.y = h[2] | (h[3] << 16);
-            b.z = h[4] | (h[5] << 16);
-            b.w = h[6] | (h[7] << 16);
-            return b;
-          });
-        }
-        if (g + 1 < p.G) x_store<FMT, BF>(xr, xs[buf ^ 1], corr[buf ^ 1]);
-        __syncthreads();
+          u4_t b;
+          b.x = h[0] | (h[1] << 16);
+          b.y = h[2] | (h[3] << 16);
+          b.z = h[4] | (h[5] << 16);
+          b.w = h[6] | (h[7] << 16);
+          return b;
+        });
       }
     }
-  }
+    if (!last) return;
+    if (g_begin == 0 && g == G - 1) {  // whole tile in this range
+      store_tile<FMT>(p, mt, nt, acc);
+      return;
+    }
+    // Split tile: publish this piece (slot 0: this range's first tile, 1: its last).
+    const int which = tile == first_tile ? 0 : 1;
+    float *piece = p.part + ((int64_t)blockIdx.x * 2 + which) * kPieceFloats;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_store(piece + ((wave * 16 + a * 4 + b) * 4 + e) * 64 + lane, acc[a][b][e], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    const int wf = int((int64_t)tile * G / p.per), wl = int(((int64_t)tile * G + G - 1) / p.per);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's piece stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last_flag = __hip_atomic_fetch_add(p.count + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  unsigned(wl - wf);
+    __syncthreads();
+    if (!last_flag) return;
+    f4_t sum[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) sum[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
+    for (int w2 = wf; w2 <= wl; ++w2) {
+      const int wh = int((int64_t)w2 * p.per / G) == tile ? 0 : 1;
+      const float *pc = p.part + ((int64_t)w2 * 2 + wh) * kPieceFloats;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sum[a][b][e] += __hip_atomic_load(pc + ((wave * 16 + a * 4 + b) * 4 + e) * 64 + lane, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    }
+    store_tile<FMT>(p, mt, nt, sum);
+    if (threadIdx.x == 0) __hip_atomic_store(p.count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
 
-  const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
-  const int wm = wave >> 1;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int n = n0 + wn * 64 + 16 * nb + j;
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * 64 + 16 * mb + 4 * q + e;
-        if (m >= p.M) continue;
-        const float v = acc[mb][nb][e] * mul;
-        if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
-        else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
-      }
-    }
+  for (int it = 0; it < n; it += 3) {
+    step(it, 0);
+    if (it + 1 >= n) break;
+    step(it + 1, 1);
+    if (it + 2 >= n) break;
+    step(it + 2, 2);
+  }
 }
+
+int stream_k_slots() { return num_cus(); }
 
 template <int FMT, bool BF>
 hipError_t launch_t(const LaunchArgs &a) {
@@ -377,12 +518,32 @@ hipError_t launch_t(const LaunchArgs &a) {
   p.y_f16 = a.y_f16;
   const Tq5Geom t = tq5_geom(a.K);
   p.s_full = int(t.s_full); p.L_tail = int(t.L_tail); p.b_tail = int(t.b_tail); p.rowbytes = int(t.rowbytes);
-  const int grid = p.tiles_m * p.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<FMT, BF>), dim3(grid), dim3(kThreads), 0, a.stream, p);
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  p.items = tiles * p.G;
+  const int slots = stream_k_slots();
+  int grid;
+  const bool sk = a.ws && tiles <= kCounterBytes / 4 && tiles > slots / 2 &&
+                  a.ws_bytes >= kCounterBytes + (int64_t)slots * 2 * kPieceFloats * 4;
+  if (sk) {
+    p.per = int((p.items + slots - 1) / slots);
+    grid = int((p.items + p.per - 1) / p.per);
+    p.count = static_cast<unsigned *>(a.ws);
+    p.part = reinterpret_cast<float *>(static_cast<char *>(a.ws) + kCounterBytes);
+  } else {
+    p.per = p.G;  // whole tiles
+    grid = int(tiles);
+  }
+  const int lds = kStages * (kStageBytes + w_stage_bytes<FMT>());
+  hipLaunchKernelGGL((gemm_kernel<FMT, BF>), dim3(grid), dim3(kThreads), lds, a.stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
+
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  (void)M; (void)N; (void)K;
+  return kCounterBytes + (int64_t)stream_k_slots() * 2 * kPieceFloats * 4;
+}
 
 hipError_t launch_gemm(const LaunchArgs &a) {
   switch (a.fmt * 2 + (a.x_bf16 ? 1 : 0)) {

@@ -124,6 +124,7 @@ def test_device_calls_validate_before_launch():
     assert L.gemv_lowbit(1, 16, 16, 1, 18, 3, 1, 1, 128, None, 0, None) == -6            # Y misaligned (f32)
     assert L.gemv_lowbit(1, None, None, 1, None, 3, 0, 5, 128, None, 0, None) == 0       # M == 0: no-op
     assert L.gemm_lowbit(1, 16, 16, 1, 16, 3, 1, 1, 128, None, -1, None) == -5  # workspace size
+    assert L.gemm_lowbit(1, 16, 16, 1, 16, 3, 1, 1, 128, 24, 4096, None) == -6  # workspace misaligned
     assert L.gemm_workspace_bytes_lowbit(1, 512, 17408, 5120) >= 0
     assert L.gemv_lowbit(1, 16, 16, 1, 16, 3, 1, 1, 128, 24, 4096, None) == -6           # workspace misaligned
     assert L.gemv_lowbit(1, 16, 16, 1, 16, 3, 1, 1, 128, None, -1, None) == -5           # workspace size

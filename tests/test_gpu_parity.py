@@ -301,3 +301,47 @@ def test_gemv_without_workspace(fmt):
         y = lb.gemv(fmt, blob, gu.x_tensor(x, "bf16"), N, K, workspace=False)
         gu.torch().cuda.synchronize()
         gu.check(y.cpu().numpy().astype(np.float64), codes, sc, x, "bf16", f"no ws {fmt} N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_without_workspace(fmt):
+    """With no workspace every workgroup takes whole tiles; same bound."""
+    g = np.random.default_rng(600)
+    for M, N, K in GEMM_SHAPES:
+        print(f"gemm {fmt} no workspace M={M} N={N} K={K}", flush=True)
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        x = synth.x_normal(g, M, K, "bf16")
+        blob = gu.w_tensor(lb.pack(fmt, codes, sc))
+        y = lb.gemm(fmt, blob, gu.x_tensor(x, "bf16"), N, K, workspace=False)
+        gu.torch().cuda.synchronize()
+        gu.check(y.cpu().numpy().astype(np.float64), codes, sc, x, "bf16", f"gemm no ws {fmt} M={M} N={N} K={K}")
+
+
+def test_gemm_shared_workspace_and_split_tiles():
+    """One zero-filled workspace across GEMM calls of different shapes (tiles
+    split between workgroups are summed through it); a second pass is
+    bitwise identical and the counters are left at zero."""
+    t = gu.torch()
+    g = np.random.default_rng(700)
+    cases = [("q1", 300, 700, 5120), ("tq5", 257, 333, 17408), ("tq2", 129, 1000, 2048), ("q1", 64, 130, 640)]
+    need = max(lb.gemm_workspace_bytes(f, M, N, K) for f, M, N, K in cases)
+    ws = t.zeros(need, dtype=t.uint8, device="cuda")
+    data, first = [], []
+    for fmt, M, N, K in cases:
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        x = synth.x_normal(g, M, K, "bf16")
+        data.append((fmt, M, N, K, codes, sc, x, gu.w_tensor(lb.pack(fmt, codes, sc)), gu.x_tensor(x, "bf16")))
+    for rep in range(2):
+        for idx, (fmt, M, N, K, codes, sc, x, w, xd) in enumerate(data):
+            print(f"gemm shared workspace pass {rep}: {fmt} M={M} N={N} K={K}", flush=True)
+            y = lb.gemm(fmt, w, xd, N, K, workspace=ws)
+            t.cuda.synchronize()
+            yv = y.cpu().numpy().astype(np.float64)
+            if rep == 0:
+                gu.check(yv, codes, sc, x, "bf16", f"gemm shared ws {fmt} M={M} N={N} K={K}")
+                first.append(yv)
+            else:
+                assert np.array_equal(yv, first[idx])
+    assert not ws[:65536].any(), "stream-K counters must be left at zero"
