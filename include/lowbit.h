@@ -101,10 +101,11 @@ int unpack_lowbit(int fmt, const void *packed, int64_t packed_bytes, int64_t N, 
                   int8_t *codes_out, uint16_t *scales_out);
 
 /* Workspace that lets gemv_lowbit take its fastest path for this problem
- * (0 = the fastest path needs none).  With bf16 activations the decode
- * product may cut K into ranges handled by different workgroups; their fp32
- * partial sums live here, after 32 KiB of arrival counters at its start.  The
- * size does not depend on the device; fp16 activations never use it.
+ * (0 = the fastest path needs none).  With binary weights and bf16
+ * activations the decode product may cut K into ranges handled by different
+ * workgroups; their fp32 partial sums live here, after 32 KiB of arrival
+ * counters at its start.  The size does not depend on the device or on the
+ * activation dtype; fp16 activations and ternary formats never use it.
  * Returns a negative status on a bad format or shape. */
 int64_t gemv_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
 
@@ -130,9 +131,10 @@ int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, in
 /* Workspace that lets gemm_lowbit balance its work over the whole chip: the
  * (tile, 128-weight group) work items are cut into one contiguous range per
  * workgroup slot, and tiles split between two ranges are summed through this
- * memory (64 KiB of arrival counters, then two 128 x 128 fp32 pieces per
- * slot).  Depends on the device's compute-unit count (256 assumed when no
- * device is visible).  Returns a negative status on a bad format or shape. */
+ * memory (64 KiB of arrival counters, then two fp32 output tiles per slot:
+ * 128 x 256 for q1 and tq2, 128 x 128 for tq5).  Depends on the format and
+ * on the device's compute-unit count (256 assumed when no device is
+ * visible).  Returns a negative status on a bad format or shape. */
 int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* Prefill GEMM: Y = X W^T for large batches (M = prompt tokens).  Same

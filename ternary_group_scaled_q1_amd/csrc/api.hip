@@ -97,7 +97,7 @@ int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K) {
   if (fmt < LOWBIT_Q1_G128 || fmt > LOWBIT_TQ5_G128) return LOWBIT_ERR_ENUM;
   if (M < 0 || N < 0 || K < 0 || K % kGroup) return LOWBIT_ERR_SHAPE;
   if (M == 0 || N == 0 || K == 0) return 0;
-  return gemm_workspace_bytes(M, N, K);
+  return gemm_workspace_bytes(fmt, M, N, K);
 }
 
 int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M, int64_t N,

@@ -8,17 +8,19 @@
 // in fp32: each group accumulates into a fresh tile that is then added as
 // s * tile (products exact, the scale is never rounded to bf16).
 //
-// Workgroup = 4 waves = 128 x 128 outputs; wave (wm, wn) owns 64 x 64 =
-// 4 x 4 MFMA tiles, so every decoded weight operand feeds 4 MFMAs.
+// Workgroup = 2 x NWN waves = 128 x (64 NWN) outputs (NWN = 4 for q1 and
+// tq2, so two waves share each SIMD and one's MFMAs overlap the other's
+// decode and waits; 2 for tq5); wave (wm, wn) owns 64 x 64 = 4 x 4 MFMA
+// tiles, so every decoded weight operand feeds 4 MFMAs.
 //
 // Activations: a ring of three LDS stages, each one group of the tile (128
 // tokens x 128 k, 32 KB) in the order the MFMA reads it: 1 KB blocks, one
 // per (16-row block, k-step), with lane 16q + j's 16 bytes at 16 * lane.
 // Direct global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
 // land at 16 * lane from the block base) fill stage (i + 2) while stage i is
-// multiplied; every wave issues exactly 8 of them per group, so waiting
-// until at most 8 loads are outstanding means the stage needed next has
-// arrived.
+// multiplied; every wave issues the same number XB = 16 / NWN of them per
+// group, last among its loads of the group, so waiting until at most XB
+// loads are outstanding means the stage needed next has arrived.
 //
 // Work split (stream-K): the (tile, group) items, tiles ordered token tile
 // fastest, are cut into one contiguous range per workgroup slot of the chip.
@@ -43,14 +45,22 @@ namespace lowbit {
 
 namespace {
 
-constexpr int kBM = 128, kBN = 128;
-constexpr int kThreads = 256;
+constexpr int kBM = 128;
 constexpr int kStages = 3;
+// Waves side by side along N (two rows of them along M): 4 for q1 / tq2
+// (128 x 256 tiles, 8 waves, two per SIMD), 2 for tq5 (128 x 128, whose
+// staged segment bytes grow with the tile width).
+template <int FMT>
+constexpr int nwn() { return FMT == 3 ? 2 : 4; }
+template <int FMT>
+constexpr int threads_of() { return 128 * nwn<FMT>(); }
+template <int FMT>
+constexpr int bn_of() { return 64 * nwn<FMT>(); }
+template <int FMT>
+constexpr int piece_floats() { return 2 * nwn<FMT>() * 64 * 64; }  // one tile, lane order
 constexpr int kStageBytes = kBM * 128 * 2;  // one group of the activation tile
-constexpr int kPieceFloats = 4 * 64 * 64;   // one 128 x 128 fp32 tile, lane order
 constexpr int64_t kCounterBytes = 64 << 10;  // arrival counters (up to 16384 tiles)
 constexpr int kRawBytes = 16 << 10;          // tq5 raw segment bytes per stage
-constexpr int kScaleStage = 4 * 256;         // staged FP16 scales per stage
 
 struct GemmParams {
   const uint8_t *W;
@@ -81,12 +91,13 @@ struct TileCols {
   int tileT[4], RT[4];
 };
 
+template <int FMT>
 __device__ __forceinline__ TileCols tile_cols(const GemmParams &p, int nt) {
-  const int wn = uni(threadIdx.x >> 6) & 1;
+  const int wn = uni(threadIdx.x >> 6) % nwn<FMT>();
   TileCols c;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    const int n = nt * kBN + wn * 64 + 16 * nb;
+    const int n = nt * bn_of<FMT>() + wn * 64 + 16 * nb;
     c.tileT[nb] = uni(n / 16);
     c.RT[nb] = uni(n < p.N ? min(16, p.N - n) : 0);
   }
@@ -101,8 +112,9 @@ struct ColBlock {
   int T, R, RR;
 };
 
+template <int FMT>
 __device__ __forceinline__ ColBlock col_block(const GemmParams &p, int nt, int wn, int nb) {
-  const int n = nt * kBN + wn * 64 + 16 * nb;
+  const int n = nt * bn_of<FMT>() + wn * 64 + 16 * nb;
   ColBlock c;
   c.R = n < p.N ? min(16, p.N - n) : 0;
   c.T = c.R > 0 ? n / 16 : 0;
@@ -111,7 +123,7 @@ __device__ __forceinline__ ColBlock col_block(const GemmParams &p, int nt, int w
 }
 
 // Per-item weight staging (in the same LDS ring as the activations): the
-// packed words of the tile's 128 columns -- [wn][nb][word][lane] x 4 bytes,
+// packed words of the tile's columns -- [wn][nb][word][lane] x 4 bytes,
 // one word per lane for q1, two for tq2 -- and their FP16 scales at
 // [wave][lane] x 4 bytes (a 2-byte global-to-LDS load writes its lane's
 // value zero-extended at 4 * lane; lane l carries the scale of row l % 16 of
@@ -123,32 +135,38 @@ template <int FMT>
 constexpr int w_words() { return FMT == 2 ? 2 : (FMT == 1 ? 1 : 0); }
 
 template <int FMT>
+constexpr int w_scale_off() { return nwn<FMT>() * 4 * w_words<FMT>() * 256; }
+
+template <int FMT>
+constexpr int w_raw_off() { return w_scale_off<FMT>() + 2 * nwn<FMT>() * 256; }
+
+template <int FMT>
 constexpr int w_stage_bytes() {
-  return 2 * 4 * w_words<FMT>() * 256 + kScaleStage + (FMT == 3 ? kRawBytes : 0);
+  return w_scale_off<FMT>() + 2 * nwn<FMT>() * 256 + (FMT == 3 ? kRawBytes : 0);
 }
 
 template <int FMT>
 __device__ __forceinline__ float w_scale(const char *wst, int nb) {
-  const int wn = (threadIdx.x >> 6) & 1, j = threadIdx.x & 15;
-  const int wave = (nb >> 1) * 2 + wn;
-  const uint16_t h = *reinterpret_cast<const uint16_t *>(wst + 2 * 4 * w_words<FMT>() * 256 + wave * 256 +
-                                                         ((nb & 1) * 16 + j) * 4);
+  const int wn = (threadIdx.x >> 6) % nwn<FMT>(), j = threadIdx.x & 15;
+  const int wave = (nb >> 1) * nwn<FMT>() + wn;
+  const uint16_t h =
+      *reinterpret_cast<const uint16_t *>(wst + w_scale_off<FMT>() + wave * 256 + ((nb & 1) * 16 + j) * 4);
   return half_to_float(h);
 }
 
 template <int FMT>
 __device__ __forceinline__ uint32_t w_word(const char *wst, int nb, int h) {
-  const int wn = (threadIdx.x >> 6) & 1, lane = threadIdx.x & 63;
+  const int wn = (threadIdx.x >> 6) % nwn<FMT>(), lane = threadIdx.x & 63;
   return *reinterpret_cast<const uint32_t *>(wst + ((wn * 4 + nb) * w_words<FMT>() + h) * 256 + lane * 4);
 }
 
 // 4 k-steps of MFMAs for one group from stage st into fresh tiles, then
 // acc += s * tile.  Bop(u, nb) returns the B operand (16 weight rows x 32 k)
 // of n-block nb for k-step u.
-template <bool BF, class Bop>
+template <int FMT, bool BF, class Bop>
 __device__ __forceinline__ void group_mma(const char *st, const float (&sc)[4], f4_t (&acc)[4][4], Bop bop) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1;
+  const int wm = wave / nwn<FMT>();
   f4_t cg[4][4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -175,14 +193,14 @@ __device__ __forceinline__ void group_mma(const char *st, const float (&sc)[4], 
 template <int FMT>
 __device__ __forceinline__ void store_tile(const GemmParams &p, int mt, int nt, const f4_t (&acc)[4][4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / nwn<FMT>(), wn = wave % nwn<FMT>();
   const int j = lane & 15, q = lane >> 4;
   const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int n = nt * kBN + wn * 64 + 16 * nb + j;
+      const int n = nt * bn_of<FMT>() + wn * 64 + 16 * nb + j;
       if (n >= p.N) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -205,7 +223,7 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int mt, int nt, 
 // staged raw bytes through the 243-entry table.
 __device__ __forceinline__ void tq5_decode(const char *slot, const uint16_t *lut, uint32_t (&d5)[4][16]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wn = wave & 1;
+  const int wn = wave % nwn<3>();
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const u4_t a = *reinterpret_cast<const u4_t *>(slot + ((wn * 4 + nb) * 2 + 0) * 1024 + lane * 16);
@@ -229,33 +247,40 @@ __device__ __forceinline__ void tq5_decode(const char *slot, const uint16_t *lut
 template <int FMT>
 struct Feed {
   int tile, g, mt, nt;
-  const uint16_t *xrow[2];    // activation rows of blocks 8w..8w+3 / 8w+4..8w+7 (+ 8q)
+  const uint16_t *xrow[2];    // activation rows of the wave's blocks (+ 8q), see x_blocks
   const uint8_t *tbase[2];    // n-blocks 2wm, 2wm+1: tile block start (+ lane part for tq5)
   int woff[2], RR[2];         // lane word index q*RR + jj, rows of the block (>= 1)
   const uint8_t *scrow;       // this lane's scale row
   const uint8_t *xfill;       // tq5: an in-bounds activation block for segments without raw bytes
 };
 
+// Activation blocks (16 rows x one k-step, 1 KB) each wave loads per item:
+// the 32 blocks of a group split over the 2 * nwn waves; wave w takes blocks
+// w * XB .. w * XB + XB - 1 (row block b / 4, k-step b % 4).
+template <int FMT>
+constexpr int x_blocks() { return 32 / (2 * nwn<FMT>()); }
+
 template <int FMT>
 __device__ __forceinline__ void feed_tile(const GemmParams &p, Feed<FMT> &f) {
+  constexpr int XB = x_blocks<FMT>();
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / nwn<FMT>(), wn = wave % nwn<FMT>();
   const int j = lane & 15, q = lane >> 4;
   f.mt = f.tile % p.tiles_m;
   f.nt = f.tile / p.tiles_m;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-    f.xrow[h] = p.X + (int64_t)min(f.mt * kBM + 16 * (2 * wave + h) + j, p.M - 1) * p.K + 8 * q;
+  for (int h = 0; h < XB / 4; ++h)
+    f.xrow[h] = p.X + (int64_t)min(f.mt * kBM + 16 * (wave * (XB / 4) + h) + j, p.M - 1) * p.K + 8 * q;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const ColBlock cb = col_block(p, f.nt, wn, 2 * wm + i);
+    const ColBlock cb = col_block<FMT>(p, f.nt, wn, 2 * wm + i);
     const int jj = min(j, cb.RR - 1);
     f.RR[i] = cb.RR;
     f.woff[i] = q * cb.RR + jj;
     if constexpr (FMT == 3) f.tbase[i] = p.W + 16 * (int64_t)cb.T * p.rowbytes + (q * cb.RR + jj) * 16;
     else f.tbase[i] = p.W + 16 * (int64_t)cb.T * p.G * (FMT == 1 ? 16 : 32);
   }
-  const ColBlock cs = col_block(p, f.nt, wn, 2 * wm + ((lane >> 4) & 1));
+  const ColBlock cs = col_block<FMT>(p, f.nt, wn, 2 * wm + ((lane >> 4) & 1));
   f.scrow = p.Sc + (int64_t)(16 * cs.T + min(j, cs.RR - 1)) * p.G * 2;
   f.xfill = reinterpret_cast<const uint8_t *>(p.X + (int64_t)min(f.mt * kBM + j, p.M - 1) * p.K + 8 * q);
 }
@@ -270,11 +295,12 @@ __device__ __forceinline__ void feed_next(const GemmParams &p, Feed<FMT> &f) {
 }
 
 // All loads of item f into activation stage xst and weight stage wst:
-// weights first, then the 8 activation loads of the wave.
+// weights first, then the XB activation loads of the wave.
 template <int FMT>
 __device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> &f, char *xst, char *wst) {
+  constexpr int XB = x_blocks<FMT>();
   const int wave = uni(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / nwn<FMT>(), wn = wave % nwn<FMT>();
   const int g = f.g;
   if constexpr (FMT != 3) {
     const int c = g >> 2, gc = g & 3;
@@ -298,11 +324,11 @@ __device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> 
     }
   }
   __builtin_amdgcn_global_load_lds((const void *)(f.scrow + 2 * g),
-                                   (lds_void *)(wst + 2 * 4 * w_words<FMT>() * 256 + wave * 256), 2, 0, 0);
+                                   (lds_void *)(wst + w_scale_off<FMT>() + wave * 256), 2, 0, 0);
   if constexpr (FMT == 3) {
     const int seg = g / 5;
     const bool full = seg < p.s_full;
-    char *slot = wst + kScaleStage;
+    char *slot = wst + w_raw_off<FMT>();
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int nb = 2 * wm + i;
@@ -314,13 +340,13 @@ __device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> 
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < XB; ++i)
     __builtin_amdgcn_global_load_lds((const void *)(f.xrow[i >> 2] + 128 * g + 32 * (i & 3)),
-                                     (lds_void *)(xst + (wave * 8 + i) * 1024), 16, 0, 0);
+                                     (lds_void *)(xst + (wave * XB + i) * 1024), 16, 0, 0);
 }
 
 template <int FMT, bool BF>
-__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
+__global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
   extern __shared__ __align__(16) char xs[];  // kStages x (activations, then weights)
   __shared__ uint16_t lut[256];
   __shared__ int last_flag;
@@ -328,7 +354,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
   const int j = lane & 15, q = lane >> 4;
 
   if constexpr (FMT == 3) {
-    for (int v = threadIdx.x; v < 256; v += kThreads) {
+    for (int v = threadIdx.x; v < 256; v += threads_of<FMT>()) {
       uint32_t f = 0;
       int d = v;
       for (int i = 0; i < 5; ++i) {
@@ -349,7 +375,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
   const int first_tile = int(i0 / G);
 
   f4_t acc[4][4];
-  TileCols tc = tile_cols(p, first_tile / p.tiles_m);
+  TileCols tc = tile_cols<FMT>(p, first_tile / p.tiles_m);
   int g_begin = int(i0 % G);
   int cur_tile = first_tile, cur_g = g_begin;  // item it
 
@@ -381,13 +407,13 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
-      tc = tile_cols(p, nt);
+      tc = tile_cols<FMT>(p, nt);
       g_begin = g;
     }
-    // Stage `slot` holds item it once at most the 8 activation loads of item
-    // it + 1 are outstanding (the last item waits for all).
-    if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
+    // Stage `slot` holds item it once at most the XB activation loads of
+    // item it + 1 are outstanding (the last item waits for all).
+    if (it + 1 < n) __builtin_amdgcn_s_waitcnt(0x0F70 | x_blocks<FMT>());  // vmcnt(XB)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                            // vmcnt(0)
     // A plain barrier: __syncthreads() would also wait for every global load
     // in flight.  LDS here is written only by the staging loads waited for
     // above, and this wave's reads of the stage refilled below were consumed
@@ -406,15 +432,15 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int h = 0; h < w_words<FMT>(); ++h) wd[nb][h] = w_word<FMT>(wst, nb, h);
-      group_mma<BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
+      group_mma<FMT, BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
         if constexpr (FMT == 1) return q1_operand_pm1<BF>(wd[nb][0], u);
         else return tq2_operand(wd[nb][u >> 1], u);
       });
     } else {
       const int seg = g / 5, gs = g % 5;
       if (seg < p.s_full) {
-        if (gs == 0 || first) tq5_decode(wst + kScaleStage, lut, d5);
-        group_mma<BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
+        if (gs == 0 || first) tq5_decode(wst + w_raw_off<FMT>(), lut, d5);
+        group_mma<FMT, BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
           u4_t b;
           b.x = tq5_pair(d5[nb][u * 4 + 0], gs);
           b.y = tq5_pair(d5[nb][u * 4 + 1], gs);
@@ -424,7 +450,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
         });
       } else {
         // Tail segment, row-major bytes: offset kt -> byte kt % B, digit kt / B.
-        group_mma<BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
+        group_mma<FMT, BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
           uint32_t h[8];
           const int R = tc.RT[nb];
           const int jj = min(j, max(R - 1, 0));
@@ -456,7 +482,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
     }
     // Split tile: publish this piece (slot 0: this range's first tile, 1: its last).
     const int which = tile == first_tile ? 0 : 1;
-    float *piece = p.part + ((int64_t)blockIdx.x * 2 + which) * kPieceFloats;
+    float *piece = p.part + ((int64_t)blockIdx.x * 2 + which) * piece_floats<FMT>();
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -480,7 +506,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams p) {
       for (int b = 0; b < 4; ++b) sum[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
     for (int w2 = wf; w2 <= wl; ++w2) {
       const int wh = int((int64_t)w2 * p.per / G) == tile ? 0 : 1;
-      const float *pc = p.part + ((int64_t)w2 * 2 + wh) * kPieceFloats;
+      const float *pc = p.part + ((int64_t)w2 * 2 + wh) * piece_floats<FMT>();
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -514,7 +540,7 @@ hipError_t launch_t(const LaunchArgs &a) {
   p.Y = a.Y;
   p.M = int(a.M); p.N = int(a.N); p.K = int(a.K); p.G = int(a.K / kGroup);
   p.tiles_m = int((a.M + kBM - 1) / kBM);
-  p.tiles_n = int((a.N + kBN - 1) / kBN);
+  p.tiles_n = int((a.N + bn_of<FMT>() - 1) / bn_of<FMT>());
   p.y_f16 = a.y_f16;
   const Tq5Geom t = tq5_geom(a.K);
   p.s_full = int(t.s_full); p.L_tail = int(t.L_tail); p.b_tail = int(t.b_tail); p.rowbytes = int(t.rowbytes);
@@ -523,7 +549,7 @@ hipError_t launch_t(const LaunchArgs &a) {
   const int slots = stream_k_slots();
   int grid;
   const bool sk = a.ws && tiles <= kCounterBytes / 4 && tiles > slots / 2 &&
-                  a.ws_bytes >= kCounterBytes + (int64_t)slots * 2 * kPieceFloats * 4;
+                  a.ws_bytes >= kCounterBytes + (int64_t)slots * 2 * piece_floats<FMT>() * 4;
   if (sk) {
     p.per = int((p.items + slots - 1) / slots);
     grid = int((p.items + p.per - 1) / p.per);
@@ -534,15 +560,16 @@ hipError_t launch_t(const LaunchArgs &a) {
     grid = int(tiles);
   }
   const int lds = kStages * (kStageBytes + w_stage_bytes<FMT>());
-  hipLaunchKernelGGL((gemm_kernel<FMT, BF>), dim3(grid), dim3(kThreads), lds, a.stream, p);
+  hipLaunchKernelGGL((gemm_kernel<FMT, BF>), dim3(grid), dim3(threads_of<FMT>()), lds, a.stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
   (void)M; (void)N; (void)K;
-  return kCounterBytes + (int64_t)stream_k_slots() * 2 * kPieceFloats * 4;
+  const int64_t piece = fmt == 3 ? piece_floats<3>() : piece_floats<1>();
+  return kCounterBytes + (int64_t)stream_k_slots() * 2 * piece * 4;
 }
 
 hipError_t launch_gemm(const LaunchArgs &a) {

@@ -510,10 +510,18 @@ hipError_t launch_mt(const LaunchArgs &a) {
 //    caller's workspace to split K across workgroups;
 //  * 9..16 tokens on a small matrix: x loaded straight into registers
 //    (gemv_wide.hip).
+//
+// The fp8 x fp4 kernels (the staged one with FP4, and the split) hold each
+// 32-value activation block at one shared exponent: values within 2^7 of
+// the block's largest stay exact, smaller ones carry an error below 2^-17 of
+// it.  With binary weights every product of the block counts in the error
+// bound (|w| = s throughout a group), so that error stays below 2^-12 of the
+// bound's sum; a ternary zero can drop the large value from the sum, so tq2
+// always takes the bf16 matrix-core kernels.
 template <int FMT, bool BF>
 hipError_t launch_fmt(const LaunchArgs &a) {
-  if constexpr (BF) {
-    constexpr int RB = FMT == 1 ? 4 : 3;
+  if constexpr (BF && FMT == 1) {
+    constexpr int RB = 4;
     const bool ws_ok = a.ws && a.ws_bytes >= gemv_split_workspace_bytes(a.M, a.N, a.K);
     if (a.M > 8) {
       if (a.N <= 8192 && a.K <= 8192) return launch_gemv_wide(a);
@@ -536,7 +544,7 @@ hipError_t launch_fmt(const LaunchArgs &a) {
 }  // namespace
 
 int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  return fmt == 3 ? 0 : gemv_split_workspace_bytes(M, N, K);
+  return fmt == 1 ? gemv_split_workspace_bytes(M, N, K) : 0;
 }
 
 hipError_t launch_gemv(const LaunchArgs &a) {

@@ -29,7 +29,7 @@ hipError_t launch_gemv_split(const LaunchArgs &a);
 int64_t gemv_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const LaunchArgs &a);
 // Workspace bytes that let launch_gemm split tiles across workgroups (stream-K).
-int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 hipError_t launch_fill_zero(void *Y, int64_t bytes, hipStream_t stream);
 
 // Compute units of the current device (cached per device, thread-safe).

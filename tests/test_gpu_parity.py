@@ -254,6 +254,29 @@ def test_bf16_x_wide_dynamic_range(fmt, M):
             gu.check(y, codes, sc, x, "bf16", f"wide range {fmt} M={M}")
 
 
+@pytest.mark.parametrize("fmt", ["tq2", "tq5"])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 130])
+def test_ternary_outliers_on_zero_weights(fmt, M):
+    """A huge activation in every 32-value block whose weights are all zero:
+    the bound counts only the non-zero products, so the small activations
+    next to the outlier must keep their full precision (an activation format
+    with one shared exponent per block would lose them)."""
+    g = np.random.default_rng(500 + M)
+    N, K = 80, 1024
+    codes = _codes(g, fmt, N, K)
+    codes[:, ::32] = 0
+    codes[:, 5::32] = 0
+    sc = synth.scales_absnormal(g, N, K // 128)
+    xf = g.standard_normal((M, K))
+    xf[:, ::32] = np.where(g.random((M, K // 32)) < 0.5, -1.0, 1.0) * 2.0 ** 30
+    xf[:, 5::32] *= 2.0 ** -20
+    x = synth.f64_to_bf16_bits(xf)
+    blob = gu.w_tensor(lb.pack(fmt, codes, sc))
+    path = "gemv" if M <= 16 else "gemm"
+    y = gu.run(path, fmt, blob, x, "bf16", "f32", N, K)
+    gu.check(y, codes, sc, x, "bf16", f"outliers {fmt} M={M}")
+
+
 def test_shared_workspace_across_shapes():
     """One zero-filled workspace serves calls of different shapes and token
     counts in a row (the split-K counters live at a fixed place and every call
