@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--print-source-digest", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="run one part only, for counter passes: a sweep (q1_M1, q1_M16, tq2_M1, tq2_M16) "
+                         "or a GEMM (gemm_q1, gemm_tq5); the JSON line then covers that part")
     return ap.parse_args()
 
 
@@ -102,6 +105,12 @@ def main():
               "and has no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    sweeps = [k for k in SWEEP if args.only in (None, f"{k[0]}_M{k[1]}")]
+    gemm_ids = [i for i, g in enumerate(GEMMS) if args.only in (None, f"gemm_{g[0]}")]
+    if not sweeps and not gemm_ids:
+        print(f"--only {args.only}: no such part", file=sys.stderr)
+        sys.exit(2)
+
     import numpy as np
     import torch
 
@@ -118,7 +127,8 @@ def main():
 
     # ---------------------------------------------------------- decode sweep
     layers = sweep_layers()
-    weights = {f: gen_weights_gpu(torch, lb, f, layers, args.seed) for f in ("q1", "tq2")}
+    weights = {f: gen_weights_gpu(torch, lb, f, layers, args.seed)
+               for f in ("q1", "tq2") if args.only in (None, f"{f}_M1", f"{f}_M16")}
     gx = torch.Generator(device="cuda")
     gx.manual_seed(args.seed + 99)
     xs = {(m, K): torch.randn((m, K), device=dev, generator=gx).to(torch.bfloat16)
@@ -126,7 +136,7 @@ def main():
     ys = {(m, N): torch.empty((m, N), device=dev, dtype=torch.float32)
           for m in (1, 16) for N in (5120, 17408, 151936)}
     # One caller-owned GEMV workspace, reused by every launch of a sweep.
-    ws_bytes = max(lb.gemv_workspace_bytes(f, m, N, K) for f in ("q1", "tq2") for m in (1, 16) for (N, K) in layers)
+    ws_bytes = max([lb.gemv_workspace_bytes(f, m, N, K) for f in weights for m in (1, 16) for (N, K) in layers] + [0])
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def sweep(fmt, m):
@@ -139,10 +149,12 @@ def main():
 
     sweep_bytes = {}
     for fmt, m in SWEEP:
+        if fmt not in weights:
+            continue
         sweep_bytes[(fmt, m)] = sum(lb.packed_bytes(fmt, N, K) + m * K * 2 + m * N * 4 for (N, K) in layers)
 
     graphs = {}
-    for fmt, m in SWEEP:
+    for fmt, m in sweeps:
         sweep(fmt, m)  # eager warm-up (first launches initialise the code objects)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -152,13 +164,15 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------- prefill GEMMs
-    gemm_data = []
+    gemm_data = {}
     for i, (fmt, M, N, K, p0) in enumerate(GEMMS):
+        if i not in gemm_ids:
+            continue
         codes, sc = synth.draw_matrix(args.seed, 4, i, N, K, p0)
         w = torch.from_numpy(lb.pack(fmt, codes, sc)).to(dev)
         x = torch.from_numpy(synth.draw_x(args.seed, 4, i, M, K, "bf16").view(np.int16)).view(torch.bfloat16).to(dev)
         y = torch.empty((M, N), device=dev, dtype=torch.float32)
-        gemm_data.append((lb.FORMATS[fmt], w, x, y, M, N, K))
+        gemm_data[i] = (lb.FORMATS[fmt], w, x, y, M, N, K)
         del codes, sc
 
     gws_bytes = max(lb.gemm_workspace_bytes(fmt, M, N, K) for (fmt, M, N, K, _) in GEMMS)
@@ -176,7 +190,7 @@ def main():
     del cal_src, cal_dst
 
     # ------------------------------------------------------------- timing
-    parts = [("sweep", k) for k in SWEEP] + [("gemm", i) for i in range(len(GEMMS))]
+    parts = [("sweep", k) for k in sweeps] + [("gemm", i) for i in gemm_ids]
     ev = {p: [] for p in parts}
 
     def step(record):
@@ -202,53 +216,60 @@ def main():
     wall = time.perf_counter() - t0
 
     ms = {p: sum(a.elapsed_time(b) for a, b in ev[p]) / args.steps for p in parts}
-    sweep_ms = sum(ms[("sweep", k)] for k in SWEEP)
-    total_sweep_bytes = sum(sweep_bytes.values())
-    value = total_sweep_bytes / (sweep_ms * 1e-3) / 1e9
+    sweep_ms = sum(ms[("sweep", k)] for k in sweeps)
+    total_sweep_bytes = sum(sweep_bytes[k] for k in sweeps)
+    value = total_sweep_bytes / (sweep_ms * 1e-3) / 1e9 if sweeps else None
 
     per_sweep = {}
-    for k in SWEEP:
+    for k in sweeps:
         t = ms[("sweep", k)]
         per_sweep[f"{k[0]}_M{k[1]}"] = {
             "ms": round(t, 4), "GB_s": round(sweep_bytes[k] / (t * 1e-3) / 1e9, 1),
             "tok_s": round(k[1] / (t * 1e-3), 1), "launches": len(layers),
             "gbytes": round(sweep_bytes[k] / 1e9, 4)}
     gemm_out = {}
-    for i, (fmt, M, N, K, _) in enumerate(GEMMS):
+    for i in gemm_ids:
+        fmt, M, N, K, _ = GEMMS[i]
         t = ms[("gemm", i)]
         gemm_out[f"{fmt}_{M}x{N}x{K}"] = {"ms": round(t, 4), "TFLOP_s": round(2 * M * N * K / (t * 1e-3) / 1e12, 1)}
 
-    # Dominant kernel: the GEMV instantiation with the most GPU time.  Its
-    # average launch duration is the sweep's event time / launches.
-    dom = max(SWEEP, key=lambda k: ms[("sweep", k)])
-    dom_ms = ms[("sweep", dom)]
-    achieved = sweep_bytes[dom] / (dom_ms * 1e-3) / 1e9
-    traffic, fetch = measured_traffic(dom)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "fetch_bytes_per_launch": fetch,
-                "kernel": f"gemv {dom[0]} M={dom[1]} (bf16 x, fp32 y)",
-                "avg_launch_us": round(dom_ms * 1e3 / len(layers), 3),
-                "bytes_per_launch": round(sweep_bytes[dom] / len(layers))}
-    gi = max(range(len(GEMMS)), key=lambda i: ms[("gemm", i)])
-    fmt, M, N, K, _ = GEMMS[gi]
-    gt = ms[("gemm", gi)]
-    roofline_gemm = {"bound": "mfma", "achieved": round(2 * M * N * K / (gt * 1e-3) / 1e12, 1),
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(2 * M * N * K / (gt * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                     "kernel": f"gemm {fmt} {M}x{N}x{K}"}
+    # Dominant kernel: the GEMV sweep with the most GPU time (its launches
+    # run the GEMV kernels of that format and batch); average launch
+    # duration = the sweep's event time / its launches.
+    roofline = None
+    if sweeps:
+        dom = max(sweeps, key=lambda k: ms[("sweep", k)])
+        dom_ms = ms[("sweep", dom)]
+        achieved = sweep_bytes[dom] / (dom_ms * 1e-3) / 1e9
+        traffic, fetch = measured_traffic(dom)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "fetch_bytes_per_launch": fetch,
+                    "kernel": f"gemv {dom[0]} M={dom[1]} (bf16 x, fp32 y)",
+                    "avg_launch_us": round(dom_ms * 1e3 / len(layers), 3),
+                    "bytes_per_launch": round(sweep_bytes[dom] / len(layers))}
+    roofline_gemm = None
+    if gemm_ids:
+        gi = max(gemm_ids, key=lambda i: ms[("gemm", i)])
+        fmt, M, N, K, _ = GEMMS[gi]
+        gt = ms[("gemm", gi)]
+        roofline_gemm = {"bound": "mfma", "achieved": round(2 * M * N * K / (gt * 1e-3) / 1e12, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(2 * M * N * K / (gt * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "kernel": f"gemm {fmt} {M}x{N}x{K}", "avg_launch_us": round(gt * 1e3, 3)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     out = {
         "metric": "low-bit GEMV HBM GB/s (% peak) + prefill GEMM TFLOP/s at 27B-class shapes",
-        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(value, 1) if value is not None else None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded packed weights, N(0,1) activations)",
         "config": {"workload": "27B-class decode weight sweep (64 blocks of q/k/v/o 5120x5120, gate/up "
                                "17408x5120, down 5120x17408 + LM head 151936x5120; q1 then tq2; M=1 and M=16) "
                                "+ prefill GEMM M=512 (q1 17408x5120, tq5 5120x17408)",
-                   "hbm_fraction": round(value / HBM_PEAK_GBS, 4)},
+                   "hbm_fraction": round(value / HBM_PEAK_GBS, 4) if value is not None else None,
+                   "only": args.only},
         "sweeps": per_sweep, "prefill_gemm": gemm_out,
         "roofline": roofline, "roofline_gemm": roofline_gemm, "cpu_baseline": cpu,
     }
