@@ -9,8 +9,10 @@ generators) and never imports it.
 * ``layout`` packed sizes, the per-weight address of every sign / code / trit
              in the device layout, pack and unpack
 * ``ref``    y = X (t*s)^T and a = |X| |t*s|^T in float64, acceptance bound
+* ``mlx``    MLX's affine 1-bit g128 weights (a * q + b) and their exact
+             Binary g128 form
 
 Pins against something other than itself live in ``tests/test_oracle_*.py``.
 Every function here is pinned; none is "parity unpinned".
 """
-from . import fp, layout, ref  # noqa: F401
+from . import fp, layout, mlx, ref  # noqa: F401

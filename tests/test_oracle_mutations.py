@@ -84,3 +84,41 @@ def test_layout_index_swaps_are_caught(monkeypatch, swap):
         return (q, u, e) if swap == "uq" else (u, e % 4, q + 4 * (e // 4))
     monkeypatch.setattr(layout, "_in_group", bad)
     assert _fails(pins.test_golden_layout_positions)
+
+
+def test_mlx_reversed_bit_order_is_caught(monkeypatch):
+    from oracle import mlx
+
+    def bad(wq):
+        wq = np.asarray(wq, dtype=np.uint32)
+        N, W = wq.shape
+        shifts = np.arange(31, -1, -1, dtype=np.uint32)  # highest bit first
+        return ((wq[:, :, None] >> shifts[None, None, :]) & np.uint32(1)).reshape(N, 32 * W).astype(np.uint8)
+    monkeypatch.setattr(mlx, "bits_q", bad)
+    assert _fails(pins.test_mlx_golden_example)
+    assert _fails(pins.test_mlx_bit_order_single_bits)
+
+
+def test_mlx_scale_from_scale_not_bias_is_caught(monkeypatch):
+    from oracle import mlx
+    orig = mlx.to_binary
+
+    def bad(wq, scales_bits, biases_bits, dtype):
+        r = orig(wq, scales_bits, biases_bits, dtype)
+        if r is None:
+            return None
+        codes, _ = r
+        a = fp.decode(scales_bits, dtype)  # s = a instead of a / 2 = -b
+        return codes, a.astype(np.float16).view(np.uint16)
+    monkeypatch.setattr(mlx, "to_binary", bad)
+    assert _fails(pins.test_mlx_golden_example)
+
+
+def test_mlx_missing_bias_is_caught(monkeypatch):
+    from oracle import mlx
+
+    def bad(wq, scales_bits, biases_bits, dtype):
+        q = mlx.bits_q(wq).astype(np.float64)
+        return np.repeat(fp.decode(scales_bits, dtype), mlx.GROUP, axis=1) * q  # bias dropped
+    monkeypatch.setattr(mlx, "dequant", bad)
+    assert _fails(pins.test_mlx_golden_example)

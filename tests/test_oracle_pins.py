@@ -350,3 +350,91 @@ def test_bf16_rounding_of_scales_breaks_the_bound():
     bad = fp.decode_bf16(x[0]) @ (t.astype(np.float64) * np.repeat(s_bf, 128, axis=1)).T
     ok, _ = ref.within_tolerance(bad[None, :], y, a)
     assert not ok
+
+
+# ----------------------------------------------------------- MLX affine --
+def _mlx_golden():
+    kv = {}
+    for line in open(os.path.join(GOLDEN, "mlx_affine.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            k, v = [s.strip() for s in line.split("=")]
+            kv[k] = v
+    words = np.array([[int(kv[f"word{i}"], 16) for i in range(4)]], dtype=np.uint32)
+    plus = [int(t) for t in kv["plus_at"].split()]
+    return kv, words, plus
+
+
+def test_mlx_golden_example():
+    """Hand-worked example: dequantised weights, bit order and the exact
+    Binary g128 form."""
+    from oracle import mlx
+    kv, words, plus = _mlx_golden()
+    a = np.array([[int(kv["scale_f16"], 16)]], dtype=np.uint16)
+    b = np.array([[int(kv["bias_f16"], 16)]], dtype=np.uint16)
+    w = mlx.dequant(words, a, b, "f16")
+    want = np.full((1, 128), -0.75)
+    want[0, plus] = 0.75
+    assert np.array_equal(w, want)
+    codes, s = mlx.to_binary(words, a, b, "f16")
+    assert s[0, 0] == int(kv["s_f16"], 16)
+    assert np.array_equal(codes[0], np.where(want[0] > 0, 1, -1))
+    # The Binary g128 weights of the converted group equal MLX's exactly.
+    assert np.array_equal(ref.weights_f64(codes, s), w)
+    bad = np.array([[int(kv["bad_bias_f16"], 16)]], dtype=np.uint16)
+    assert mlx.to_binary(words, a, bad, "f16") is None
+
+
+def test_mlx_bit_order_single_bits():
+    """q[n, k] is bit k % 32 of word k // 32: a word with only bit i set
+    gives exactly one q = 1, at k = 32 * word + i (brute force over all)."""
+    from oracle import mlx
+    for wi in range(4):
+        for i in range(32):
+            words = np.zeros((1, 4), dtype=np.uint32)
+            words[0, wi] = np.uint32(1) << np.uint32(i)
+            q = mlx.bits_q(words)
+            assert q.sum() == 1 and q[0, 32 * wi + i] == 1
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_mlx_symmetric_groups_closed_form(dtype):
+    """Groups built as a = 2s, b = -s (s an FP16 value representable in the
+    dtype) dequantise to exactly +-s, and convert back to s with codes 2q-1."""
+    from oracle import mlx
+    g = np.random.default_rng(71)
+    N, K = 6, 384
+    # s with at most 8 significant bits and a modest exponent: exact in all three.
+    mant = g.integers(128, 256, size=(N, K // 128))
+    ex = g.integers(-12, 4, size=(N, K // 128))
+    s = np.ldexp(mant.astype(np.float64), ex - 7) * np.where(g.random((N, K // 128)) < 0.2, -1, 1)
+    enc = {"f16": lambda v: v.astype(np.float16).view(np.uint16),
+           "bf16": synth.f64_to_bf16_bits,
+           "f32": lambda v: v.astype(np.float32).view(np.uint32)}[dtype]
+    a, b = enc(2 * s), enc(-s)
+    words = g.integers(0, 2 ** 32, size=(N, K // 32), dtype=np.uint64).astype(np.uint32)
+    w = mlx.dequant(words, a, b, dtype)
+    q = mlx.bits_q(words)
+    assert np.array_equal(w, np.where(q == 1, 1.0, -1.0) * np.repeat(s, 128, axis=1))
+    codes, s16 = mlx.to_binary(words, a, b, dtype)
+    assert np.array_equal(s16, s.astype(np.float16).view(np.uint16))
+    assert np.array_equal(ref.weights_f64(codes, s16), w)
+
+
+def test_mlx_rejections():
+    """Groups that are not {-s, +s} with s FP16 have no Binary g128 form:
+    a != -2b, s below the FP16 range or with too many bits, non-finite."""
+    from oracle import mlx
+    words = np.zeros((1, 4), dtype=np.uint32)
+
+    def conv(a, b, dtype):
+        return mlx.to_binary(words, np.array([[a]]), np.array([[b]]), dtype)
+
+    f = lambda v: np.uint32(np.array(v, dtype=np.float32).view(np.uint32))
+    assert conv(f(2.0), f(-1.0), "f32") is not None
+    assert conv(f(2.0), f(-0.5), "f32") is None              # {-0.5, 1.5}
+    assert conv(f(2 ** -30), f(-2 ** -31), "f32") is None    # s below fp16 subnormals
+    assert conv(f(2.0 + 2 ** -20), f(-1.0 - 2 ** -21), "f32") is None  # 22 significant bits
+    assert conv(f(np.inf), f(-np.inf), "f32") is None
+    assert conv(f(131072.0), f(-65536.0), "f32") is None    # s beyond fp16 max
+    assert conv(f(0.0), f(-0.0), "f32") is not None           # all-zero group: s = +0
