@@ -5,7 +5,9 @@ One step = the whole hot path over one batch of synthetic input:
      gate/up 17408x5120, down 5120x17408, plus the LM head 151936x5120),
      dependency-ordered GEMV launches on one stream, captured in a HIP graph,
      once with Binary g128 (q1) weights and once with Ternary g128 2-bit-slot
-     (tq2) weights, each at batch M = 1 and M = 16 (x bf16, y fp32);
+     (tq2) weights, each at batch M = 1 and M = 16 (x bf16, y fp32); the
+     matrices that share an input run as one fused launch (q/k/v, gate/up),
+     so a block is 4 launches and the sweep 257;
   2. the two prefill GEMMs at M = 512 tokens (x bf16, y fp32): q1 weights
      17408x5120 and tq5 (5 trits/byte) weights 5120x17408.
 Weights are packed once before timing (the packer is off the timed path).
@@ -133,19 +135,35 @@ def main():
     gx.manual_seed(args.seed + 99)
     xs = {(m, K): torch.randn((m, K), device=dev, generator=gx).to(torch.bfloat16)
           for m in (1, 16) for K in (5120, 17408)}
-    ys = {(m, N): torch.empty((m, N), device=dev, dtype=torch.float32)
-          for m in (1, 16) for N in (5120, 17408, 151936)}
+    # Launches: lists of layer indices that share one input (fused).
+    launches = []
+    for b in range(N_BLOCKS):
+        i = len(BLOCK) * b
+        launches += [[i, i + 1, i + 2], [i + 3], [i + 4, i + 5], [i + 6]]
+    launches.append([len(BLOCK) * N_BLOCKS])
+    # Output buffers per (M, N, slot in its launch).
+    ys = {(m, N, j): torch.empty((m, N), device=dev, dtype=torch.float32)
+          for m in (1, 16) for N in (5120, 17408, 151936) for j in range(3)}
     # One caller-owned GEMV workspace, reused by every launch of a sweep.
-    ws_bytes = max([lb.gemv_workspace_bytes(f, m, N, K) for f in weights for m in (1, 16) for (N, K) in layers] + [0])
+    ws_bytes = max([lb.gemv_multi_workspace_bytes(f, [layers[i][0] for i in L], m, layers[L[0]][1])
+                    for f in weights for m in (1, 16) for L in launches] + [0])
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def sweep(fmt, m):
         buf, offs = weights[fmt]
         base = buf.data_ptr()
         f = lb.FORMATS[fmt]
-        for (N, K), off in zip(layers, offs):
-            lb.gemv_raw(f, base + off, xs[(m, K)].data_ptr(), BF, ys[(m, N)].data_ptr(), F32, m, N, K,
-                        torch.cuda.current_stream(dev).cuda_stream, ws.data_ptr(), ws_bytes)
+        s = torch.cuda.current_stream(dev).cuda_stream
+        for L in launches:
+            K = layers[L[0]][1]
+            Ns = [layers[i][0] for i in L]
+            yp = [ys[(m, N, j)].data_ptr() for j, N in enumerate(Ns)]
+            if len(L) == 1:
+                lb.gemv_raw(f, base + offs[L[0]], xs[(m, K)].data_ptr(), BF, yp[0], F32, m, Ns[0], K, s,
+                            ws.data_ptr(), ws_bytes)
+            else:
+                lb.gemv_multi_raw(f, [base + offs[i] for i in L], Ns, xs[(m, K)].data_ptr(), BF, yp, F32, m, K, s,
+                                  ws.data_ptr(), ws_bytes)
 
     sweep_bytes = {}
     for fmt, m in SWEEP:
@@ -225,7 +243,7 @@ def main():
         t = ms[("sweep", k)]
         per_sweep[f"{k[0]}_M{k[1]}"] = {
             "ms": round(t, 4), "GB_s": round(sweep_bytes[k] / (t * 1e-3) / 1e9, 1),
-            "tok_s": round(k[1] / (t * 1e-3), 1), "launches": len(layers),
+            "tok_s": round(k[1] / (t * 1e-3), 1), "launches": len(launches),
             "gbytes": round(sweep_bytes[k] / 1e9, 4)}
     gemm_out = {}
     for i in gemm_ids:
@@ -246,8 +264,8 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "fetch_bytes_per_launch": fetch,
                     "kernel": f"gemv {dom[0]} M={dom[1]} (bf16 x, fp32 y)",
-                    "avg_launch_us": round(dom_ms * 1e3 / len(layers), 3),
-                    "bytes_per_launch": round(sweep_bytes[dom] / len(layers))}
+                    "avg_launch_us": round(dom_ms * 1e3 / len(launches), 3),
+                    "bytes_per_launch": round(sweep_bytes[dom] / len(launches))}
     roofline_gemm = None
     if gemm_ids:
         gi = max(gemm_ids, key=lambda i: ms[("gemm", i)])
@@ -266,7 +284,8 @@ def main():
         "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded packed weights, N(0,1) activations)",
         "config": {"workload": "27B-class decode weight sweep (64 blocks of q/k/v/o 5120x5120, gate/up "
-                               "17408x5120, down 5120x17408 + LM head 151936x5120; q1 then tq2; M=1 and M=16) "
+                               "17408x5120, down 5120x17408 + LM head 151936x5120; q1 then tq2; M=1 and M=16; "
+                               "q/k/v and gate/up as fused launches, 257 per sweep) "
                                "+ prefill GEMM M=512 (q1 17408x5120, tq5 5120x17408)",
                    "hbm_fraction": round(value / HBM_PEAK_GBS, 4) if value is not None else None,
                    "only": args.only},

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 2
+#define LOWBIT_ABI_VERSION 3
 
 typedef enum { LOWBIT_Q1_G128 = 1, LOWBIT_TQ2_G128 = 2, LOWBIT_TQ5_G128 = 3 } lowbit_format;
 typedef enum { LOWBIT_F16 = 1, LOWBIT_BF16 = 2, LOWBIT_F32 = 3 } lowbit_dtype;
@@ -95,6 +95,21 @@ int pack_tq2_g128(const int8_t *codes, const uint16_t *scales, int64_t N, int64_
 int pack_tq5_g128(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                   void *out, int64_t out_bytes);
 
+/* Import of MLX's grouped affine 1-bit format (1.25 bits/weight): per group
+ * of 128 weights along K a scale a and a bias b, weight = a * q + b with
+ * q in {0, 1} (lnrk.cn page, MLX packing paragraph; aberweb.com page,
+ * summary section 2).
+ *   wq: host, uint32 [N][K/32]; bit k % 32 of word k / 32 holds q[n][k]
+ *   scales, biases: host, [N][K/128] in sb_dtype (LOWBIT_F16, LOWBIT_BF16 or
+ *     LOWBIT_F32 bit patterns)
+ *   out: host, packed_bytes_lowbit(LOWBIT_Q1_G128, N, K) bytes: the Binary
+ *     g128 blob of the same matrix (bit q -> code 2q - 1, scale s = -b).
+ * A group converts exactly when a = -2 b (its two values are -s and +s)
+ * and -b is an FP16 value; any other group returns LOWBIT_ERR_VALUE and
+ * nothing is written.  Other errors as for pack_*. */
+int import_mlx_q1_g128(const uint32_t *wq, const void *scales, const void *biases, int sb_dtype,
+                       int64_t N, int64_t K, void *out, int64_t out_bytes);
+
 /* Exact inverse of pack_* (host memory).  codes_out int8 [N][K] and
  * scales_out uint16 [N][K/128] are caller-owned; either may be NULL to skip it. */
 int unpack_lowbit(int fmt, const void *packed, int64_t packed_bytes, int64_t N, int64_t K,
@@ -127,6 +142,32 @@ int64_t gemv_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
 int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype,
                 int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
                 void *hip_stream);
+
+/* Matrices one fused decode call may cover. */
+#define LOWBIT_MAX_FUSED 4
+
+/* Workspace for gemv_multi_lowbit over these matrices (same meaning and
+ * rules as gemv_workspace_bytes_lowbit).  Ns: host array of count row counts.
+ * Returns a negative status on a bad format, count or shape. */
+int64_t gemv_multi_workspace_bytes_lowbit(int fmt, int count, const int64_t *Ns, int64_t M, int64_t K);
+
+/* Fused decode GEMV: Y_i = X W_i^T for i < count (1..LOWBIT_MAX_FUSED), for
+ * matrices that share the activations X and K, such as the query, key and
+ * value projections, or the gate and up projections, of a transformer block
+ * (serving with draft-token verification makes M small but above one:
+ * lnrk.cn page, DSpark section; ksqn.cn page).  One launch covers the row
+ * tiles of all of them, so the fixed cost of a launch is paid once.
+ *   Ws: host array of count device pointers, the packed blob of (fmt, Ns[i], K)
+ *   Ns: host array of count row counts (0 allowed: that matrix is skipped)
+ *   Ys: host array of count device pointers, M x Ns[i] each, y_dtype
+ *   X, x_dtype, y_dtype, M, K, workspace, hip_stream: as for gemv_lowbit
+ * Each Y_i obeys the same bound as gemv_lowbit.  Base-3 (tq5) weights run
+ * one matrix at a time on the prefill kernel.  Errors as for gemv_lowbit,
+ * checked for every matrix before anything is launched; a count outside
+ * 1..LOWBIT_MAX_FUSED is LOWBIT_ERR_SHAPE. */
+int gemv_multi_lowbit(int fmt, int count, const void *const *Ws, const int64_t *Ns, const void *X,
+                      int x_dtype, void *const *Ys, int y_dtype, int64_t M, int64_t K,
+                      void *workspace, int64_t workspace_bytes, void *hip_stream);
 
 /* Workspace that lets gemm_lowbit balance its work over the whole chip: the
  * (tile, 128-weight group) work items are cut into one contiguous range per

@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE ONLY: nothing in the product imports this package.
 MLX stores, for every group of 128 weights along K, a scale a and a bias b
 next to the bits, so that a weight is a * q + b with q in {0, 1}; storing two
 16-bit values per group is what makes its 1-bit package 1.25 bits per weight
-against 1.125 for the scale-only format (cnblogs.com page, section 2; lnrk.cn
-page, the MLX packing paragraph).  The bits sit 32 to a uint32 word along K,
+against 1.125 for the scale-only format (lnrk.cn page, the MLX packing
+paragraph; aberweb.com page, summary section 2).  The bits sit 32 to a
+uint32 word along K,
 lowest bit first (q[n, k] is bit k % 32 of word k // 32).
 
 A group holds the two values b (q = 0) and a + b (q = 1).  It is a Binary

@@ -52,8 +52,11 @@ def load() -> ctypes.CDLL:
         "pack_tq2_g128": (i32, [vp, vp, i64, i64, vp, i64]),
         "pack_tq5_g128": (i32, [vp, vp, i64, i64, vp, i64]),
         "unpack_lowbit": (i32, [i32, vp, i64, i64, i64, vp, vp]),
+        "import_mlx_q1_g128": (i32, [vp, vp, vp, i32, i64, i64, vp, i64]),
         "gemv_workspace_bytes_lowbit": (i64, [i32, i64, i64, i64]),
         "gemv_lowbit": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp, i64, vp]),
+        "gemv_multi_workspace_bytes_lowbit": (i64, [i32, i32, vp, i64, i64]),
+        "gemv_multi_lowbit": (i32, [i32, i32, vp, vp, vp, i32, vp, i32, i64, i64, vp, i64, vp]),
         "gemm_workspace_bytes_lowbit": (i64, [i32, i64, i64, i64]),
         "gemm_lowbit": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp, i64, vp]),
     }
@@ -103,6 +106,34 @@ def pack(fmt, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     out = np.empty(packed_bytes(f, N, K), dtype=np.uint8)
     fn = {1: load().pack_q1_g128, 2: load().pack_tq2_g128, 3: load().pack_tq5_g128}[f]
     _check(fn(codes.ctypes.data, scales.ctypes.data, N, K, out.ctypes.data, out.size))
+    return out
+
+
+def import_mlx_q1(wq: np.ndarray, scales: np.ndarray, biases: np.ndarray, dtype: str = "f16") -> np.ndarray:
+    """MLX affine 1-bit g128 -> Binary g128 blob (see import_mlx_q1_g128).
+
+    wq uint32[N, K/32] (bit k % 32 of word k / 32 is q[n, k]); scales and
+    biases [N, K/128] as bit patterns (uint16 for dtype "f16" / "bf16",
+    uint32 for "f32") or as float16 / float32 arrays."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint32)
+    N, W = wq.shape
+    K = 32 * W
+    sb = {"f16": DT_F16, "bf16": DT_BF16, "f32": DT_F32}[dtype]
+    bits = np.uint32 if sb == DT_F32 else np.uint16
+
+    def as_bits(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype in (np.float16, np.float32):
+            a = a.view(bits)
+        a = np.ascontiguousarray(a, dtype=bits)
+        if a.shape != (N, K // GROUP):
+            raise ValueError("scales and biases must have shape (N, K // 128)")
+        return a
+
+    scales, biases = as_bits(scales), as_bits(biases)
+    out = np.empty(packed_bytes(1, N, K), dtype=np.uint8)
+    _check(load().import_mlx_q1_g128(wq.ctypes.data, scales.ctypes.data, biases.ctypes.data, sb, N, K,
+                                     out.ctypes.data, out.size))
     return out
 
 
@@ -184,6 +215,57 @@ def gemv(fmt, w, x, N: int, K: int, out_dtype=None, out=None, workspace=None, st
     _check(load().gemv_lowbit(f, w.data_ptr(), x.data_ptr(), _x_dtype(x), out.data_ptr(), _y_dtype(out.dtype),
                               M, N, K, ws_ptr, ws_n, s))
     return out
+
+
+MAX_FUSED = 4
+
+
+def _ptr_arrays(ptrs, Ns):
+    n = len(ptrs)
+    return (ctypes.c_void_p * n)(*ptrs), (ctypes.c_int64 * n)(*Ns)
+
+
+def gemv_multi_workspace_bytes(fmt, Ns, M: int, K: int) -> int:
+    arr = (ctypes.c_int64 * len(Ns))(*Ns)
+    n = load().gemv_multi_workspace_bytes_lowbit(_fmt(fmt), len(Ns), arr, M, K)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def gemv_multi(fmt, ws, x, Ns, K: int, out_dtype=None, outs=None, workspace=None, stream=None):
+    """[x @ W_i^T for each i] in one fused launch (matrices sharing x and K,
+    e.g. q/k/v or gate/up).  ws: list of packed uint8 device tensors; Ns:
+    their row counts.  workspace as for gemv()."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    if len(ws) != len(Ns) or not 1 <= len(ws) <= MAX_FUSED:
+        raise ValueError(f"need 1..{MAX_FUSED} matrices with one row count each")
+    f = _fmt(fmt)
+    outs = list(outs) if outs is not None else [None] * len(ws)
+    prepped = [_prep(f, w, x, N, K, out_dtype, o) for w, N, o in zip(ws, Ns, outs)]
+    xx, M = prepped[0][1], prepped[0][2]
+    outs = [p[3] for p in prepped]
+    if workspace is None:
+        need = gemv_multi_workspace_bytes(f, Ns, M, K)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=xx.device) if need else False
+    ws_ptr = workspace.data_ptr() if workspace is not False else None
+    ws_n = workspace.numel() if workspace is not False else 0
+    s = stream if stream is not None else torch.cuda.current_stream(xx.device).cuda_stream
+    wa, na = _ptr_arrays([w.data_ptr() for w in ws], Ns)
+    ya = (ctypes.c_void_p * len(outs))(*[o.data_ptr() for o in outs])
+    _check(load().gemv_multi_lowbit(f, len(ws), wa, na, xx.data_ptr(), _x_dtype(xx), ya, _y_dtype(out_dtype), M, K,
+                                    ws_ptr, ws_n, s))
+    return outs
+
+
+def gemv_multi_raw(fmt: int, w_ptrs, Ns, x_ptr: int, x_dtype: int, y_ptrs, y_dtype: int, M: int, K: int,
+                   stream_ptr: int, ws_ptr: int = 0, ws_bytes: int = 0) -> None:
+    """Pointer-level fused call (no tensor checks) for tight timing loops."""
+    wa, na = _ptr_arrays(w_ptrs, Ns)
+    ya = (ctypes.c_void_p * len(y_ptrs))(*y_ptrs)
+    _check(load().gemv_multi_lowbit(fmt, len(w_ptrs), wa, na, x_ptr, x_dtype, ya, y_dtype, M, K, ws_ptr or None,
+                                    ws_bytes, stream_ptr))
 
 
 def gemm_workspace_bytes(fmt, M: int, N: int, K: int) -> int:

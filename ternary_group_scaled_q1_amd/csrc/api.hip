@@ -45,6 +45,7 @@ int run(bool gemm, int fmt, const void *Wp, const void *X, int x_dtype, void *Y,
   a.y_f16 = y_dtype == LOWBIT_F16;
   a.M = M; a.N = N; a.K = K;
   a.stream = static_cast<hipStream_t>(stream);
+  single_matrix(a);
   hipError_t e;
   if (K == 0) {
     e = launch_fill_zero(Y, M * N * (a.y_f16 ? 2 : 4), a.stream);
@@ -54,6 +55,24 @@ int run(bool gemm, int fmt, const void *Wp, const void *X, int x_dtype, void *Y,
     e = launch_gemv(a);
   }
   return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_DEVICE;
+}
+
+// Rows of a fused launch: each matrix rounded up to whole 16-row tiles.
+int64_t launch_rows(int count, const int64_t *Ns) {
+  int64_t nv = 0;
+  for (int i = 0; i < count; ++i) nv += (Ns[i] + 15) / 16 * 16;
+  return nv;
+}
+
+int check_multi_shape(int fmt, int count, const int64_t *Ns, int64_t M, int64_t K) {
+  if (fmt < LOWBIT_Q1_G128 || fmt > LOWBIT_TQ5_G128) return LOWBIT_ERR_ENUM;
+  if (count < 1 || count > kMaxMats) return LOWBIT_ERR_SHAPE;
+  if (!Ns) return LOWBIT_ERR_NULL;
+  if (M < 0 || K < 0 || K % kGroup) return LOWBIT_ERR_SHAPE;
+  for (int i = 0; i < count; ++i)
+    if (Ns[i] < 0 || Ns[i] > (1 << 30)) return LOWBIT_ERR_SHAPE;
+  if (M * launch_rows(count, Ns) >= (int64_t(1) << 31)) return LOWBIT_ERR_SHAPE;
+  return LOWBIT_OK;
 }
 
 }  // namespace
@@ -98,6 +117,64 @@ int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0 || K % kGroup) return LOWBIT_ERR_SHAPE;
   if (M == 0 || N == 0 || K == 0) return 0;
   return gemm_workspace_bytes(fmt, M, N, K);
+}
+
+int64_t gemv_multi_workspace_bytes_lowbit(int fmt, int count, const int64_t *Ns, int64_t M, int64_t K) {
+  const int st = check_multi_shape(fmt, count, Ns, M, K);
+  if (st != LOWBIT_OK) return st;
+  const int64_t nv = launch_rows(count, Ns);
+  if (M == 0 || nv == 0 || K == 0) return 0;
+  return gemv_workspace_bytes(fmt, M, nv, K);
+}
+
+int gemv_multi_lowbit(int fmt, int count, const void *const *Ws, const int64_t *Ns, const void *X, int x_dtype,
+                      void *const *Ys, int y_dtype, int64_t M, int64_t K, void *workspace, int64_t workspace_bytes,
+                      void *hip_stream) {
+  int st = check_multi_shape(fmt, count, Ns, M, K);
+  if (st != LOWBIT_OK) return st;
+  if (!Ws || !Ys) return LOWBIT_ERR_NULL;
+  for (int i = 0; i < count; ++i) {
+    st = check_product(fmt, Ws[i], X, x_dtype, Ys[i], y_dtype, M, Ns[i], K);
+    if (st != LOWBIT_OK) return st;
+  }
+  if (workspace_bytes < 0) return LOWBIT_ERR_SIZE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 15)) return LOWBIT_ERR_ALIGN;
+  if (M == 0) return LOWBIT_OK;
+  // Matrices without rows take no part.
+  LaunchArgs a;
+  a.nmat = 0;
+  for (int i = 0; i < count; ++i) {
+    if (Ns[i] == 0) continue;
+    a.Ws[a.nmat] = static_cast<const uint8_t *>(Ws[i]);
+    a.Ys[a.nmat] = Ys[i];
+    a.Ns[a.nmat] = Ns[i];
+    ++a.nmat;
+  }
+  if (a.nmat == 0) return LOWBIT_OK;
+  hipError_t e = hipSuccess;
+  if (K == 0 || fmt == LOWBIT_TQ5_G128) {
+    // Base-3 weights run on the prefill kernel, one matrix at a time.
+    for (int i = 0; i < a.nmat; ++i) {
+      st = run(false, fmt, a.Ws[i], X, x_dtype, a.Ys[i], y_dtype, M, a.Ns[i], K, workspace, workspace_bytes,
+               hip_stream);
+      if (st != LOWBIT_OK) return st;
+    }
+    return LOWBIT_OK;
+  }
+  a.ws = workspace;
+  a.ws_bytes = workspace ? workspace_bytes : 0;
+  a.fmt = fmt;
+  a.W = a.Ws[0];
+  a.X = static_cast<const uint16_t *>(X);
+  a.Y = a.Ys[0];
+  a.x_bf16 = x_dtype == LOWBIT_BF16;
+  a.y_f16 = y_dtype == LOWBIT_F16;
+  a.M = M;
+  a.N = launch_rows(a.nmat, a.Ns);
+  a.K = K;
+  a.stream = static_cast<hipStream_t>(hip_stream);
+  e = launch_gemv(a);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_DEVICE;
 }
 
 int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M, int64_t N,

@@ -48,11 +48,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
 struct GemvParams {
-  const uint8_t *W;    // plane A
-  const uint16_t *Sc;  // plane B: FP16 scales [N][G]
+  MatSet ms;           // the matrices (row tiles numbered across them)
   const uint16_t *X;   // [M][K]
-  void *Y;             // [M][N]
-  int M, N, K, G;
+  int M, K, G;
   int tiles, chunks;
   int S;         // waves splitting the chunks of a stage
   int SC;        // chunks per stage (multiple of S)
@@ -215,15 +213,12 @@ __device__ __forceinline__ void store_tiles(const GemvParams &p, int t0, const f
   const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int n = 16 * (t0 + r) + j;
-    if (n >= p.N) continue;
+    if (t0 + r >= p.tiles) continue;
+    const TileRef tr = tile_ref(p.ms, t0 + r);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int m = 4 * q + e;
-      if (m >= p.M) continue;
-      const float v = yacc[r][e] * mul;
-      if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
-      else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+      if (m < p.M) store_y(tr, j, m, yacc[r][e] * mul, p.y_f16);
     }
   }
 }
@@ -268,15 +263,12 @@ __device__ __forceinline__ void store_fp4(const GemvParams &p, int t0, const flo
   const float mul = FMT == 1 ? 1.f : 0.5f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int n = 16 * (t0 + r) + j;
-    if (n >= p.N) continue;
+    if (t0 + r >= p.tiles) continue;
+    const TileRef tr = tile_ref(p.ms, t0 + r);
 #pragma unroll
     for (int tt = 0; tt < E / 2; ++tt) {
       const int m = 2 * qa + tt;
-      if (m >= p.M) continue;
-      const float v = (yacc[r][2 * tt] + yacc[r][2 * tt + 1]) * mul;
-      if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
-      else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+      if (m < p.M) store_y(tr, j, m, (yacc[r][2 * tt] + yacc[r][2 * tt + 1]) * mul, p.y_f16);
     }
   }
 }
@@ -427,11 +419,9 @@ double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) 
   constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
   p = GemvParams{};
   const int64_t G = a.K / kGroup;
-  p.W = a.W;
-  p.Sc = reinterpret_cast<const uint16_t *>(a.W + plane_a_bytes(a.fmt, a.N, a.K));
+  p.ms = mat_set(a);
   p.X = a.X;
-  p.Y = a.Y;
-  p.M = int(a.M); p.N = int(a.N); p.K = int(a.K); p.G = int(G);
+  p.M = int(a.M); p.K = int(a.K); p.G = int(G);
   p.tiles = int((a.N + 15) / 16);
   p.chunks = int((G + 3) / 4);
   p.tilesets = (p.tiles + R - 1) / R;
@@ -553,7 +543,8 @@ hipError_t launch_gemv(const LaunchArgs &a) {
     LaunchArgs b = a;
     b.M = a.M - m0 < 16 ? a.M - m0 : 16;
     b.X = a.X + m0 * a.K;
-    b.Y = static_cast<char *>(a.Y) + m0 * a.N * (a.y_f16 ? 2 : 4);
+    for (int i = 0; i < a.nmat; ++i) b.Ys[i] = static_cast<char *>(a.Ys[i]) + m0 * a.Ns[i] * (a.y_f16 ? 2 : 4);
+    b.Y = b.Ys[0];
     hipError_t e;
     if (a.fmt == 1) e = a.x_bf16 ? launch_fmt<1, true>(b) : launch_fmt<1, false>(b);
     else e = a.x_bf16 ? launch_fmt<2, true>(b) : launch_fmt<2, false>(b);

@@ -3,12 +3,87 @@
 // and its branch-free load.
 #pragma once
 #include "device.hpp"
+#include "kernels.hpp"
 #include "layout.hpp"
 
 namespace lowbit {
 namespace {
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The matrices of one launch as the kernels see them: row tiles of all of
+// them are numbered one after the other (each matrix starts a new tile), so
+// a launch over several matrices that share x walks one tile range.
+struct MatSet {
+  const uint8_t *W[kMaxMats];   // plane A
+  const uint16_t *Sc[kMaxMats];  // plane B: FP16 scales [N][G]
+  void *Y[kMaxMats];             // [M][N]
+  int N[kMaxMats];
+  int tile_end[kMaxMats];        // tiles of matrices 0..i; the total past the last
+};
+
+inline MatSet mat_set(const LaunchArgs &a) {
+  MatSet m{};
+  int end = 0;
+  for (int i = 0; i < kMaxMats; ++i) {
+    const int k = i < a.nmat ? i : a.nmat - 1;
+    m.W[i] = a.Ws[k];
+    m.Sc[i] = reinterpret_cast<const uint16_t *>(a.Ws[k] + plane_a_bytes(a.fmt, a.Ns[k], a.K));
+    m.Y[i] = a.Ys[k];
+    m.N[i] = int(a.Ns[k]);
+    if (i < a.nmat) end += int((a.Ns[k] + 15) / 16);
+    m.tile_end[i] = end;
+  }
+  return m;
+}
+
+// Matrix and local tile of launch tile vt (wave-uniform: scalar selects).
+struct TileRef {
+  const uint8_t *W;
+  const uint16_t *Sc;
+  void *Y;
+  int N, t;
+};
+
+// Each field read passes through readfirstlane before the selects: a select
+// between two fields read straight from the parameter block would be folded
+// into one load at a computed offset, which forces a copy of the whole block
+// into scratch memory.
+template <class T>
+__device__ __forceinline__ T *uni_ptr(T *ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<T *>((uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ TileRef tile_ref(const MatSet &m, int vt) {
+  TileRef r{uni_ptr(m.W[0]), uni_ptr(m.Sc[0]), uni_ptr(m.Y[0]), uni(m.N[0]), vt};
+#pragma unroll
+  for (int i = 1; i < kMaxMats; ++i) {
+    const int e = uni(m.tile_end[i - 1]);
+    const bool c = vt >= e;
+    const uint8_t *w = uni_ptr(m.W[i]);
+    const uint16_t *sc = uni_ptr(m.Sc[i]);
+    void *y = uni_ptr(m.Y[i]);
+    const int n = uni(m.N[i]);
+    r.W = c ? w : r.W;
+    r.Sc = c ? sc : r.Sc;
+    r.Y = c ? y : r.Y;
+    r.N = c ? n : r.N;
+    r.t = c ? vt - e : r.t;
+  }
+  return r;
+}
+
+// Stores value v of token m at row 16 t + j of the tile's matrix (rows past
+// the matrix are skipped).
+__device__ __forceinline__ void store_y(const TileRef &tr, int j, int m, float v, bool y_f16) {
+  const int n = 16 * tr.t + j;
+  if (n >= tr.N) return;
+  if (y_f16) reinterpret_cast<uint16_t *>(tr.Y)[(int64_t)m * tr.N + n] = float_to_half_rne(v);
+  else reinterpret_cast<float *>(tr.Y)[(int64_t)m * tr.N + n] = v;
+}
 
 // One A row of a group in the fp8 x fp4 path's LDS staging: 128 bytes of
 // pieces in lane order plus 16 bytes that spread the rows over the LDS banks.
@@ -25,7 +100,8 @@ struct Unit {
 // Loads are issued without per-lane branches (ragged tiles clamp their
 // addresses and zero the values afterwards): a divergent branch around a
 // load makes the compiler wait for every outstanding load at the join, which
-// would drain the prefetch ring.  P provides W, Sc, N, G and tiles.
+// would drain the prefetch ring.  P provides ms (the matrices), G and tiles
+// (tiles of the launch).
 template <int FMT, int R, class P>
 __device__ __forceinline__ void load_unit(const P &p, Unit<FMT, R> &u, int t0, int c, bool valid) {
   const int lane = threadIdx.x & 63;
@@ -42,8 +118,9 @@ __device__ __forceinline__ void load_unit(const P &p, Unit<FMT, R> &u, int t0, i
       u.s[r][0] = u.s[r][1] = 0;
       continue;
     }
-    const int RT = uni(min(16, p.N - 16 * t));
-    const uint8_t *blk = p.W + 16 * (int64_t)t * p.G * unit + (int64_t)RT * 4 * c * unit;
+    const TileRef tr = tile_ref(p.ms, t);
+    const int RT = uni(min(16, tr.N - 16 * tr.t));
+    const uint8_t *blk = tr.W + 16 * (int64_t)tr.t * p.G * unit + (int64_t)RT * 4 * c * unit;
     if (RT == 16 && Gc == 4 && (p.G & 3) == 0) {  // wave-uniform fast path
       const u4_t v0 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk) + lane);
       u.w[r][0] = v0.x; u.w[r][1] = v0.y; u.w[r][2] = v0.z; u.w[r][3] = v0.w;
@@ -51,13 +128,13 @@ __device__ __forceinline__ void load_unit(const P &p, Unit<FMT, R> &u, int t0, i
         const u4_t v1 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk + 1024) + lane);
         u.w[r][4] = v1.x; u.w[r][5] = v1.y; u.w[r][6] = v1.z; u.w[r][7] = v1.w;
       }
-      const u2_t sv = *reinterpret_cast<const u2_t *>(p.Sc + (int64_t)(16 * t + j) * p.G + 4 * c);
+      const u2_t sv = *reinterpret_cast<const u2_t *>(tr.Sc + (int64_t)(16 * tr.t + j) * p.G + 4 * c);
       u.s[r][0] = sv.x; u.s[r][1] = sv.y;
     } else {
       const bool row_ok = j < RT;
       const int jj = min(j, RT - 1);
       const uint32_t *base = reinterpret_cast<const uint32_t *>(blk);
-      const uint16_t *srow = p.Sc + (int64_t)(16 * t + jj) * p.G + 4 * c;
+      const uint16_t *srow = tr.Sc + (int64_t)(16 * tr.t + jj) * p.G + 4 * c;
       uint32_t h[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {

@@ -43,13 +43,12 @@ constexpr int kSWaves = 8;
 constexpr int kSThreads = 64 * kSWaves;
 
 struct SplitParams {
-  const uint8_t *W;    // plane A
-  const uint16_t *Sc;  // plane B: FP16 scales [N][G]
+  MatSet ms;           // the matrices (row tiles numbered across them)
   const uint16_t *X;   // [M][K]
-  void *Y;             // [M][N]
-  float *part;         // [KS][M][N] partial sums (KS > 1)
+  float *part;         // [KS][M][NV] partial sums (KS > 1)
   unsigned *count;     // [row_blocks] arrival counters, 0 between calls
-  int M, N, K, G, tiles;
+  int M, K, G, tiles;
+  int NV;          // launch rows: 16 x tiles
   int GK;          // groups per K range (a multiple of 4 when KS > 1)
   int KS;          // K ranges
   int GP;          // groups per staging pass (a multiple of 4)
@@ -224,34 +223,32 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
   if (p.KS == 1) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int n = 16 * (t0 + r) + j;
-      if (n >= p.N) continue;
+      if (t0 + r >= p.tiles) continue;
+      const TileRef tr = tile_ref(p.ms, t0 + r);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int m = 8 * tb + 2 * qa + tt;
-          if (m >= p.M) continue;
-          const float v = ys[r][tb][tt] * mul;
-          if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
-          else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+          if (m < p.M) store_y(tr, j, m, ys[r][tb][tt] * mul, p.y_f16);
         }
     }
     return;
   }
 
-  // K split across workgroups: publish this range's partial sums.
+  // K split across workgroups: publish this range's partial sums (at launch
+  // rows, every row of a tile included).
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int n = 16 * (t0 + r) + j;
-    if (n >= p.N) continue;
+    if (t0 + r >= p.tiles) continue;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int m = 8 * tb + 2 * qa + tt;
         if (m >= p.M) continue;
-        __hip_atomic_store(p.part + ((int64_t)ks * p.M + m) * p.N + n, ys[r][tb][tt], __ATOMIC_RELAXED,
+        __hip_atomic_store(p.part + ((int64_t)ks * p.M + m) * p.NV + n, ys[r][tb][tt], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
   }
@@ -264,15 +261,13 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
   if (!last_flag) return;
   // Last workgroup of the block: Y = sum over ranges in range order.
   const int n0 = rb * 8 * R * 16;
-  const int rows = min(8 * R * 16, p.N - n0);
+  const int rows = min(8 * R * 16, p.NV - n0);
   for (int idx = threadIdx.x; idx < p.M * rows; idx += kSThreads) {
     const int m = idx / rows, n = n0 + idx % rows;
     float v = 0.f;
     for (int k2 = 0; k2 < p.KS; ++k2)
-      v += __hip_atomic_load(p.part + ((int64_t)k2 * p.M + m) * p.N + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    v *= mul;
-    if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
-    else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+      v += __hip_atomic_load(p.part + ((int64_t)k2 * p.M + m) * p.NV + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_y(tile_ref(p.ms, n >> 4), n & 15, m, v * mul, p.y_f16);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -313,12 +308,11 @@ struct SplitPlan {
 template <int FMT, int MP, int R>
 void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
   SplitParams p{};
-  p.W = a.W;
-  p.Sc = reinterpret_cast<const uint16_t *>(a.W + plane_a_bytes(a.fmt, a.N, a.K));
+  p.ms = mat_set(a);
   p.X = a.X;
-  p.Y = a.Y;
-  p.M = int(a.M); p.N = int(a.N); p.K = int(a.K); p.G = int(a.K / kGroup);
+  p.M = int(a.M); p.K = int(a.K); p.G = int(a.K / kGroup);
   p.tiles = int((a.N + 15) / 16);
+  p.NV = 16 * p.tiles;
   p.y_f16 = a.y_f16;
   p.row_blocks = (p.tiles + 8 * R - 1) / (8 * R);
   p.GP = pass_groups(MP, p.G);
@@ -330,8 +324,8 @@ void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
     const int gk = GK < p.G ? GK : p.G;
     const int KS = (p.G + gk - 1) / gk;
     if (KS > kMaxKS) continue;
-    if (KS > 1 && (gk % 4 || (int64_t)KS * a.M * a.N * 4 > kMaxPartBytes || p.row_blocks > kMaxCounters ||
-                   split_ws_bytes(a.M, a.N, KS) > ws_bytes))
+    if (KS > 1 && (gk % 4 || (int64_t)KS * a.M * p.NV * 4 > kMaxPartBytes || p.row_blocks > kMaxCounters ||
+                   split_ws_bytes(a.M, p.NV, KS) > ws_bytes))
       continue;
     const int64_t wgs = (int64_t)p.row_blocks * KS;
     const double rounds = double((wgs + slots - 1) / slots);
@@ -386,6 +380,7 @@ int64_t gemv_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   // The counters plus the largest partial-sum area any plan may use
   // (16-token launches).
   const int64_t m = M < 16 ? M : 16;
+  N = (N + 15) / 16 * 16;  // partial sums are kept for whole row tiles
   int64_t ks = kMaxPartBytes / (m * N * 4);
   if (ks > kMaxKS) ks = kMaxKS;
   if (ks > K / kGroup) ks = K / kGroup;

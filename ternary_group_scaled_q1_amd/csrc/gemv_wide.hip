@@ -20,6 +20,7 @@
 // per group), as on the aberweb.com page, section 4.1: the signs are decoded
 // inside the kernel and no dense weight tensor exists.
 #include "device.hpp"
+#include "gemv_common.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
 
@@ -31,18 +32,14 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
 struct WideParams {
-  const uint8_t *W;    // plane A
-  const uint16_t *Sc;  // plane B: FP16 scales [N][G]
+  MatSet ms;           // the matrices (row tiles numbered across them)
   const uint16_t *X;   // [M][K]
-  void *Y;             // [M][N]
-  int M, N, K, G;
+  int M, K, G;
   int tiles, tilesets;
   int S;    // waves of a wave-row splitting the groups
   int GS;   // groups per wave (ceil(G / S))
   int y_f16;
 };
-
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 template <int FMT, int R>
 struct WUnit {
@@ -91,11 +88,12 @@ __device__ __forceinline__ void load_wunit(const WideParams &p, WUnit<FMT, R> &u
       u.s[r] = 0;
       continue;
     }
-    const int RT = uni(min(16, p.N - 16 * t));
+    const TileRef tr = tile_ref(p.ms, t);
+    const int RT = uni(min(16, tr.N - 16 * tr.t));
     const bool row_ok = j < RT;
     const int jj = min(j, RT - 1);
     const uint32_t *blk =
-        reinterpret_cast<const uint32_t *>(p.W + 16 * (int64_t)t * p.G * unit + (int64_t)RT * 4 * c * unit);
+        reinterpret_cast<const uint32_t *>(tr.W + 16 * (int64_t)tr.t * p.G * unit + (int64_t)RT * 4 * c * unit);
     if constexpr (FMT == 1) {
       const uint32_t w = __builtin_nontemporal_load(blk + (q * RT + jj) * Gc + gc);
       u.w[r][0] = row_ok ? w : 0u;
@@ -106,7 +104,7 @@ __device__ __forceinline__ void load_wunit(const WideParams &p, WUnit<FMT, R> &u
       u.w[r][0] = row_ok ? w.x : 0u;
       u.w[r][1] = row_ok ? w.y : 0u;
     }
-    const uint32_t sv = p.Sc[(int64_t)(16 * t + jj) * p.G + g];
+    const uint32_t sv = tr.Sc[(int64_t)(16 * tr.t + jj) * p.G + g];
     u.s[r] = row_ok ? sv : 0u;
   }
 }
@@ -139,15 +137,12 @@ __device__ __forceinline__ void store_wide(const WideParams &p, int t0, const fl
   const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int n = 16 * (t0 + r) + j;
-    if (n >= p.N) continue;
+    if (t0 + r >= p.tiles) continue;
+    const TileRef tr = tile_ref(p.ms, t0 + r);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = 4 * q + e;
-      if (m >= p.M) continue;
-      const float v = yacc[r][e] * mul;
-      if (p.y_f16) reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = float_to_half_rne(v);
-      else reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = v;
+      if (m < p.M) store_y(tr, j, m, yacc[r][e] * mul, p.y_f16);
     }
   }
 }
@@ -232,11 +227,9 @@ __global__ void __launch_bounds__(kThreads, 2) gemv_wide_kernel(WideParams p) {
 template <class Kern>
 double plan_wide(const LaunchArgs &a, int R, Kern kernel, WideParams &p, int &grid) {
   p = WideParams{};
-  p.W = a.W;
-  p.Sc = reinterpret_cast<const uint16_t *>(a.W + plane_a_bytes(a.fmt, a.N, a.K));
+  p.ms = mat_set(a);
   p.X = a.X;
-  p.Y = a.Y;
-  p.M = int(a.M); p.N = int(a.N); p.K = int(a.K); p.G = int(a.K / kGroup);
+  p.M = int(a.M); p.K = int(a.K); p.G = int(a.K / kGroup);
   p.tiles = int((a.N + 15) / 16);
   p.tilesets = (p.tiles + R - 1) / R;
   p.y_f16 = a.y_f16;

@@ -3,7 +3,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/lowbit.h"
+
 namespace lowbit {
+
+// Matrices that one fused decode launch may cover (they share X and K).
+constexpr int kMaxMats = LOWBIT_MAX_FUSED;
 
 struct LaunchArgs {
   int fmt;                // 1 q1, 2 tq2, 3 tq5
@@ -16,7 +21,22 @@ struct LaunchArgs {
   void *ws;          // caller-owned device workspace (may be NULL)
   int64_t ws_bytes;  // its size in bytes
   hipStream_t stream;
+  // The matrices of the launch: nmat = 1 and (W, N, Y) for a single product;
+  // for a fused decode launch N is the rows of all of them, each rounded up
+  // to whole 16-row tiles, and (W, Y) are those of the first.
+  int nmat = 1;
+  const uint8_t *Ws[kMaxMats] = {};
+  void *Ys[kMaxMats] = {};
+  int64_t Ns[kMaxMats] = {};
 };
+
+// Fills the matrix list of a single-matrix launch.
+inline void single_matrix(LaunchArgs &a) {
+  a.nmat = 1;
+  a.Ws[0] = a.W;
+  a.Ys[0] = a.Y;
+  a.Ns[0] = a.N;
+}
 
 // Each returns a hipError_t of the launch (hipSuccess when nothing to do).
 hipError_t launch_gemv(const LaunchArgs &a);

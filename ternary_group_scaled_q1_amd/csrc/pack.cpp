@@ -7,7 +7,9 @@
 // arrangement of bits is the device layout v1 described in layout.hpp.
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstring>
+#include <limits>
 #include <thread>
 #include <vector>
 
@@ -55,7 +57,9 @@ static bool codes_valid(const int8_t *codes, int64_t n, bool binary) {
 }
 
 // ------------------------------------------------------------- q1 / tq2 ---
-static void pack_bits(int fmt, const int8_t *codes, const Geom &g, uint8_t *plane) {
+// code(n, k) gives the code of row n, column k (-1/+1, or -1/0/+1).
+template <class Code>
+static void pack_bits(int fmt, Code code, const Geom &g, uint8_t *plane) {
   const int64_t unit = fmt == 1 ? 16 : 32;
   parallel_for(g.tiles, [&](int64_t T) {
     const int64_t R = std::min<int64_t>(16, g.N - 16 * T);
@@ -65,12 +69,12 @@ static void pack_bits(int fmt, const int8_t *codes, const Geom &g, uint8_t *plan
       for (int q = 0; q < 4; ++q)
         for (int64_t j = 0; j < R; ++j)
           for (int64_t gi = 0; gi < Gc; ++gi) {
-            const int8_t *row = codes + (16 * T + j) * g.K + (4 * c + gi) * kGroup;
+            const int64_t n = 16 * T + j, k0 = (4 * c + gi) * kGroup;
             if (fmt == 1) {
               uint32_t w = 0;
               for (int u = 0; u < 4; ++u)
                 for (int e = 0; e < 8; ++e)
-                  if (row[32 * u + 8 * q + e] == 1) w |= 1u << q1_pos(u, e);
+                  if (code(n, k0 + 32 * u + 8 * q + e) == 1) w |= 1u << q1_pos(u, e);
               store_u32(blk + 4 * ((q * R + j) * Gc + gi), w);
             } else {
               const int64_t hh = gi / 2, Gh = std::min<int64_t>(2, Gc - 2 * hh);
@@ -80,8 +84,8 @@ static void pack_bits(int fmt, const int8_t *codes, const Geom &g, uint8_t *plan
                 for (int uu = 0; uu < 2; ++uu)
                   for (int e = 0; e < 8; ++e) {
                     int u = 2 * v + uu;
-                    uint32_t code = uint32_t(row[32 * u + 8 * q + e] + 1);
-                    w |= code << tq2_pos(u, e);
+                    const uint32_t cv = uint32_t(code(n, k0 + 32 * u + 8 * q + e) + 1);
+                    w |= cv << tq2_pos(u, e);
                   }
                 store_u32(half + 4 * (((q * R + j) * Gh + (gi - 2 * hh)) * 2 + v), w);
               }
@@ -217,9 +221,61 @@ static int pack_any(int fmt, const int8_t *codes, const uint16_t *scales, int64_
   const Geom g = geom(N, K);
   uint8_t *plane = static_cast<uint8_t *>(out);
   if (fmt == 3) pack_tq5(codes, g, plane);
-  else pack_bits(fmt, codes, g, plane);
+  else pack_bits(fmt, [&](int64_t n, int64_t k) { return codes[n * K + k]; }, g, plane);
   std::memcpy(plane + plane_a_bytes(fmt, N, K), scales, size_t(N * g.G * 2));
   return LOWBIT_OK;
+}
+
+// ------------------------------------------------------------ MLX import ---
+// MLX's grouped affine format stores, per group of 128 weights, a scale and
+// a bias next to the packed bits, w = scale * q + bias, which is why its 1-bit
+// package costs 1.25 bits per weight against 1.125 for the scale-only
+// format (lnrk.cn page, MLX packing paragraph; aberweb.com page, summary
+// section 2).  A group whose two values are {bias, scale + bias} = {-s, +s},
+// i.e. scale = -2 bias, is a Binary g128 group with scale s = -bias and the
+// same bits (bit 1 -> +s).
+
+static double half_value(uint16_t h) {
+  const int e = (h >> 10) & 31, f = h & 1023;
+  double v;
+  if (e == 31) v = f ? std::numeric_limits<double>::quiet_NaN() : std::numeric_limits<double>::infinity();
+  else if (e == 0) v = std::ldexp(double(f), -24);
+  else v = std::ldexp(double(1024 + f), e - 25);
+  return (h & 0x8000) ? -v : v;
+}
+
+static double float_value(uint32_t u) {
+  float f;
+  std::memcpy(&f, &u, 4);
+  return double(f);
+}
+
+// The FP16 pattern of v when v is exactly representable, else false.
+static bool half_exact(double v, uint16_t &out) {
+  if (!std::isfinite(v)) return false;
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  const double a = std::fabs(v);
+  if (a == 0.0) { out = sign; return true; }
+  if (a > 65504.0) return false;
+  int E;
+  std::frexp(a, &E);  // a = m 2^E, m in [0.5, 1)
+  const int e = E - 1;
+  if (e >= -14) {
+    const double f = std::ldexp(a, 10 - e);  // in [1024, 2048)
+    if (f != std::floor(f)) return false;
+    out = uint16_t(sign | ((e + 15) << 10) | (uint16_t(f) - 1024));
+  } else {
+    const double f = std::ldexp(a, 24);
+    if (f != std::floor(f)) return false;
+    out = uint16_t(sign | uint16_t(f));
+  }
+  return true;
+}
+
+static double affine_value(const void *base, int dtype, int64_t i) {
+  if (dtype == LOWBIT_F32) return float_value(static_cast<const uint32_t *>(base)[i]);
+  const uint16_t h = static_cast<const uint16_t *>(base)[i];
+  return dtype == LOWBIT_F16 ? half_value(h) : float_value(uint32_t(h) << 16);
 }
 
 }  // namespace lowbit
@@ -245,6 +301,40 @@ int pack_tq2_g128(const int8_t *codes, const uint16_t *scales, int64_t N, int64_
 int pack_tq5_g128(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K, void *out,
                   int64_t out_bytes) {
   return pack_any(3, codes, scales, N, K, out, out_bytes);
+}
+
+int import_mlx_q1_g128(const uint32_t *wq, const void *scales, const void *biases, int sb_dtype, int64_t N,
+                       int64_t K, void *out, int64_t out_bytes) {
+  if (sb_dtype < LOWBIT_F16 || sb_dtype > LOWBIT_F32) return LOWBIT_ERR_ENUM;
+  int st = check_fmt_shape(1, N, K);
+  if (st) return st;
+  const int64_t need = packed_bytes_lowbit(1, N, K);
+  if (need > 0 && (!wq || !scales || !biases || !out)) return LOWBIT_ERR_NULL;
+  if (out_bytes < need) return LOWBIT_ERR_SIZE;
+  if (need == 0) return LOWBIT_OK;
+  const Geom g = geom(N, K);
+  // Every group is checked before anything is written.
+  std::vector<uint16_t> sc(size_t(N * g.G));
+  std::atomic<bool> ok(true);
+  parallel_for(N, [&](int64_t n) {
+    for (int64_t gi = 0; gi < g.G; ++gi) {
+      const double a = affine_value(scales, sb_dtype, n * g.G + gi);
+      const double b = affine_value(biases, sb_dtype, n * g.G + gi);
+      uint16_t h;
+      if (!std::isfinite(a) || a != -2.0 * b || !half_exact(-b, h)) {
+        ok = false;
+        return;
+      }
+      sc[size_t(n * g.G + gi)] = h;
+    }
+  });
+  if (!ok) return LOWBIT_ERR_VALUE;
+  const int64_t words = K / 32;
+  uint8_t *plane = static_cast<uint8_t *>(out);
+  pack_bits(1, [&](int64_t n, int64_t k) -> int8_t { return ((wq[n * words + k / 32] >> (k % 32)) & 1) ? 1 : -1; },
+            g, plane);
+  std::memcpy(plane + plane_a_bytes(1, N, K), sc.data(), size_t(N * g.G * 2));
+  return LOWBIT_OK;
 }
 
 int unpack_lowbit(int fmt, const void *packed, int64_t packed_bytes, int64_t N, int64_t K,

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(lb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert lb.abi_version() == 2
+    assert lb.abi_version() == 3
 
 
 def test_strerror_covers_all_codes():
@@ -162,3 +162,88 @@ def test_single_hip_runtime_in_process():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, check=True)
     libs = eval(out.stdout.strip().splitlines()[-1])
     assert len(libs) == 1, libs
+
+
+def _mlx_matrix(g, N, K, dtype):
+    """Random MLX affine 1-bit matrix whose groups are {-s, +s} (a = 2s, b = -s)."""
+    s = synth.scales_absnormal(g, N, K // 128)
+    sv = s.view(np.float16).astype(np.float64) * np.where(g.random((N, K // 128)) < 0.1, -1.0, 1.0)
+    enc = {"f16": synth.f64_to_f16_bits, "bf16": synth.f64_to_bf16_bits,
+           "f32": lambda v: np.asarray(v, dtype=np.float32).view(np.uint32)}[dtype]
+    if dtype == "bf16":
+        # keep s exact in bf16: round it to 8 significant bits first
+        sv = synth.f64_to_bf16_bits(sv).astype(np.uint32)
+        sv = (sv << 16).view(np.float32).astype(np.float64)
+    wq = g.integers(0, 2 ** 32, size=(N, K // 32), dtype=np.uint64).astype(np.uint32)
+    return wq, enc(2 * sv), enc(-sv)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_import_mlx_matches_oracle(dtype):
+    """The library's import equals the oracle's exact Binary g128 form, packed
+    by the oracle's own packer, byte for byte."""
+    from oracle import mlx
+    g = np.random.default_rng(81)
+    for N, K in [(1, 128), (17, 640), (40, 1152)]:
+        wq, a, b = _mlx_matrix(g, N, K, dtype)
+        blob = lb.import_mlx_q1(wq, a, b, dtype)
+        codes, s = mlx.to_binary(wq, a, b, dtype)
+        assert np.array_equal(blob, layout.pack("q1", codes, s)), (dtype, N, K)
+
+
+def test_import_mlx_rejections():
+    g = np.random.default_rng(82)
+    N, K = 4, 256
+    wq, a, b = _mlx_matrix(g, N, K, "f32")
+    bad = b.copy()
+    bad[2, 1] = np.float32(np.float32(bad[2, 1].view(np.float32)) * 2).view(np.uint32)  # a != -2b
+    with pytest.raises(lb.LowbitError) as e:
+        lb.import_mlx_q1(wq, a, bad, "f32")
+    assert e.value.status == -4
+    tiny_a = np.full((N, K // 128), np.float32(2 ** -30)).view(np.uint32)
+    tiny_b = np.full((N, K // 128), np.float32(-2 ** -31)).view(np.uint32)
+    with pytest.raises(lb.LowbitError) as e:
+        lb.import_mlx_q1(wq, tiny_a, tiny_b, "f32")   # s below fp16 subnormals
+    assert e.value.status == -4
+    L = lb.load()
+    out = np.zeros(lb.packed_bytes("q1", N, K), dtype=np.uint8)
+    assert L.import_mlx_q1_g128(wq.ctypes.data, a.ctypes.data, b.ctypes.data, 9, N, K, out.ctypes.data,
+                                out.size) == -2
+    assert L.import_mlx_q1_g128(wq.ctypes.data, a.ctypes.data, b.ctypes.data, 3, N, 100, out.ctypes.data,
+                                out.size) == -3
+    assert L.import_mlx_q1_g128(None, a.ctypes.data, b.ctypes.data, 3, N, K, out.ctypes.data, out.size) == -1
+    assert L.import_mlx_q1_g128(wq.ctypes.data, a.ctypes.data, b.ctypes.data, 3, N, K, out.ctypes.data,
+                                out.size - 1) == -5
+    assert not out.any()  # nothing written on error
+
+
+def test_gemv_multi_validation():
+    """Fused decode GEMV: shapes, counts and pointers are checked for every
+    matrix before any launch (no GPU work is reached here)."""
+    L = lb.load()
+    I64 = ctypes.c_int64
+    VP = ctypes.c_void_p
+    Ns = (I64 * 3)(5120, 1024, 1024)
+    assert L.gemv_multi_workspace_bytes_lowbit(1, 3, Ns, 16, 5120) == lb.gemv_workspace_bytes("q1", 16, 7168, 5120)
+    assert L.gemv_multi_workspace_bytes_lowbit(1, 0, Ns, 16, 5120) == -3
+    assert L.gemv_multi_workspace_bytes_lowbit(1, 5, Ns, 16, 5120) == -3
+    assert L.gemv_multi_workspace_bytes_lowbit(1, 3, None, 16, 5120) == -1
+    assert L.gemv_multi_workspace_bytes_lowbit(1, 3, Ns, 16, 100) == -3
+    assert L.gemv_multi_workspace_bytes_lowbit(7, 3, Ns, 16, 5120) == -2
+    bad = (I64 * 2)(17, -1)
+    assert L.gemv_multi_workspace_bytes_lowbit(1, 2, bad, 1, 128) == -3
+    # ragged rows round up to whole 16-row tiles in the launch
+    assert lb.gemv_multi_workspace_bytes("q1", [17, 33], 16, 5120) == lb.gemv_workspace_bytes("q1", 16, 80, 5120)
+    W = (VP * 2)(4096, 8192)
+    Y = (VP * 2)(4096, 8192)
+    N2 = (I64 * 2)(16, 16)
+    args = lambda cnt, w, y, K=128: (1, cnt, w, N2, 4096, 2, y, 1, 1, K, None, 0, None)
+    assert L.gemv_multi_lowbit(*args(0, W, Y)) == -3
+    assert L.gemv_multi_lowbit(*args(5, W, Y)) == -3
+    assert L.gemv_multi_lowbit(*args(2, None, Y)) == -1
+    assert L.gemv_multi_lowbit(*args(2, W, None)) == -1
+    assert L.gemv_multi_lowbit(*args(2, (VP * 2)(4096, 8200), Y)) == -6       # second W misaligned
+    assert L.gemv_multi_lowbit(*args(2, (VP * 2)(4096, None), Y)) == -1       # second W missing
+    assert L.gemv_multi_lowbit(*args(2, W, Y, K=100)) == -3
+    # M = 0: nothing to do
+    assert L.gemv_multi_lowbit(1, 2, W, N2, 4096, 2, Y, 1, 0, 128, None, 0, None) == 0

@@ -368,3 +368,68 @@ def test_gemm_shared_workspace_and_split_tiles():
             else:
                 assert np.array_equal(yv, first[idx])
     assert not ws[:65536].any(), "stream-K counters must be left at zero"
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+def test_mlx_affine_import_product(path):
+    """An MLX affine 1-bit g128 matrix imported into Binary g128 gives the
+    product of MLX's own dequantised weights (scale * q + bias), within the
+    bound."""
+    from oracle import fp, mlx
+    g = np.random.default_rng(600)
+    N, K, M = (300, 1280, 3) if path == "gemv" else (200, 640, 130)
+    s = synth.scales_absnormal(g, N, K // 128).view(np.float16).astype(np.float64)
+    a, b = synth.f64_to_f16_bits(2 * s), synth.f64_to_f16_bits(-s)
+    wq = g.integers(0, 2 ** 32, size=(N, K // 32), dtype=np.uint64).astype(np.uint32)
+    blob = gu.w_tensor(lb.import_mlx_q1(wq, a, b, "f16"))
+    x = synth.x_normal(g, M, K, "bf16")
+    y = gu.run(path, "q1", blob, x, "bf16", "f32", N, K)
+    w = mlx.dequant(wq, a, b, "f16")
+    xf = fp.decode(x, "bf16")
+    y_ref, a_ref = xf @ w.T, np.abs(xf) @ np.abs(w).T
+    ok, worst = ref.within_tolerance(y, y_ref, a_ref)
+    assert ok, f"mlx import {path}: worst ratio {worst}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_gemv_multi_fused(fmt, xdt):
+    """One fused launch over several matrices sharing x (ragged row counts,
+    a matrix without rows, 1..16 tokens): every output within the bound, and
+    a second call with a shared workspace bitwise identical to the first."""
+    t = gu.torch()
+    g = np.random.default_rng(700)
+    cases = [(1, [17, 300, 64], 1280), (3, [5120, 1024, 1024], 640), (16, [48, 0, 130], 2048),
+             (9, [16, 16, 16, 16], 17408), (2, [4100], 384)]
+    for M, Ns, K in cases:
+        print(f"multi {fmt} {xdt} M={M} Ns={Ns} K={K}", flush=True)
+        mats = []
+        for N in Ns:
+            codes = _codes(g, fmt, N, K)
+            sc = synth.scales_absnormal(g, N, K // 128)
+            mats.append((codes, sc, gu.w_tensor(lb.pack(fmt, codes, sc))))
+        x = synth.x_normal(g, M, K, xdt)
+        xt = gu.x_tensor(x, xdt)
+        need = lb.gemv_multi_workspace_bytes(fmt, Ns, M, K)
+        ws = t.zeros(max(need, 16), dtype=t.uint8, device="cuda")
+        for ydt in ("f32", "f16"):
+            odt = t.float32 if ydt == "f32" else t.float16
+            ys = lb.gemv_multi(fmt, [m[2] for m in mats], xt, Ns, K, out_dtype=odt, workspace=ws)
+            ys2 = lb.gemv_multi(fmt, [m[2] for m in mats], xt, Ns, K, out_dtype=odt, workspace=ws)
+            t.cuda.synchronize()
+            for i, ((codes, sc, _), y, y2) in enumerate(zip(mats, ys, ys2)):
+                assert t.equal(y, y2), (fmt, M, Ns, i)
+                if Ns[i] == 0:
+                    continue
+                yn = y.float().cpu().numpy().astype(np.float64)
+                if ydt == "f32":
+                    gu.check(yn, codes, sc, x, xdt, f"multi {fmt} {xdt} M={M} Ns={Ns} mat {i}")
+                else:
+                    y_ref, a_ref = ref.product(codes, sc, x, xdt)
+                    assert np.all(np.abs(yn - y_ref) <= ref.RTOL * a_ref + ref.ATOL + np.abs(y_ref) * 2.0 ** -11)
+        # no workspace: the paths that need none
+        ys = lb.gemv_multi(fmt, [m[2] for m in mats], xt, Ns, K, workspace=False)
+        t.cuda.synchronize()
+        for i, ((codes, sc, _), y) in enumerate(zip(mats, ys)):
+            if Ns[i]:
+                gu.check(y.cpu().numpy().astype(np.float64), codes, sc, x, xdt, f"multi no-ws {fmt} mat {i}")
