@@ -73,6 +73,7 @@ struct GemmParams {
   int tiles_m, tiles_n;
   int64_t items;  // tiles * G
   int per;        // items per workgroup
+  int last_chunk_groups;  // groups in the last chunk of 4 (1..4)
   int y_f16;
   // tq5 geometry
   int s_full, L_tail, b_tail, rowbytes;
@@ -241,17 +242,18 @@ __device__ __forceinline__ void tq5_decode(const char *slot, const uint16_t *lut
   }
 }
 
-// The stream of items this workgroup loads: position (tile, group) and the
-// lane addresses that depend only on the tile, refreshed when the tile
-// changes, so that issuing an item's loads is a few adds per load.
+// The stream of items this workgroup loads, two ahead of the one it
+// multiplies: position (tile, group), the tile's coordinates and the lane
+// addresses that depend only on the tile (refreshed when the tile changes),
+// so that issuing an item's loads is a few adds per load.
 template <int FMT>
 struct Feed {
   int tile, g, mt, nt;
-  const uint16_t *xrow[2];    // activation rows of the wave's blocks (+ 8q), see x_blocks
-  const uint8_t *tbase[2];    // n-blocks 2wm, 2wm+1: tile block start (+ lane part for tq5)
-  int woff[2], RR[2];         // lane word index q*RR + jj, rows of the block (>= 1)
-  const uint8_t *scrow;       // this lane's scale row
-  const uint8_t *xfill;       // tq5: an in-bounds activation block for segments without raw bytes
+  const uint16_t *xrow[2];  // activation rows of the wave's row blocks (+ 8q), see x_blocks
+  const uint8_t *wb[2];     // n-blocks 2wm, 2wm+1: tile block start (tq5: + lane part)
+  uint32_t wl[2];           // q1: 4 woff, tq2: 8 woff (woff = lane word index q RR + j)
+  int RR[2];                // rows of the block (>= 1)
+  const uint8_t *scrow;     // this lane's scale row
 };
 
 // Activation blocks (16 rows x one k-step, 1 KB) each wave loads per item:
@@ -266,23 +268,30 @@ __device__ __forceinline__ void feed_tile(const GemmParams &p, Feed<FMT> &f) {
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave / nwn<FMT>(), wn = wave % nwn<FMT>();
   const int j = lane & 15, q = lane >> 4;
-  f.mt = f.tile % p.tiles_m;
-  f.nt = f.tile / p.tiles_m;
 #pragma unroll
   for (int h = 0; h < XB / 4; ++h)
     f.xrow[h] = p.X + (int64_t)min(f.mt * kBM + 16 * (wave * (XB / 4) + h) + j, p.M - 1) * p.K + 8 * q;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const ColBlock cb = col_block<FMT>(p, f.nt, wn, 2 * wm + i);
-    const int jj = min(j, cb.RR - 1);
+    const uint32_t woff = uint32_t(q * cb.RR + min(j, cb.RR - 1));
     f.RR[i] = cb.RR;
-    f.woff[i] = q * cb.RR + jj;
-    if constexpr (FMT == 3) f.tbase[i] = p.W + 16 * (int64_t)cb.T * p.rowbytes + (q * cb.RR + jj) * 16;
-    else f.tbase[i] = p.W + 16 * (int64_t)cb.T * p.G * (FMT == 1 ? 16 : 32);
+    if constexpr (FMT == 3) {
+      f.wb[i] = p.W + 16 * (int64_t)cb.T * p.rowbytes + woff * 16;
+    } else if constexpr (FMT == 1) {
+      // word of (lane, group gc) in chunk c of Gc groups:
+      // c * RR * 64 + 4 * (woff * Gc + gc) bytes
+      f.wb[i] = p.W + 16 * (int64_t)cb.T * p.G * 16;
+      f.wl[i] = 4 * woff;
+    } else {
+      // word pair of (lane, group gc) in chunk c, half hh = gc / 2 of Gh
+      // groups: c * RR * 128 + hh * RR * 64 + 8 * (woff * Gh + gc - 2 hh) bytes
+      f.wb[i] = p.W + 16 * (int64_t)cb.T * p.G * 32;
+      f.wl[i] = 8 * woff;
+    }
   }
   const ColBlock cs = col_block<FMT>(p, f.nt, wn, 2 * wm + ((lane >> 4) & 1));
   f.scrow = p.Sc + (int64_t)(16 * cs.T + min(j, cs.RR - 1)) * p.G * 2;
-  f.xfill = reinterpret_cast<const uint8_t *>(p.X + (int64_t)min(f.mt * kBM + j, p.M - 1) * p.K + 8 * q);
 }
 
 template <int FMT>
@@ -290,36 +299,39 @@ __device__ __forceinline__ void feed_next(const GemmParams &p, Feed<FMT> &f) {
   if (++f.g == p.G) {
     f.g = 0;
     ++f.tile;
+    if (++f.mt == p.tiles_m) {
+      f.mt = 0;
+      ++f.nt;
+    }
     feed_tile<FMT>(p, f);
   }
 }
 
 // All loads of item f into activation stage xst and weight stage wst:
-// weights first, then the XB activation loads of the wave.
+// weights first, then the XB activation loads of the wave.  tq5 loads the
+// raw bytes of a segment only with `raw` (the item that decodes them).
 template <int FMT>
-__device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> &f, char *xst, char *wst) {
+__device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> &f, char *xst, char *wst, bool raw) {
   constexpr int XB = x_blocks<FMT>();
   const int wave = uni(threadIdx.x >> 6);
   const int wm = wave / nwn<FMT>(), wn = wave % nwn<FMT>();
   const int g = f.g;
   if constexpr (FMT != 3) {
     const int c = g >> 2, gc = g & 3;
-    const int Gc = min(4, p.G - 4 * c);
-    constexpr int unit = FMT == 1 ? 16 : 32;
+    const int Gc = 4 * c + 4 > p.G ? p.last_chunk_groups : 4;
+    const int hh = gc >> 1;
+    const int Gh = min(2, Gc - 2 * hh);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int nb = 2 * wm + i;
-      const uint32_t *blk = reinterpret_cast<const uint32_t *>(f.tbase[i] + (int64_t)f.RR[i] * 4 * c * unit);
       if constexpr (FMT == 1) {
-        __builtin_amdgcn_global_load_lds((const void *)(blk + f.woff[i] * Gc + gc), (lds_void *)(wst + (wn * 4 + nb) * 256),
-                                         4, 0, 0);
+        const uint8_t *a = f.wb[i] + (f.RR[i] * 64 * c + 4 * gc) + f.wl[i] * uint32_t(Gc);
+        __builtin_amdgcn_global_load_lds((const void *)a, (lds_void *)(wst + (wn * 4 + nb) * 256), 4, 0, 0);
       } else {
-        const int hh = gc >> 1, Gh = min(2, Gc - 2 * hh);
-        const uint32_t *w = blk + f.RR[i] * 16 * hh + (f.woff[i] * Gh + (gc - 2 * hh)) * 2;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          __builtin_amdgcn_global_load_lds((const void *)(w + h), (lds_void *)(wst + ((wn * 4 + nb) * 2 + h) * 256), 4,
-                                           0, 0);
+        const uint8_t *a = f.wb[i] + (f.RR[i] * (128 * c + 64 * hh) + 8 * (gc - 2 * hh)) + f.wl[i] * uint32_t(Gh);
+        __builtin_amdgcn_global_load_lds((const void *)a, (lds_void *)(wst + ((wn * 4 + nb) * 2) * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(a + 4), (lds_void *)(wst + ((wn * 4 + nb) * 2 + 1) * 256), 4,
+                                         0, 0);
       }
     }
   }
@@ -327,16 +339,17 @@ __device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> 
                                    (lds_void *)(wst + w_scale_off<FMT>() + wave * 256), 2, 0, 0);
   if constexpr (FMT == 3) {
     const int seg = g / 5;
-    const bool full = seg < p.s_full;
-    char *slot = wst + w_raw_off<FMT>();
+    if (raw && seg < p.s_full) {  // wave-uniform
+      char *slot = wst + w_raw_off<FMT>();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int nb = 2 * wm + i;
-      const uint8_t *sb = f.tbase[i] + (int64_t)f.RR[i] * 128 * seg;
+      for (int i = 0; i < 2; ++i) {
+        const int nb = 2 * wm + i;
+        const uint8_t *sb = f.wb[i] + (int64_t)f.RR[i] * 128 * seg;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        __builtin_amdgcn_global_load_lds((const void *)(full ? sb + h * f.RR[i] * 64 : f.xfill),
-                                         (lds_void *)(slot + ((wn * 4 + nb) * 2 + h) * 1024), 16, 0, 0);
+        for (int h = 0; h < 2; ++h)
+          __builtin_amdgcn_global_load_lds((const void *)(sb + h * f.RR[i] * 64),
+                                           (lds_void *)(slot + ((wn * 4 + nb) * 2 + h) * 1024), 16, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -367,17 +380,37 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
     }
   }
 
-  const int64_t i0 = (int64_t)blockIdx.x * p.per;
-  const int64_t i1 = min(i0 + p.per, p.items);
-  if (i0 >= i1) return;  // workgroup-uniform
-  const int n = int(i1 - i0);
   const int G = p.G;
-  const int first_tile = int(i0 / G);
+  // This workgroup's items [i0, i0 + n): whole tile blockIdx.x, or (stream-K,
+  // fewer than 2^31 items) a range of per items.  wf / wl: the workgroups
+  // whose ranges cover the first and the last tile of the range (only those
+  // two tiles can be split between workgroups).
+  int n, first_tile, last_tile, g0, wf0, wl0, wf1, wl1;
+  if (p.per == G) {
+    n = G;
+    first_tile = last_tile = blockIdx.x;
+    g0 = 0;
+    wf0 = wl0 = wf1 = wl1 = blockIdx.x;
+  } else {
+    const uint32_t per = uint32_t(p.per), ug = uint32_t(G);
+    const uint32_t i0 = blockIdx.x * per;
+    const uint32_t i1 = min(i0 + per, uint32_t(p.items));
+    if (i0 >= i1) return;  // workgroup-uniform
+    n = int(i1 - i0);
+    first_tile = int(i0 / ug);
+    last_tile = int((i1 - 1) / ug);
+    g0 = int(i0 - uint32_t(first_tile) * ug);
+    wf0 = int(uint32_t(first_tile) * ug / per);
+    wl0 = int((uint32_t(first_tile) * ug + ug - 1) / per);
+    wf1 = int(uint32_t(last_tile) * ug / per);
+    wl1 = int((uint32_t(last_tile) * ug + ug - 1) / per);
+  }
 
   f4_t acc[4][4];
-  TileCols tc = tile_cols<FMT>(p, first_tile / p.tiles_m);
-  int g_begin = int(i0 % G);
-  int cur_tile = first_tile, cur_g = g_begin;  // item it
+  int cur_tile = first_tile, cur_g = g0;
+  int cur_mt = first_tile % p.tiles_m, cur_nt = first_tile / p.tiles_m;
+  int g_begin = cur_g;
+  TileCols tc = tile_cols<FMT>(p, cur_nt);
 
   // tq5: decoded pairs of the current segment.
   uint32_t d5[4][16];
@@ -387,19 +420,28 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
   // Items 0 and 1 in flight; the feed then points at item 2 (it stops at
   // the last item, whose loads are repeated into otherwise unused stages).
   Feed<FMT> feed;
-  feed.tile = first_tile;
-  feed.g = g_begin;
+  feed.tile = cur_tile;
+  feed.g = cur_g;
+  feed.mt = cur_mt;
+  feed.nt = cur_nt;
   feed_tile<FMT>(p, feed);
-  feed_issue<FMT>(p, feed, xs, wring);
   int feed_it = 0;
+  auto raw_for = [&]() { return FMT == 3 && (feed_it == 0 || feed.g % 5 == 0); };
+  feed_issue<FMT>(p, feed, xs, wring, raw_for());
   if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
-  feed_issue<FMT>(p, feed, xs + kStageBytes, wring + kW);
+  feed_issue<FMT>(p, feed, xs + kStageBytes, wring + kW, raw_for());
   if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
 
   auto step = [&](int it, int slot) {
-    const int tile = cur_tile, g = cur_g;
-    if (++cur_g == G) { cur_g = 0; ++cur_tile; }
-    const int mt = tile % p.tiles_m, nt = tile / p.tiles_m;
+    const int tile = cur_tile, g = cur_g, mt = cur_mt, nt = cur_nt;
+    if (++cur_g == G) {
+      cur_g = 0;
+      ++cur_tile;
+      if (++cur_mt == p.tiles_m) {
+        cur_mt = 0;
+        ++cur_nt;
+      }
+    }
     const bool first = it == 0 || g == 0;
     const bool last = it == n - 1 || g == G - 1;
     if (first) {
@@ -407,7 +449,7 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
-      tc = tile_cols<FMT>(p, nt);
+      if constexpr (FMT == 3) tc = tile_cols<FMT>(p, nt);
       g_begin = g;
     }
     // Stage `slot` holds item it once at most the XB activation loads of
@@ -419,7 +461,8 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
     // above, and this wave's reads of the stage refilled below were consumed
     // by its MFMAs of the previous item.
     __builtin_amdgcn_s_barrier();
-    feed_issue<FMT>(p, feed, xs + ((slot + 2) % kStages) * kStageBytes, wring + ((slot + 2) % kStages) * kW);
+    feed_issue<FMT>(p, feed, xs + ((slot + 2) % kStages) * kStageBytes, wring + ((slot + 2) % kStages) * kW,
+                    raw_for());
     if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
     const char *st = xs + slot * kStageBytes;
     const char *wst = wring + slot * kW;
@@ -437,7 +480,7 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
         else return tq2_operand(wd[nb][u >> 1], u);
       });
     } else {
-      const int seg = g / 5, gs = g % 5;
+      const int seg = g / 5, gs = g - 5 * seg;
       if (seg < p.s_full) {
         if (gs == 0 || first) tq5_decode(wst + w_raw_off<FMT>(), lut, d5);
         group_mma<FMT, BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
@@ -482,6 +525,7 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
     }
     // Split tile: publish this piece (slot 0: this range's first tile, 1: its last).
     const int which = tile == first_tile ? 0 : 1;
+    const int wf = which ? wf1 : wf0, wl = which ? wl1 : wl0;
     float *piece = p.part + ((int64_t)blockIdx.x * 2 + which) * piece_floats<FMT>();
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -491,7 +535,6 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
         for (int e = 0; e < 4; ++e)
           __hip_atomic_store(piece + ((wave * 16 + a * 4 + b) * 4 + e) * 64 + lane, acc[a][b][e], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
-    const int wf = int((int64_t)tile * G / p.per), wl = int(((int64_t)tile * G + G - 1) / p.per);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's piece stores have completed
     __syncthreads();
     if (threadIdx.x == 0)
@@ -505,7 +548,8 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) sum[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
     for (int w2 = wf; w2 <= wl; ++w2) {
-      const int wh = int((int64_t)w2 * p.per / G) == tile ? 0 : 1;
+      // Piece 0 of workgroup w2 belongs to the first tile of its range.
+      const int wh = int(uint32_t(w2) * uint32_t(p.per) / uint32_t(G)) == tile ? 0 : 1;
       const float *pc = p.part + ((int64_t)w2 * 2 + wh) * piece_floats<FMT>();
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -540,6 +584,7 @@ hipError_t launch_t(const LaunchArgs &a) {
   p.Y = a.Y;
   p.M = int(a.M); p.N = int(a.N); p.K = int(a.K); p.G = int(a.K / kGroup);
   p.tiles_m = int((a.M + kBM - 1) / kBM);
+  p.last_chunk_groups = p.G - 4 * ((p.G - 1) / 4);
   p.tiles_n = int((a.N + bn_of<FMT>() - 1) / bn_of<FMT>());
   p.y_f16 = a.y_f16;
   const Tq5Geom t = tq5_geom(a.K);
@@ -548,7 +593,7 @@ hipError_t launch_t(const LaunchArgs &a) {
   p.items = tiles * p.G;
   const int slots = stream_k_slots();
   int grid;
-  const bool sk = a.ws && tiles <= kCounterBytes / 4 && tiles > slots / 2 &&
+  const bool sk = a.ws && tiles <= kCounterBytes / 4 && tiles > slots / 2 && p.items < (int64_t(1) << 31) &&
                   a.ws_bytes >= kCounterBytes + (int64_t)slots * 2 * piece_floats<FMT>() * 4;
   if (sk) {
     p.per = int((p.items + slots - 1) / slots);
