@@ -276,6 +276,7 @@ def main():
                          "frac": round(2 * M * N * K / (gt * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "kernel": f"gemm {fmt} {M}x{N}x{K}", "avg_launch_us": round(gt * 1e3, 3)}
 
+    probes = platform_probes(torch, dev) if args.only is None else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     out = {
@@ -290,9 +291,43 @@ def main():
                    "hbm_fraction": round(value / HBM_PEAK_GBS, 4) if value is not None else None,
                    "only": args.only},
         "sweeps": per_sweep, "prefill_gemm": gemm_out,
-        "roofline": roofline, "roofline_gemm": roofline_gemm, "cpu_baseline": cpu,
+        "roofline": roofline, "roofline_gemm": roofline_gemm, "platform_probes": probes, "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def platform_probes(torch, dev):
+    """What this machine sustains outside this library, as context for the
+    rooflines (untimed by the step): a 1 GiB device copy (HBM read + write)
+    and torch's dense bf16 matmul (the platform BLAS) at the q1 prefill
+    shape 512 x 17408 x 5120, with N(0,1) operands."""
+    out = {}
+    src = torch.empty(1 << 28, device=dev, dtype=torch.float32).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["hbm_copy_GBps"] = round(2 * src.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    M, N, K = 512, 17408, 5120
+    a = torch.randn((M, K), device=dev).to(torch.bfloat16)
+    b = torch.randn((K, N), device=dev).to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    e0.record()
+    for _ in range(20):
+        c = torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    out["dense_bf16_matmul_TFLOPs"] = round(2 * M * N * K * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    out["dense_bf16_matmul_shape"] = f"{M}x{N}x{K}"
+    del a, b, c
+    return out
 
 
 def _source_digest():

@@ -161,8 +161,7 @@ int64_t gemv_multi_workspace_bytes_lowbit(int fmt, int count, const int64_t *Ns,
  *   Ns: host array of count row counts (0 allowed: that matrix is skipped)
  *   Ys: host array of count device pointers, M x Ns[i] each, y_dtype
  *   X, x_dtype, y_dtype, M, K, workspace, hip_stream: as for gemv_lowbit
- * Each Y_i obeys the same bound as gemv_lowbit.  Base-3 (tq5) weights run
- * one matrix at a time on the prefill kernel.  Errors as for gemv_lowbit,
+ * Each Y_i obeys the same bound as gemv_lowbit.  Errors as for gemv_lowbit,
  * checked for every matrix before anything is launched; a count outside
  * 1..LOWBIT_MAX_FUSED is LOWBIT_ERR_SHAPE. */
 int gemv_multi_lowbit(int fmt, int count, const void *const *Ws, const int64_t *Ns, const void *X,

@@ -49,7 +49,7 @@ int run(bool gemm, int fmt, const void *Wp, const void *X, int x_dtype, void *Y,
   hipError_t e;
   if (K == 0) {
     e = launch_fill_zero(Y, M * N * (a.y_f16 ? 2 : 4), a.stream);
-  } else if (gemm || fmt == LOWBIT_TQ5_G128) {
+  } else if (gemm) {
     e = launch_gemm(a);
   } else {
     e = launch_gemv(a);
@@ -152,8 +152,7 @@ int gemv_multi_lowbit(int fmt, int count, const void *const *Ws, const int64_t *
   }
   if (a.nmat == 0) return LOWBIT_OK;
   hipError_t e = hipSuccess;
-  if (K == 0 || fmt == LOWBIT_TQ5_G128) {
-    // Base-3 weights run on the prefill kernel, one matrix at a time.
+  if (K == 0) {
     for (int i = 0; i < a.nmat; ++i) {
       st = run(false, fmt, a.Ws[i], X, x_dtype, a.Ys[i], y_dtype, M, a.Ns[i], K, workspace, workspace_bytes,
                hip_stream);

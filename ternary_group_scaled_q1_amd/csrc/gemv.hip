@@ -547,7 +547,8 @@ hipError_t launch_gemv(const LaunchArgs &a) {
     b.Y = b.Ys[0];
     hipError_t e;
     if (a.fmt == 1) e = a.x_bf16 ? launch_fmt<1, true>(b) : launch_fmt<1, false>(b);
-    else e = a.x_bf16 ? launch_fmt<2, true>(b) : launch_fmt<2, false>(b);
+    else if (a.fmt == 2) e = a.x_bf16 ? launch_fmt<2, true>(b) : launch_fmt<2, false>(b);
+    else e = launch_gemv_tq5(b);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

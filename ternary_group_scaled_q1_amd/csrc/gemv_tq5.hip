@@ -1,0 +1,363 @@
+// Decode GEMV for Ternary g128 at 5 trits per byte (tq5), up to 16 tokens:
+// Y[m][n] = sum_k X[m][k] t[n][k] s[n][k/128].
+//
+// Base-3 packing stores 5 trits in a byte (cnblogs.com page, section 2.4),
+// 1.725 bits per weight against 2.125 for 2-bit slots, so the same HBM rate
+// streams 23% more weights.  In device layout v1 a row is cut into 640-trit
+// segments (5 groups): byte w = 8u + e of lane (q, j)'s 32 segment bytes holds
+// the weight at in-group offset 32u + 8q + e of all five groups, digit i for
+// group i.  A unit of work is R row tiles x one segment: per tile a lane loads
+// its 32 bytes (two 16-byte loads; a full tile's segment is 2 KB contiguous)
+// and the rows' five FP16 scales, turns each pair of bytes into one word of
+// five (sign, non-zero) bit pairs through a 243-entry LDS table (bits 15-2i /
+// 14-2i hold trit i of both bytes), and one shift and one AND then give the
+// exact 2t bf16/f16 operand pair of group i.  As in the other decode kernels
+// the products run on v_mfma_f32_16x16x32 (x as A: lane 16q + j reads 8
+// values of token j), each group fills a fresh fp32 tile that is added as
+// s * tile, and no dense weight tensor exists (aberweb.com page, section
+// 4.1).
+//
+// The activations are read straight into registers, one group ahead of the
+// MFMAs that use them (x is small and shared by every workgroup, so the L2
+// and the CU's L1 serve it).  A segment's raw bytes arrive one unit ahead.
+// The 8 waves of a workgroup form wave-rows of S waves that split the
+// segments; their partial sums are added through LDS in a fixed order.  The
+// tail of a row (K mod 640 trits, stored row-major) takes a slow per-weight
+// path; it is at most 4 of every 5 groups of one segment.
+#include "device.hpp"
+#include "gemv_common.hpp"
+#include "kernels.hpp"
+#include "layout.hpp"
+
+namespace lowbit {
+
+namespace {
+
+constexpr int kT5Waves = 8;
+constexpr int kT5Threads = 64 * kT5Waves;
+
+struct T5Params {
+  MatSet ms;          // the matrices (row tiles numbered across them)
+  const uint16_t *X;  // [M][K]
+  int M, K, G;
+  int tiles, tilesets;
+  int nseg;           // segments per row (full ones, plus one for a tail)
+  int s_full, b_tail, rowbytes;
+  int S;              // waves of a wave-row splitting the segments
+  int SS;             // segments per wave (ceil(nseg / S))
+  int y_f16;
+};
+
+// Raw segment bytes and scales of R tiles for one lane.
+template <int R>
+struct T5Unit {
+  u4_t a[R], b[R];    // bytes 0..15 and 16..31 of the lane's segment bytes
+  uint16_t s[R][5];   // FP16 scales of the segment's groups (0 past K)
+};
+
+// Branch-free loads (ragged tiles clamp addresses and zero values); tail and
+// invalid units load nothing into a / b.
+template <int R>
+__device__ __forceinline__ void t5_load(const T5Params &p, T5Unit<R> &u, int t0, int seg, bool valid) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  const u4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = uni(t0 + r);
+    u.a[r] = z;
+    u.b[r] = z;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) u.s[r][i] = 0;
+    if (!valid || t >= p.tiles) continue;  // wave-uniform
+    const TileRef tr = tile_ref(p.ms, t);
+    const int RT = uni(min(16, tr.N - 16 * tr.t));
+    const bool row_ok = j < RT;
+    const int jj = min(j, RT - 1);
+    const uint8_t *tb = tr.W + 16 * (int64_t)tr.t * p.rowbytes;
+    if (seg < p.s_full) {  // wave-uniform
+      const uint8_t *sb = tb + (int64_t)RT * 128 * seg + (q * RT + jj) * 16;
+      const u4_t va = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(sb));
+      const u4_t vb = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(sb + RT * 64));
+      u.a[r] = row_ok ? va : z;
+      u.b[r] = row_ok ? vb : z;
+    }
+    const uint16_t *srow = tr.Sc + (int64_t)(16 * tr.t + jj) * p.G;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int g = 5 * seg + i;
+      const uint16_t v = srow[min(g, p.G - 1)];
+      u.s[r][i] = row_ok && g < p.G ? v : uint16_t(0);
+    }
+  }
+}
+
+// x fragment of group g (4 k-steps): lane 16q + j holds x[j][128 g + 32 u + 8 q .. + 8].
+__device__ __forceinline__ void t5_load_x(const T5Params &p, u4_t (&x)[4], int g, bool valid) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  const bool tok = valid && j < p.M;
+  const uint16_t *xr = p.X + (tok ? (int64_t)j * p.K + 128 * g : 0) + 8 * q;
+  const u4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const u4_t v = *reinterpret_cast<const u4_t *>(xr + 32 * u);
+    x[u] = tok ? v : z;
+  }
+}
+
+// (sign, non-zero) words of the lane's segment bytes: d[u * 4 + p] holds the
+// five pairs of bytes 8u + 2p (low half) and 8u + 2p + 1 (high half).
+__device__ __forceinline__ void t5_decode(const u4_t &a, const u4_t &b, const uint16_t *lut, uint32_t (&d)[16]) {
+  const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const uint32_t word = wds[w >> 1];
+    const uint32_t b0 = (word >> (16 * (w & 1))) & 0xFF;
+    const uint32_t b1 = (word >> (16 * (w & 1) + 8)) & 0xFF;
+    d[w] = uint32_t(lut[b0]) | (uint32_t(lut[b1]) << 16);
+  }
+}
+
+// Tail segment (row-major bytes, B = b_tail per row): the 2t operand of
+// k-step u, group i of the tail, for this lane's row.
+__device__ __forceinline__ u4_t t5_tail_operand(const T5Params &p, const TileRef &tr, int i, int u) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  const int RT = min(16, tr.N - 16 * tr.t);
+  const int jj = min(j, RT - 1);
+  const uint8_t *rb = tr.W + 16 * (int64_t)tr.t * p.rowbytes + (int64_t)RT * 128 * p.s_full + (int64_t)jj * p.b_tail;
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int kt = 128 * i + 32 * u + 8 * q + e;
+    int v = rb[kt % p.b_tail];
+    for (int t = kt / p.b_tail; t > 0; --t) v /= 3;
+    const int dgt = v % 3;
+    h[e] = dgt == 1 ? 0u : (dgt == 2 ? 0x4000u : 0xC000u);
+  }
+  u4_t o;
+  o.x = h[0] | (h[1] << 16);
+  o.y = h[2] | (h[3] << 16);
+  o.z = h[4] | (h[5] << 16);
+  o.w = h[6] | (h[7] << 16);
+  return o;
+}
+
+template <int R>
+__device__ __forceinline__ void t5_store(const T5Params &p, int t0, const float (&yacc)[R][4]) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (t0 + r >= p.tiles) continue;
+    const TileRef tr = tile_ref(p.ms, t0 + r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * q + e;
+      if (m < p.M) store_y(tr, j, m, yacc[r][e] * 0.5f, p.y_f16);  // operands carry 2t
+    }
+  }
+}
+
+template <bool BF, int R>
+__global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
+  __shared__ uint16_t lut[256];
+  __shared__ float red[kT5Waves * R * 4 * 64];
+  for (int v = threadIdx.x; v < 256; v += kT5Threads) {
+    uint32_t f = 0;
+    int dgt = v;
+    for (int i = 0; i < 5; ++i) {
+      const int di = dgt % 3;
+      dgt /= 3;
+      f |= (uint32_t(di == 0) << (15 - 2 * i)) | (uint32_t(di != 1) << (14 - 2 * i));
+    }
+    lut[v] = uint16_t(v < 243 ? f : 0);
+  }
+  __syncthreads();
+
+  const int wave = uni(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int S = uni(p.S), P = kT5Waves / S;
+  const int pr = uni(wave / S), s = uni(wave - pr * S);
+  const int rows_total = gridDim.x * P;
+  const int my_row = pr * gridDim.x + blockIdx.x;
+  const int iters = (p.tilesets + rows_total - 1) / rows_total;
+  const int SS = uni(p.SS);
+  const int total = uni(iters * SS);
+  const int seg0 = s * SS;
+
+  auto tile0 = [&](int i) { return ((i / SS) * rows_total + my_row) * R; };
+  auto segment = [&](int i) { return seg0 + i % SS; };
+  auto valid = [&](int i) { return i < total && (i / SS) * rows_total + my_row < p.tilesets && segment(i) < p.nseg; };
+
+  T5Unit<R> cur, nxt;
+  t5_load<R>(p, cur, uni(tile0(0)), uni(segment(0)), valid(0));
+  u4_t xc[4], xn[4];
+  t5_load_x(p, xc, 5 * segment(0), valid(0));
+
+  float yacc[R][4];
+  for (int i = 0; i < total; ++i) {
+    const bool vi = valid(i);
+    const int seg = uni(segment(i));
+    const int t0 = uni(tile0(i));
+    // Next unit's weights go out before this one is worked on.
+    t5_load<R>(p, nxt, uni(tile0(i + 1)), uni(segment(i + 1)), valid(i + 1));
+    if (i % SS == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yacc[r][e] = 0.f;
+    }
+    if (vi) {  // wave-uniform
+      const int ng = uni(min(5, p.G - 5 * seg));
+      const int gnext = 5 * uni(segment(i + 1));
+      const bool vnext = valid(i + 1);
+      if (seg < p.s_full) {  // full segment: five groups through the table
+        uint32_t d[R][16];
+#pragma unroll
+        for (int r = 0; r < R; ++r) t5_decode(cur.a[r], cur.b[r], lut, d[r]);
+#pragma unroll
+        for (int gi = 0; gi < 5; ++gi) {
+          // x of the next group (of this segment, else of the next unit).
+          if (gi < 4) t5_load_x(p, xn, 5 * seg + gi + 1, true);
+          else t5_load_x(p, xn, gnext, vnext);
+          f4_t acc[R];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              u4_t bop;
+              bop.x = tq5_pair(d[r][4 * u + 0], gi);
+              bop.y = tq5_pair(d[r][4 * u + 1], gi);
+              bop.z = tq5_pair(d[r][4 * u + 2], gi);
+              bop.w = tq5_pair(d[r][4 * u + 3], gi);
+              acc[r] = u == 0 ? mfma16x16x32_zero<BF>(xc[u], bop) : mfma16x16x32<BF>(xc[u], bop, acc[r]);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const float sc = half_to_float(cur.s[r][gi]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yacc[r][e] = fmaf(sc, acc[r][e], yacc[r][e]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) xc[u] = xn[u];
+        }
+      } else {  // tail segment: ng < 5 groups, row-major bytes
+        for (int gi = 0; gi < ng; ++gi) {
+          const int gnx = gi + 1 < ng ? 5 * seg + gi + 1 : gnext;
+          t5_load_x(p, xn, gnx, gi + 1 < ng ? true : vnext);
+          f4_t acc[R];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const int t = t0 + r < p.tiles ? t0 + r : 0;
+              const u4_t bop = t5_tail_operand(p, tile_ref(p.ms, t), gi, u);
+              acc[r] = u == 0 ? mfma16x16x32_zero<BF>(xc[u], bop) : mfma16x16x32<BF>(xc[u], bop, acc[r]);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint16_t sh = gi == 0 ? cur.s[r][0] : gi == 1 ? cur.s[r][1] : gi == 2 ? cur.s[r][2] : cur.s[r][3];
+            const float sc = half_to_float(sh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yacc[r][e] = fmaf(sc, acc[r][e], yacc[r][e]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) xc[u] = xn[u];
+        }
+      }
+    } else {
+      t5_load_x(p, xc, 5 * uni(segment(i + 1)), valid(i + 1));
+    }
+    cur = nxt;
+    if (i % SS == SS - 1) {
+      const bool ts_ok = (i / SS) * rows_total + my_row < p.tilesets;
+      if (S == 1) {
+        if (ts_ok) t5_store<R>(p, t0, yacc);
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[((wave * R + r) * 4 + e) * 64 + lane] = yacc[r][e];
+        __syncthreads();
+        if (s == 0 && ts_ok) {
+          float tot[R][4];
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float v = 0.f;
+              for (int s2 = 0; s2 < S; ++s2) v += red[(((pr * S + s2) * R + r) * 4 + e) * 64 + lane];
+              tot[r][e] = v;
+            }
+          t5_store<R>(p, t0, tot);
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// Plan: the (S, grid) with the smallest per-wave work (tile sets per
+// wave-row x R x segments per wave), with a small charge for the K split.
+template <class Kern>
+double plan_tq5(const LaunchArgs &a, int R, Kern kernel, T5Params &p, int &grid) {
+  p = T5Params{};
+  p.ms = mat_set(a);
+  p.X = a.X;
+  p.M = int(a.M); p.K = int(a.K); p.G = int(a.K / kGroup);
+  p.tiles = int((a.N + 15) / 16);
+  p.tilesets = (p.tiles + R - 1) / R;
+  const Tq5Geom g = tq5_geom(a.K);
+  p.s_full = int(g.s_full);
+  p.b_tail = int(g.b_tail);
+  p.rowbytes = int(g.rowbytes);
+  p.nseg = p.s_full + (g.L_tail > 0 ? 1 : 0);
+  p.y_f16 = a.y_f16;
+  const int slots = num_cus() * resident_blocks(reinterpret_cast<const void *>(kernel), kT5Threads, 0);
+  double best = 1e300;
+  T5Params bp = p;
+  int bgrid = 1;
+  for (int S = 1; S <= 8; S *= 2) {
+    if (S > 1 && S > p.nseg) break;
+    const int P = kT5Waves / S;
+    const int gsz = max(1, min((p.tilesets + P - 1) / P, slots));
+    const int64_t rows = (int64_t)gsz * P;
+    const int SS = (p.nseg + S - 1) / S;
+    const double cost = double((p.tilesets + rows - 1) / rows) * R * SS * (S > 1 ? 1.05 : 1.0);
+    if (cost < best) {
+      best = cost;
+      bp = p;
+      bp.S = S;
+      bp.SS = SS;
+      bgrid = gsz;
+    }
+  }
+  p = bp;
+  grid = bgrid;
+  return best;
+}
+
+template <bool BF>
+hipError_t launch_tq5_t(const LaunchArgs &a) {
+  T5Params p1, p2;
+  int g1, g2;
+  const double c1 = plan_tq5(a, 1, &gemv_tq5_kernel<BF, 1>, p1, g1);
+  const double c2 = plan_tq5(a, 2, &gemv_tq5_kernel<BF, 2>, p2, g2);
+  if (c1 <= c2 * 1.1)
+    hipLaunchKernelGGL((gemv_tq5_kernel<BF, 1>), dim3(g1), dim3(kT5Threads), 0, a.stream, p1);
+  else
+    hipLaunchKernelGGL((gemv_tq5_kernel<BF, 2>), dim3(g2), dim3(kT5Threads), 0, a.stream, p2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_tq5(const LaunchArgs &a) {
+  return a.x_bf16 ? launch_tq5_t<true>(a) : launch_tq5_t<false>(a);
+}
+
+}  // namespace lowbit

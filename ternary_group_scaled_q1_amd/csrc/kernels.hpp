@@ -47,6 +47,8 @@ int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 // GEMV on fp8 x fp4 instructions with row blocks x K ranges (bf16 x, M <= 16).
 hipError_t launch_gemv_split(const LaunchArgs &a);
 int64_t gemv_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// GEMV for base-3 (tq5) weights, up to 16 tokens.
+hipError_t launch_gemv_tq5(const LaunchArgs &a);
 hipError_t launch_gemm(const LaunchArgs &a);
 // Workspace bytes that let launch_gemm split tiles across workgroups (stream-K).
 int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);

@@ -221,13 +221,23 @@ def test_workload_sweep_shapes(fmt, shape, M):
     _sampled(fmt, N, K, M, "bf16", "gemv", 5, SWEEP_SHAPES.index(shape), None if fmt == "q1" else 0.3)
 
 
+@pytest.mark.parametrize("mid", [0, 1])
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_workload_tq5_decode_27b_shapes(mid, M):
+    """Base-3 weights at the 27B-class decode shapes (34816x5120: 8 full
+    segments per row; 5120x17408: 27 full segments and a 128-trit tail)."""
+    N, K = synth.CONFIGS[3]["shapes"][mid]
+    print(f"tq5 gemv N={N} K={K} M={M}", flush=True)
+    _sampled("tq5", N, K, M, "bf16", "gemv", 3, mid, 0.3)
+
+
 def test_workload_sweep_lm_head_q1():
     print("q1 gemv N=151936 K=5120 M=1", flush=True)
     _sampled("q1", 151936, 5120, 1, "bf16", "gemv", 5, 3, None, rows=32)
 
 
 # ------------------------------------------------ bf16 x over a wide range ----
-@pytest.mark.parametrize("fmt", ["q1", "tq2"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [1, 2, 3, 8])
 def test_bf16_x_wide_dynamic_range(fmt, M):
     """bf16 activations whose magnitudes spread over 2^-40 .. 2^8 inside every
