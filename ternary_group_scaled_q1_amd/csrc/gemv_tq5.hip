@@ -48,6 +48,10 @@ struct T5Params {
   int y_f16;
 };
 
+// One token (the decode case) with x staged in LDS: x[0][0..K) as is, then
+// a zero cell that the lanes of token slots 1..15 read.
+inline int t5_xlds_bytes(int64_t K) { return int(K * 2 + 16); }
+
 // Raw segment bytes and scales of R tiles for one lane.
 template <int R>
 struct T5Unit {
@@ -106,6 +110,17 @@ __device__ __forceinline__ void t5_load_x(const T5Params &p, u4_t (&x)[4], int g
   }
 }
 
+// The same from the LDS copy of x (one token): cell k / 8 for lanes of token
+// 0, the zero cell past K for the others.
+__device__ __forceinline__ void t5_lds_x(const T5Params &p, const char *xl, u4_t (&x)[4], int g) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  const int base = j == 0 ? (128 * g + 8 * q) * 2 : p.K * 2;
+  const int step = j == 0 ? 64 : 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const u4_t *>(xl + base + step * u);
+}
+
 // (sign, non-zero) words of the lane's segment bytes: d[u * 4 + p] holds the
 // five pairs of bytes 8u + 2p (low half) and 8u + 2p + 1 (high half).
 __device__ __forceinline__ void t5_decode(const u4_t &a, const u4_t &b, const uint16_t *lut, uint32_t (&d)[16]) {
@@ -160,10 +175,19 @@ __device__ __forceinline__ void t5_store(const T5Params &p, int t0, const float 
   }
 }
 
-template <bool BF, int R>
+// XL: one token, x staged in LDS (read right before its MFMAs) and the
+// weights three units deep; else x one group ahead in registers and the
+// weights two units deep.
+template <bool BF, int R, bool XL>
 __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
   __shared__ uint16_t lut[256];
   __shared__ float red[kT5Waves * R * 4 * 64];
+  extern __shared__ __align__(16) char xl[];
+  if constexpr (XL) {
+    for (int i = threadIdx.x; i < p.K / 8; i += kT5Threads)
+      reinterpret_cast<u4_t *>(xl)[i] = reinterpret_cast<const u4_t *>(p.X)[i];
+    if (threadIdx.x == 0) *reinterpret_cast<u4_t *>(xl + p.K * 2) = u4_t{0u, 0u, 0u, 0u};
+  }
   for (int v = threadIdx.x; v < 256; v += kT5Threads) {
     uint32_t f = 0;
     int dgt = v;
@@ -191,18 +215,20 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
   auto segment = [&](int i) { return seg0 + i % SS; };
   auto valid = [&](int i) { return i < total && (i / SS) * rows_total + my_row < p.tilesets && segment(i) < p.nseg; };
 
-  T5Unit<R> cur, nxt;
+  T5Unit<R> cur, nxt, nx2;
   t5_load<R>(p, cur, uni(tile0(0)), uni(segment(0)), valid(0));
+  if constexpr (XL) t5_load<R>(p, nxt, uni(tile0(1)), uni(segment(1)), valid(1));
   u4_t xc[4], xn[4];
-  t5_load_x(p, xc, 5 * segment(0), valid(0));
+  if constexpr (!XL) t5_load_x(p, xc, 5 * segment(0), valid(0));
 
   float yacc[R][4];
   for (int i = 0; i < total; ++i) {
     const bool vi = valid(i);
     const int seg = uni(segment(i));
     const int t0 = uni(tile0(i));
-    // Next unit's weights go out before this one is worked on.
-    t5_load<R>(p, nxt, uni(tile0(i + 1)), uni(segment(i + 1)), valid(i + 1));
+    // The weights of unit i + 1 (XL: i + 2) go out before this one is worked on.
+    if constexpr (XL) t5_load<R>(p, nx2, uni(tile0(i + 2)), uni(segment(i + 2)), valid(i + 2));
+    else t5_load<R>(p, nxt, uni(tile0(i + 1)), uni(segment(i + 1)), valid(i + 1));
     if (i % SS == 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
@@ -220,7 +246,8 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
 #pragma unroll
         for (int gi = 0; gi < 5; ++gi) {
           // x of the next group (of this segment, else of the next unit).
-          if (gi < 4) t5_load_x(p, xn, 5 * seg + gi + 1, true);
+          if constexpr (XL) t5_lds_x(p, xl, xc, 5 * seg + gi);
+          else if (gi < 4) t5_load_x(p, xn, 5 * seg + gi + 1, true);
           else t5_load_x(p, xn, gnext, vnext);
           f4_t acc[R];
 #pragma unroll
@@ -241,13 +268,16 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) yacc[r][e] = fmaf(sc, acc[r][e], yacc[r][e]);
           }
+          if constexpr (!XL) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) xc[u] = xn[u];
+            for (int u = 0; u < 4; ++u) xc[u] = xn[u];
+          }
         }
       } else {  // tail segment: ng < 5 groups, row-major bytes
         for (int gi = 0; gi < ng; ++gi) {
           const int gnx = gi + 1 < ng ? 5 * seg + gi + 1 : gnext;
-          t5_load_x(p, xn, gnx, gi + 1 < ng ? true : vnext);
+          if constexpr (XL) t5_lds_x(p, xl, xc, 5 * seg + gi);
+          else t5_load_x(p, xn, gnx, gi + 1 < ng ? true : vnext);
           f4_t acc[R];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -265,14 +295,17 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) yacc[r][e] = fmaf(sc, acc[r][e], yacc[r][e]);
           }
+          if constexpr (!XL) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) xc[u] = xn[u];
+            for (int u = 0; u < 4; ++u) xc[u] = xn[u];
+          }
         }
       }
-    } else {
+    } else if constexpr (!XL) {
       t5_load_x(p, xc, 5 * uni(segment(i + 1)), valid(i + 1));
     }
     cur = nxt;
+    if constexpr (XL) nxt = nx2;
     if (i % SS == SS - 1) {
       const bool ts_ok = (i / SS) * rows_total + my_row < p.tilesets;
       if (S == 1) {
@@ -304,7 +337,7 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
 // Plan: the (S, grid) with the smallest per-wave work (tile sets per
 // wave-row x R x segments per wave), with a small charge for the K split.
 template <class Kern>
-double plan_tq5(const LaunchArgs &a, int R, Kern kernel, T5Params &p, int &grid) {
+double plan_tq5(const LaunchArgs &a, int R, Kern kernel, int lds, T5Params &p, int &grid) {
   p = T5Params{};
   p.ms = mat_set(a);
   p.X = a.X;
@@ -317,7 +350,7 @@ double plan_tq5(const LaunchArgs &a, int R, Kern kernel, T5Params &p, int &grid)
   p.rowbytes = int(g.rowbytes);
   p.nseg = p.s_full + (g.L_tail > 0 ? 1 : 0);
   p.y_f16 = a.y_f16;
-  const int slots = num_cus() * resident_blocks(reinterpret_cast<const void *>(kernel), kT5Threads, 0);
+  const int slots = num_cus() * resident_blocks(reinterpret_cast<const void *>(kernel), kT5Threads, lds);
   double best = 1e300;
   T5Params bp = p;
   int bgrid = 1;
@@ -341,17 +374,25 @@ double plan_tq5(const LaunchArgs &a, int R, Kern kernel, T5Params &p, int &grid)
   return best;
 }
 
-template <bool BF>
-hipError_t launch_tq5_t(const LaunchArgs &a) {
+template <bool BF, bool XL>
+hipError_t launch_tq5_x(const LaunchArgs &a) {
   T5Params p1, p2;
   int g1, g2;
-  const double c1 = plan_tq5(a, 1, &gemv_tq5_kernel<BF, 1>, p1, g1);
-  const double c2 = plan_tq5(a, 2, &gemv_tq5_kernel<BF, 2>, p2, g2);
+  const int lds = XL ? t5_xlds_bytes(a.K) : 0;
+  const double c1 = plan_tq5(a, 1, &gemv_tq5_kernel<BF, 1, XL>, lds, p1, g1);
+  const double c2 = plan_tq5(a, 2, &gemv_tq5_kernel<BF, 2, XL>, lds, p2, g2);
   if (c1 <= c2 * 1.1)
-    hipLaunchKernelGGL((gemv_tq5_kernel<BF, 1>), dim3(g1), dim3(kT5Threads), 0, a.stream, p1);
+    hipLaunchKernelGGL((gemv_tq5_kernel<BF, 1, XL>), dim3(g1), dim3(kT5Threads), lds, a.stream, p1);
   else
-    hipLaunchKernelGGL((gemv_tq5_kernel<BF, 2>), dim3(g2), dim3(kT5Threads), 0, a.stream, p2);
+    hipLaunchKernelGGL((gemv_tq5_kernel<BF, 2, XL>), dim3(g2), dim3(kT5Threads), lds, a.stream, p2);
   return hipGetLastError();
+}
+
+// One token whose x fits in 64 KB of LDS: staged once per workgroup.
+template <bool BF>
+hipError_t launch_tq5_t(const LaunchArgs &a) {
+  if (a.M == 1 && t5_xlds_bytes(a.K) <= 64 * 1024) return launch_tq5_x<BF, true>(a);
+  return launch_tq5_x<BF, false>(a);
 }
 
 }  // namespace
