@@ -116,11 +116,11 @@ int unpack_lowbit(int fmt, const void *packed, int64_t packed_bytes, int64_t N, 
                   int8_t *codes_out, uint16_t *scales_out);
 
 /* Workspace that lets gemv_lowbit take its fastest path for this problem
- * (0 = the fastest path needs none).  With binary weights and bf16
- * activations the decode product may cut K into ranges handled by different
- * workgroups; their fp32 partial sums live here, after 32 KiB of arrival
- * counters at its start.  The size does not depend on the device or on the
- * activation dtype; fp16 activations and ternary formats never use it.
+ * (0 = the fastest path needs none).  The decode product may cut K into
+ * ranges handled by different workgroups; their fp32 partial sums live here,
+ * after 32 KiB of arrival counters at its start.  The size does not depend
+ * on the device or on the activation dtype; base-3 (tq5) weights never use
+ * it.
  * Returns a negative status on a bad format or shape. */
 int64_t gemv_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
 

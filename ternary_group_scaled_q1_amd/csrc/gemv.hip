@@ -492,7 +492,8 @@ hipError_t launch_mt(const LaunchArgs &a) {
   return hipGetLastError();
 }
 
-// Path choice for bf16 x, from timings of the decode shapes on MI355X:
+// Path choice, from timings of the decode shapes on MI355X.
+// Binary weights with bf16 x (fp8 x fp4 kernels):
 //  * one token, or small x: the workgroup-staged kernel above (x of the
 //    whole K fits in LDS at once, no second kernel stage);
 //  * more tokens with a long K, or 9..16 tokens: the 2-D split (row blocks x
@@ -500,6 +501,9 @@ hipError_t launch_mt(const LaunchArgs &a) {
 //    caller's workspace to split K across workgroups;
 //  * 9..16 tokens on a small matrix: x loaded straight into registers
 //    (gemv_wide.hip).
+// Exact f16 / bf16 operands (ternary weights, fp16 x): the 2-D split for 2+
+// tokens on long rows or tall matrices (x staged as it is), else the staged
+// kernel for up to 4 tokens and the register kernel beyond.
 //
 // The fp8 x fp4 kernels (the staged one with FP4, and the split) hold each
 // 32-value activation block at one shared exponent: values within 2^7 of
@@ -507,12 +511,12 @@ hipError_t launch_mt(const LaunchArgs &a) {
 // it.  With binary weights every product of the block counts in the error
 // bound (|w| = s throughout a group), so that error stays below 2^-12 of the
 // bound's sum; a ternary zero can drop the large value from the sum, so tq2
-// always takes the bf16 matrix-core kernels.
+// always takes exact operands.
 template <int FMT, bool BF>
 hipError_t launch_fmt(const LaunchArgs &a) {
+  const bool ws_ok = a.ws && a.ws_bytes >= gemv_split_workspace_bytes(a.M, a.N, a.K);
   if constexpr (BF && FMT == 1) {
     constexpr int RB = 4;
-    const bool ws_ok = a.ws && a.ws_bytes >= gemv_split_workspace_bytes(a.M, a.N, a.K);
     if (a.M > 8) {
       if (a.N <= 8192 && a.K <= 8192) return launch_gemv_wide(a);
       if (ws_ok || a.N >= 65536) return launch_gemv_split(a);
@@ -525,6 +529,10 @@ hipError_t launch_fmt(const LaunchArgs &a) {
     if (a.M <= 4) return launch_mt<FMT, BF, 4, true, 2, RB>(a);
     return launch_mt<FMT, BF, 8, true, 2, RB>(a);
   } else {
+    if (a.M >= 2) {
+      const bool split = a.K >= 8192 || (a.N >= 24576 && (a.M > 4 || a.N < 65536));
+      if (split && (ws_ok || a.N >= 65536)) return launch_gemv_split(a);
+    }
     if (a.M <= 1) return launch_mt<FMT, BF, 1, false, 1, 2>(a);
     if (a.M <= 4) return launch_mt<FMT, BF, 4, false, 1, 2>(a);
     return launch_gemv_wide(a);
@@ -534,7 +542,7 @@ hipError_t launch_fmt(const LaunchArgs &a) {
 }  // namespace
 
 int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  return fmt == 1 ? gemv_split_workspace_bytes(M, N, K) : 0;
+  return fmt == 3 ? 0 : gemv_split_workspace_bytes(M, N, K);
 }
 
 hipError_t launch_gemv(const LaunchArgs &a) {

@@ -1,5 +1,8 @@
-// Decode GEMV on the fp8 x fp4 matrix instructions with a 2-D work split:
-// Y[m][n] = sum_k X[m][k] t[n][k] s[n][k/128], bf16 x, up to 16 tokens.
+// Decode GEMV with a 2-D work split: Y[m][n] = sum_k X[m][k] t[n][k] s[n][k/128],
+// up to 16 tokens.  Binary weights with bf16 x run on the fp8 x fp4 matrix
+// instructions (below); ternary weights and fp16 x take exact f16 / bf16
+// operands on v_mfma_f32_16x16x32 with x staged in LDS as it is (the same
+// work split).
 //
 // A workgroup owns a row block (8 waves x R row tiles of 16 rows) and one
 // K range of the matrix.  It converts the x of its K range once into LDS as
@@ -57,9 +60,16 @@ struct SplitParams {
   int buf_bytes;   // LDS bytes of one staging buffer
 };
 
-// LDS of one staging buffer: GP groups x 2*MP A rows, then GP*MP*4 scale bytes.
-__host__ __device__ constexpr int split_buf_bytes(int MP, int GP) {
-  return (GP * 2 * MP * kRowBytes + GP * MP * 4 + 15) / 16 * 16;
+// Operand modes: kFp4 (bf16 x as fp8 pieces, binary weights as fp4, scaled
+// 16x16x128 MFMA) or exact f16 / bf16 operands on v_mfma_f32_16x16x32
+// (kBf16, kF16: x staged as it is, weights decoded to exact +-1 / 2t).
+constexpr int kFp4 = 0, kBf16 = 1, kF16 = 2;
+
+// LDS of one staging buffer.  kFp4: GP groups x 2*MP A rows, then GP*MP*4
+// scale bytes.  Exact modes: 16-byte cells (group, k-step u, quarter q,
+// token m) of x[m][128 g + 32 u + 8 q .. + 8], then one zero cell.
+__host__ __device__ constexpr int split_buf_bytes(int MP, int GP, int MODE) {
+  return MODE == kFp4 ? (GP * 2 * MP * kRowBytes + GP * MP * 4 + 15) / 16 * 16 : GP * 16 * MP * 16 + 16;
 }
 
 // Raw x of one (token, group, lane quarter) item, held between its load and
@@ -83,10 +93,15 @@ __device__ __forceinline__ void load_raw(const SplitParams &p, RawQ &r, int g0, 
   }
 }
 
-template <int FMT, int MP>
+template <int FMT, int MP, int MODE>
 __device__ __forceinline__ void convert_raw(const SplitParams &p, const RawQ &r, char *buf, int item) {
   const int q = item & 3, rest = item >> 2;
   const int gl = rest % p.GP, m = rest / p.GP;
+  if constexpr (MODE != kFp4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u4_t *>(buf + (((gl * 4 + u) * 4 + q) * MP + m) * 16) = r.v[u];
+    return;
+  }
   XQuarter xq;
   split_x_regs<FMT>(r.v, xq);
   char *row = buf + (gl * 2 * MP + 2 * m) * kRowBytes;
@@ -140,22 +155,46 @@ __device__ __forceinline__ void compute_chunk(const SplitParams &p, const char *
   }
 }
 
-// Accumulator element e of lane 16qa + j, token block tb, is A row 4qa + e:
-// token 8 tb + 2 qa + e / 2, piece e % 2.  The two pieces add here.
-template <int R, int TB>
-__device__ __forceinline__ void token_sums(const float (&yacc)[R][TB][4], float (&y)[R][TB][2]) {
+// Exact modes: one chunk (4 groups at buffer group offset gb) for R tiles.
+// Lane 16q + j reads the cell of token j (the zero cell for j >= MP); the
+// group's 4 k-steps fill a fresh tile that is added as s * tile.
+template <int FMT, int MP, int R, int MODE>
+__device__ __forceinline__ void compute_chunk_ex(const SplitParams &p, const char *buf, const Unit<FMT, R> &u, int gb,
+                                                 int ng, float (&yacc)[R][1][4]) {
+  constexpr bool BF = MODE == kBf16;
+  const int lane = threadIdx.x & 63, q = lane >> 4, j = lane & 15;
+  const bool tok = j < MP;
+  const int zero = p.GP * 16 * MP * 16;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int gi = 0; gi < 4; ++gi) {
+    if (gi >= ng) break;  // wave-uniform: groups past K in the last chunk
+    const int gl = gb + gi;
+    u4_t a[4];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      y[r][tb][0] = yacc[r][tb][0] + yacc[r][tb][1];
-      y[r][tb][1] = yacc[r][tb][2] + yacc[r][tb][3];
+    for (int uu = 0; uu < 4; ++uu)
+      a[uu] = *reinterpret_cast<const u4_t *>(buf + (tok ? (((gl * 4 + uu) * 4 + q) * MP + j) * 16 : zero));
+#pragma unroll
+    for (int r2 = 0; r2 < R; ++r2) {
+      f4_t acc;
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        u4_t b;
+        if constexpr (FMT == 1) b = q1_operand_pm1<BF>(u.w[r2][gi], uu);
+        else b = tq2_operand(u.w[r2][2 * gi + (uu >> 1)], uu);
+        acc = uu == 0 ? mfma16x16x32_zero<BF>(a[uu], b) : mfma16x16x32<BF>(a[uu], b, acc);
+      }
+      const float s = half_to_float(uint16_t(u.s[r2][gi >> 1] >> (16 * (gi & 1))));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yacc[r2][0][e] = fmaf(s, acc[e], yacc[r2][0][e]);
     }
+  }
 }
 
-template <int FMT, int MP, int R>
+template <int FMT, int MP, int R, int MODE>
 __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p) {
-  constexpr int TB = MP > 8 ? 2 : 1;
+  // Accumulator sets per tile: fp4 A rows hold (token, piece) pairs, 8 tokens
+  // per MFMA; exact operands hold 16 tokens per MFMA.
+  constexpr int TB = MODE == kFp4 && MP > 8 ? 2 : 1;
   extern __shared__ __align__(16) char lds[];
   __shared__ int last_flag;
   const int wave = uni(threadIdx.x >> 6);
@@ -178,7 +217,13 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
   RawQ raw;
   bool live;
   load_raw<MP>(p, raw, g0, min(p.GP, ng), threadIdx.x, live);
-  if (live) convert_raw<FMT, MP>(p, raw, lds, threadIdx.x);
+  if (live) convert_raw<FMT, MP, MODE>(p, raw, lds, threadIdx.x);
+  if constexpr (MODE != kFp4) {
+    if (threadIdx.x == 0) {
+      *reinterpret_cast<u4_t *>(lds + p.GP * 16 * MP * 16) = u4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u4_t *>(lds + p.buf_bytes + p.GP * 16 * MP * 16) = u4_t{0u, 0u, 0u, 0u};
+    }
+  }
   __syncthreads();
 
   float yacc[R][TB][4];
@@ -199,7 +244,8 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
     if (more) load_raw<MP>(p, raw, g0 + pg0 + p.GP, min(p.GP, ng - pg0 - p.GP), threadIdx.x, live);
     // Chunks of this pass (GP is a multiple of 4, so passes hold whole chunks).
     for (int cc = 0; cc < (png + 3) / 4; cc += 2) {
-      compute_chunk<FMT, MP, R, TB>(p, cur, u0, 4 * cc, min(4, png - 4 * cc), yacc);
+      if constexpr (MODE == kFp4) compute_chunk<FMT, MP, R, TB>(p, cur, u0, 4 * cc, min(4, png - 4 * cc), yacc);
+      else compute_chunk_ex<FMT, MP, R, MODE>(p, cur, u0, 4 * cc, min(4, png - 4 * cc), yacc);
       if (c + 2 < nchunks) load_unit<FMT, R>(p, u0, t0, c0 + c + 2, true);
       ++c;
       if (cc + 1 >= (png + 3) / 4) {
@@ -209,49 +255,47 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
         u1 = t;
         break;
       }
-      compute_chunk<FMT, MP, R, TB>(p, cur, u1, 4 * (cc + 1), min(4, png - 4 * (cc + 1)), yacc);
+      if constexpr (MODE == kFp4) compute_chunk<FMT, MP, R, TB>(p, cur, u1, 4 * (cc + 1), min(4, png - 4 * (cc + 1)), yacc);
+      else compute_chunk_ex<FMT, MP, R, MODE>(p, cur, u1, 4 * (cc + 1), min(4, png - 4 * (cc + 1)), yacc);
       if (c + 2 < nchunks) load_unit<FMT, R>(p, u1, t0, c0 + c + 2, true);
       ++c;
     }
-    if (more && live) convert_raw<FMT, MP>(p, raw, nxt, threadIdx.x);
+    if (more && live) convert_raw<FMT, MP, MODE>(p, raw, nxt, threadIdx.x);
     __syncthreads();
   }
 
-  float ys[R][TB][2];
-  token_sums<R, TB>(yacc, ys);
+  // This lane's outputs: (tile r, token m, value).  fp4: element e of lane
+  // 16qa + j, token block tb, is A row 4qa + e (token 8 tb + 2 qa + e / 2,
+  // piece e % 2; the pieces add here); exact: token 4q + e.
   const int j = lane & 15, qa = lane >> 4;
-  if (p.KS == 1) {
+  auto each_output = [&](auto f) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (t0 + r >= p.tiles) continue;
-      const TileRef tr = tile_ref(p.ms, t0 + r);
+      if constexpr (MODE == kFp4) {
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int m = 8 * tb + 2 * qa + tt;
-          if (m < p.M) store_y(tr, j, m, ys[r][tb][tt] * mul, p.y_f16);
-        }
+          for (int tt = 0; tt < 2; ++tt) f(r, 8 * tb + 2 * qa + tt, yacc[r][tb][2 * tt] + yacc[r][tb][2 * tt + 1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f(r, 4 * qa + e, yacc[r][0][e]);
+      }
     }
+  };
+  if (p.KS == 1) {
+    each_output([&](int r, int m, float v) {
+      if (t0 + r < p.tiles && m < p.M) store_y(tile_ref(p.ms, t0 + r), j, m, v * mul, p.y_f16);
+    });
     return;
   }
 
   // K split across workgroups: publish this range's partial sums (at launch
   // rows, every row of a tile included).
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int n = 16 * (t0 + r) + j;
-    if (t0 + r >= p.tiles) continue;
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int m = 8 * tb + 2 * qa + tt;
-        if (m >= p.M) continue;
-        __hip_atomic_store(p.part + ((int64_t)ks * p.M + m) * p.NV + n, ys[r][tb][tt], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-  }
+  each_output([&](int r, int m, float v) {
+    if (t0 + r < p.tiles && m < p.M)
+      __hip_atomic_store(p.part + ((int64_t)ks * p.M + m) * p.NV + 16 * (t0 + r) + j, v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  });
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
   if (threadIdx.x == 0)
@@ -274,9 +318,9 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
 
 // Largest pass (groups, a multiple of 4) whose x fits in one item per thread
 // and whose two buffers fit in 64 KB of LDS.
-inline int pass_groups(int MP, int G) {
+inline int pass_groups(int MP, int G, int MODE) {
   int gp = 4;
-  while (gp + 4 <= 128 && MP * (gp + 4) * 4 <= kSThreads && 2 * split_buf_bytes(MP, gp + 4) <= 64 * 1024) gp += 4;
+  while (gp + 4 <= 128 && MP * (gp + 4) * 4 <= kSThreads && 2 * split_buf_bytes(MP, gp + 4, MODE) <= 66 * 1024) gp += 4;
   const int g4 = (G + 3) / 4 * 4;
   return gp < g4 ? gp : g4;
 }
@@ -305,7 +349,7 @@ struct SplitPlan {
 
 // Per-wave work of the busiest workgroup slot, in (tile, group) units, with
 // charges for staging x, for workgroup start-up and for the partial sums.
-template <int FMT, int MP, int R>
+template <int FMT, int MP, int R, int MODE>
 void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
   SplitParams p{};
   p.ms = mat_set(a);
@@ -315,10 +359,10 @@ void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
   p.NV = 16 * p.tiles;
   p.y_f16 = a.y_f16;
   p.row_blocks = (p.tiles + 8 * R - 1) / (8 * R);
-  p.GP = pass_groups(MP, p.G);
-  p.buf_bytes = split_buf_bytes(MP, p.GP);
+  p.GP = pass_groups(MP, p.G, MODE);
+  p.buf_bytes = split_buf_bytes(MP, p.GP, MODE);
   const int lds = 2 * p.buf_bytes;
-  const void *kern = reinterpret_cast<const void *>(&gemv_split_kernel<FMT, MP, R>);
+  const void *kern = reinterpret_cast<const void *>(&gemv_split_kernel<FMT, MP, R, MODE>);
   const int slots = num_cus() * resident_blocks(kern, kSThreads, lds);
   for (int GK = 4; GK < p.G + 4; GK += 4) {
     const int gk = GK < p.G ? GK : p.G;
@@ -330,7 +374,7 @@ void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
     const int64_t wgs = (int64_t)p.row_blocks * KS;
     const double rounds = double((wgs + slots - 1) / slots);
     const double stage = 8.0 * ((gk + p.GP - 1) / p.GP);        // per pass: convert + barrier
-    const double work = double(R) * gk * (MP > 8 ? 2.0 : 1.0);   // MFMA sets per wave
+    const double work = double(R) * gk * (MODE == kFp4 ? (MP > 8 ? 2.0 : 1.0) : 2.0);  // MFMA sets per wave
     const double reduce = KS > 1 ? 6.0 + 0.02 * KS * MP * R : 0.0;
     const double cost = rounds * (work + stage + 12.0 + reduce);
     if (cost < best.cost) {
@@ -345,12 +389,12 @@ void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
   }
 }
 
-template <int FMT, int MP>
+template <int FMT, int MP, int MODE>
 hipError_t launch_split_mp(const LaunchArgs &a) {
   SplitPlan b1, b2, b4;
-  plan_split<FMT, MP, 1>(a, a.ws_bytes, b1);
-  plan_split<FMT, MP, 2>(a, a.ws_bytes, b2);
-  plan_split<FMT, MP, 4>(a, a.ws_bytes, b4);
+  plan_split<FMT, MP, 1, MODE>(a, a.ws_bytes, b1);
+  plan_split<FMT, MP, 2, MODE>(a, a.ws_bytes, b2);
+  plan_split<FMT, MP, 4, MODE>(a, a.ws_bytes, b4);
   int R = 1;
   SplitPlan *b = &b1;
   if (b2.cost < b->cost) { b = &b2; R = 2; }
@@ -359,19 +403,29 @@ hipError_t launch_split_mp(const LaunchArgs &a) {
     b->p.count = static_cast<unsigned *>(a.ws);
     b->p.part = reinterpret_cast<float *>(static_cast<char *>(a.ws) + kPartOffset);
   }
-  if (R == 1) hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
-  else if (R == 2) hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
-  else hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
+  if (R == 1)
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
+  else if (R == 2)
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2, MODE>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
+  else
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4, MODE>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
   return hipGetLastError();
 }
 
-template <int FMT>
+// Exact modes stage 1, 4 or 16 token slots (cells per token slot).
+template <int FMT, int MODE>
 hipError_t launch_split_fmt(const LaunchArgs &a) {
-  if (a.M <= 1) return launch_split_mp<FMT, 1>(a);
-  if (a.M <= 2) return launch_split_mp<FMT, 2>(a);
-  if (a.M <= 4) return launch_split_mp<FMT, 4>(a);
-  if (a.M <= 8) return launch_split_mp<FMT, 8>(a);
-  return launch_split_mp<FMT, 16>(a);
+  if constexpr (MODE == kFp4) {
+    if (a.M <= 1) return launch_split_mp<FMT, 1, MODE>(a);
+    if (a.M <= 2) return launch_split_mp<FMT, 2, MODE>(a);
+    if (a.M <= 4) return launch_split_mp<FMT, 4, MODE>(a);
+    if (a.M <= 8) return launch_split_mp<FMT, 8, MODE>(a);
+    return launch_split_mp<FMT, 16, MODE>(a);
+  } else {
+    if (a.M <= 1) return launch_split_mp<FMT, 1, MODE>(a);
+    if (a.M <= 4) return launch_split_mp<FMT, 4, MODE>(a);
+    return launch_split_mp<FMT, 16, MODE>(a);
+  }
 }
 
 }  // namespace
@@ -389,7 +443,10 @@ int64_t gemv_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemv_split(const LaunchArgs &a) {
-  return a.fmt == 1 ? launch_split_fmt<1>(a) : launch_split_fmt<2>(a);
+  // fp8 pieces of x only with binary weights (their error bound needs every
+  // product of a block to count): tq2 and fp16 x take exact operands.
+  if (a.fmt == 1) return a.x_bf16 ? launch_split_fmt<1, kFp4>(a) : launch_split_fmt<1, kF16>(a);
+  return a.x_bf16 ? launch_split_fmt<2, kBf16>(a) : launch_split_fmt<2, kF16>(a);
 }
 
 }  // namespace lowbit
