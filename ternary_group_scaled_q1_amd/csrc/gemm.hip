@@ -8,10 +8,11 @@
 // in fp32: each group accumulates into a fresh tile that is then added as
 // s * tile (products exact, the scale is never rounded to bf16).
 //
-// Workgroup = 2 x NWN waves = 128 x (64 NWN) outputs (NWN = 4 for q1 and
-// tq2, so two waves share each SIMD and one's MFMAs overlap the other's
-// decode and waits; 2 for tq5); wave (wm, wn) owns 64 x 64 = 4 x 4 MFMA
-// tiles, so every decoded weight operand feeds 4 MFMAs.
+// Workgroup = 8 waves (two per SIMD, so one's MFMAs overlap the other's
+// decode and waits) in 2 rows along M x 4 along N; wave (wm, wn) owns 64 rows
+// x NB n-blocks of 16 columns = 4 x NB MFMA tiles (NB = 4 for q1 / tq2,
+// 128 x 256 tiles; 2 for tq5, 128 x 128 tiles), so every decoded weight
+// operand feeds 4 MFMAs.
 //
 // Activations: a ring of three LDS stages, each one group of the tile (128
 // tokens x 128 k, 32 KB) in the order the MFMA reads it: 1 KB blocks, one
@@ -47,17 +48,21 @@ namespace {
 
 constexpr int kBM = 128;
 constexpr int kStages = 3;
-// Waves side by side along N (two rows of them along M): 4 for q1 / tq2
-// (128 x 256 tiles, 8 waves, two per SIMD), 2 for tq5 (128 x 128, whose
-// staged segment bytes grow with the tile width).
+// 8 waves, 4 side by side along N and two rows of them along M (two waves
+// per SIMD).  A wave owns 64 rows x NB n-blocks of 16 columns: NB = 4 for
+// q1 / tq2 (128 x 256 tiles), 2 for tq5 (128 x 128 tiles: its staged
+// segment bytes grow with the tile width, and its decoded segment words
+// with the wave's width).
 template <int FMT>
-constexpr int nwn() { return FMT == 3 ? 2 : 4; }
+constexpr int nwn() { return 4; }
+template <int FMT>
+constexpr int nbw() { return FMT == 3 ? 2 : 4; }
 template <int FMT>
 constexpr int threads_of() { return 128 * nwn<FMT>(); }
 template <int FMT>
-constexpr int bn_of() { return 64 * nwn<FMT>(); }
+constexpr int bn_of() { return 16 * nbw<FMT>() * nwn<FMT>(); }
 template <int FMT>
-constexpr int piece_floats() { return 2 * nwn<FMT>() * 64 * 64; }  // one tile, lane order
+constexpr int piece_floats() { return 2 * nwn<FMT>() * 64 * 16 * nbw<FMT>(); }  // one tile, lane order
 constexpr int kStageBytes = kBM * 128 * 2;  // one group of the activation tile
 constexpr int64_t kCounterBytes = 64 << 10;  // arrival counters (up to 16384 tiles)
 constexpr int kRawBytes = 16 << 10;          // tq5 raw segment bytes per stage
@@ -97,8 +102,8 @@ __device__ __forceinline__ TileCols tile_cols(const GemmParams &p, int nt) {
   const int wn = uni(threadIdx.x >> 6) % nwn<FMT>();
   TileCols c;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int n = nt * bn_of<FMT>() + wn * 64 + 16 * nb;
+  for (int nb = 0; nb < nbw<FMT>(); ++nb) {
+    const int n = nt * bn_of<FMT>() + wn * 16 * nbw<FMT>() + 16 * nb;
     c.tileT[nb] = uni(n / 16);
     c.RT[nb] = uni(n < p.N ? min(16, p.N - n) : 0);
   }
@@ -115,7 +120,7 @@ struct ColBlock {
 
 template <int FMT>
 __device__ __forceinline__ ColBlock col_block(const GemmParams &p, int nt, int wn, int nb) {
-  const int n = nt * bn_of<FMT>() + wn * 64 + 16 * nb;
+  const int n = nt * bn_of<FMT>() + wn * 16 * nbw<FMT>() + 16 * nb;
   ColBlock c;
   c.R = n < p.N ? min(16, p.N - n) : 0;
   c.T = c.R > 0 ? n / 16 : 0;
@@ -128,15 +133,15 @@ __device__ __forceinline__ ColBlock col_block(const GemmParams &p, int nt, int w
 // one word per lane for q1, two for tq2 -- and their FP16 scales at
 // [wave][lane] x 4 bytes (a 2-byte global-to-LDS load writes its lane's
 // value zero-extended at 4 * lane; lane l carries the scale of row l % 16 of
-// n-block 2 wm + (l / 16) % 2).  Wave (wm, wn) loads
-// n-blocks 2wm, 2wm + 1 of its column half.  Weight rows past N (ragged last
+// n-block H wm + (l / 16) % H, H = NB / 2).  Wave (wm, wn) loads n-blocks
+// H wm .. H wm + H - 1 of its column block.  Weight rows past N (ragged last
 // tile, n-blocks past N) read a clamped, in-bounds address and keep whatever
 // they load: they only feed output columns that are never stored.
 template <int FMT>
 constexpr int w_words() { return FMT == 2 ? 2 : (FMT == 1 ? 1 : 0); }
 
 template <int FMT>
-constexpr int w_scale_off() { return nwn<FMT>() * 4 * w_words<FMT>() * 256; }
+constexpr int w_scale_off() { return nwn<FMT>() * nbw<FMT>() * w_words<FMT>() * 256; }
 
 template <int FMT>
 constexpr int w_raw_off() { return w_scale_off<FMT>() + 2 * nwn<FMT>() * 256; }
@@ -148,51 +153,54 @@ constexpr int w_stage_bytes() {
 
 template <int FMT>
 __device__ __forceinline__ float w_scale(const char *wst, int nb) {
+  constexpr int H = nbw<FMT>() / 2;  // n-blocks whose scales one wave stages
   const int wn = (threadIdx.x >> 6) % nwn<FMT>(), j = threadIdx.x & 15;
-  const int wave = (nb >> 1) * nwn<FMT>() + wn;
+  const int wave = (nb / H) * nwn<FMT>() + wn;
   const uint16_t h =
-      *reinterpret_cast<const uint16_t *>(wst + w_scale_off<FMT>() + wave * 256 + ((nb & 1) * 16 + j) * 4);
+      *reinterpret_cast<const uint16_t *>(wst + w_scale_off<FMT>() + wave * 256 + ((nb % H) * 16 + j) * 4);
   return half_to_float(h);
 }
 
 template <int FMT>
 __device__ __forceinline__ uint32_t w_word(const char *wst, int nb, int h) {
   const int wn = (threadIdx.x >> 6) % nwn<FMT>(), lane = threadIdx.x & 63;
-  return *reinterpret_cast<const uint32_t *>(wst + ((wn * 4 + nb) * w_words<FMT>() + h) * 256 + lane * 4);
+  return *reinterpret_cast<const uint32_t *>(wst + ((wn * nbw<FMT>() + nb) * w_words<FMT>() + h) * 256 + lane * 4);
 }
 
 // 4 k-steps of MFMAs for one group from stage st into fresh tiles, then
 // acc += s * tile.  Bop(u, nb) returns the B operand (16 weight rows x 32 k)
 // of n-block nb for k-step u.
 template <int FMT, bool BF, class Bop>
-__device__ __forceinline__ void group_mma(const char *st, const float (&sc)[4], f4_t (&acc)[4][4], Bop bop) {
+__device__ __forceinline__ void group_mma(const char *st, const float (&sc)[nbw<FMT>()], f4_t (&acc)[4][nbw<FMT>()],
+                                          Bop bop) {
+  constexpr int NB = nbw<FMT>();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / nwn<FMT>();
-  f4_t cg[4][4];
+  f4_t cg[4][NB];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    u4_t A[4], B[4];
+    u4_t A[4], B[NB];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
       A[mb] = *reinterpret_cast<const u4_t *>(st + ((wm * 4 + mb) * 4 + u) * 1024 + lane * 16);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) B[nb] = bop(u, nb);
+    for (int nb = 0; nb < NB; ++nb) B[nb] = bop(u, nb);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
         cg[mb][nb] = u == 0 ? mfma16x16x32_zero<BF>(A[mb], B[nb]) : mfma16x16x32<BF>(A[mb], B[nb], cg[mb][nb]);
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[mb][nb][e] = fmaf(sc[nb], cg[mb][nb][e], acc[mb][nb][e]);
 }
 
 template <int FMT>
-__device__ __forceinline__ void store_tile(const GemmParams &p, int mt, int nt, const f4_t (&acc)[4][4]) {
+__device__ __forceinline__ void store_tile(const GemmParams &p, int mt, int nt, const f4_t (&acc)[4][nbw<FMT>()]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / nwn<FMT>(), wn = wave % nwn<FMT>();
   const int j = lane & 15, q = lane >> 4;
@@ -200,8 +208,8 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int mt, int nt, 
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int n = nt * bn_of<FMT>() + wn * 64 + 16 * nb + j;
+    for (int nb = 0; nb < nbw<FMT>(); ++nb) {
+      const int n = nt * bn_of<FMT>() + wn * 16 * nbw<FMT>() + 16 * nb + j;
       if (n >= p.N) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -214,21 +222,20 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int mt, int nt, 
     }
 }
 
-// tq5: the raw bytes of the full segment holding each item, staged per item
-// in the weight stage (after the scales): layout [wn][nb][half][lane] x 16
-// bytes (32 bytes per lane and n-block, 16 KB); wave (wm, wn) fills n-blocks
-// 2wm, 2wm + 1.  Items of the tail segment (and matrices without a full
-// segment) load a harmless in-bounds block of x instead.
+// tq5: the raw bytes of the full segment holding each item, staged on the
+// items that decode them, in the weight stage (after the scales): layout
+// [wn][nb][half][lane] x 16 bytes (32 bytes per lane and n-block, 16 KB);
+// wave (wm, wn) fills n-block wm of its column block.
 
 // (sign, non-zero) pairs of the segment for the wave's 4 n-blocks, from the
 // staged raw bytes through the 243-entry table.
-__device__ __forceinline__ void tq5_decode(const char *slot, const uint16_t *lut, uint32_t (&d5)[4][16]) {
+__device__ __forceinline__ void tq5_decode(const char *slot, const uint16_t *lut, uint32_t (&d5)[nbw<3>()][16]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wn = wave % nwn<3>();
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const u4_t a = *reinterpret_cast<const u4_t *>(slot + ((wn * 4 + nb) * 2 + 0) * 1024 + lane * 16);
-    const u4_t b = *reinterpret_cast<const u4_t *>(slot + ((wn * 4 + nb) * 2 + 1) * 1024 + lane * 16);
+  for (int nb = 0; nb < nbw<3>(); ++nb) {
+    const u4_t a = *reinterpret_cast<const u4_t *>(slot + ((wn * nbw<3>() + nb) * 2 + 0) * 1024 + lane * 16);
+    const u4_t b = *reinterpret_cast<const u4_t *>(slot + ((wn * nbw<3>() + nb) * 2 + 1) * 1024 + lane * 16);
     const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -250,7 +257,7 @@ template <int FMT>
 struct Feed {
   int tile, g, mt, nt;
   const uint16_t *xrow[2];  // activation rows of the wave's row blocks (+ 8q), see x_blocks
-  const uint8_t *wb[2];     // n-blocks 2wm, 2wm+1: tile block start (tq5: + lane part)
+  const uint8_t *wb[2];     // n-blocks H wm + i the wave loads: tile block start (tq5: + lane part)
   uint32_t wl[2];           // q1: 4 woff, tq2: 8 woff (woff = lane word index q RR + j)
   int RR[2];                // rows of the block (>= 1)
   const uint8_t *scrow;     // this lane's scale row
@@ -272,8 +279,8 @@ __device__ __forceinline__ void feed_tile(const GemmParams &p, Feed<FMT> &f) {
   for (int h = 0; h < XB / 4; ++h)
     f.xrow[h] = p.X + (int64_t)min(f.mt * kBM + 16 * (wave * (XB / 4) + h) + j, p.M - 1) * p.K + 8 * q;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const ColBlock cb = col_block<FMT>(p, f.nt, wn, 2 * wm + i);
+  for (int i = 0; i < nbw<FMT>() / 2; ++i) {
+    const ColBlock cb = col_block<FMT>(p, f.nt, wn, (nbw<FMT>() / 2) * wm + i);
     const uint32_t woff = uint32_t(q * cb.RR + min(j, cb.RR - 1));
     f.RR[i] = cb.RR;
     if constexpr (FMT == 3) {
@@ -290,7 +297,7 @@ __device__ __forceinline__ void feed_tile(const GemmParams &p, Feed<FMT> &f) {
       f.wl[i] = 8 * woff;
     }
   }
-  const ColBlock cs = col_block<FMT>(p, f.nt, wn, 2 * wm + ((lane >> 4) & 1));
+  const ColBlock cs = col_block<FMT>(p, f.nt, wn, (nbw<FMT>() / 2) * wm + ((lane >> 4) % (nbw<FMT>() / 2)));
   f.scrow = p.Sc + (int64_t)(16 * cs.T + min(j, cs.RR - 1)) * p.G * 2;
 }
 
@@ -322,16 +329,17 @@ __device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> 
     const int hh = gc >> 1;
     const int Gh = min(2, Gc - 2 * hh);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int nb = 2 * wm + i;
+    for (int i = 0; i < nbw<FMT>() / 2; ++i) {
+      const int nb = (nbw<FMT>() / 2) * wm + i;
       if constexpr (FMT == 1) {
         const uint8_t *a = f.wb[i] + (f.RR[i] * 64 * c + 4 * gc) + f.wl[i] * uint32_t(Gc);
-        __builtin_amdgcn_global_load_lds((const void *)a, (lds_void *)(wst + (wn * 4 + nb) * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)a, (lds_void *)(wst + (wn * nbw<FMT>() + nb) * 256), 4, 0, 0);
       } else {
         const uint8_t *a = f.wb[i] + (f.RR[i] * (128 * c + 64 * hh) + 8 * (gc - 2 * hh)) + f.wl[i] * uint32_t(Gh);
-        __builtin_amdgcn_global_load_lds((const void *)a, (lds_void *)(wst + ((wn * 4 + nb) * 2) * 256), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(a + 4), (lds_void *)(wst + ((wn * 4 + nb) * 2 + 1) * 256), 4,
+        __builtin_amdgcn_global_load_lds((const void *)a, (lds_void *)(wst + ((wn * nbw<FMT>() + nb) * 2) * 256), 4,
                                          0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(a + 4),
+                                         (lds_void *)(wst + ((wn * nbw<FMT>() + nb) * 2 + 1) * 256), 4, 0, 0);
       }
     }
   }
@@ -342,13 +350,13 @@ __device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> 
     if (raw && seg < p.s_full) {  // wave-uniform
       char *slot = wst + w_raw_off<FMT>();
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int nb = 2 * wm + i;
+      for (int i = 0; i < nbw<FMT>() / 2; ++i) {
+        const int nb = (nbw<FMT>() / 2) * wm + i;
         const uint8_t *sb = f.wb[i] + (int64_t)f.RR[i] * 128 * seg;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           __builtin_amdgcn_global_load_lds((const void *)(sb + h * f.RR[i] * 64),
-                                           (lds_void *)(slot + ((wn * 4 + nb) * 2 + h) * 1024), 16, 0, 0);
+                                           (lds_void *)(slot + ((wn * nbw<FMT>() + nb) * 2 + h) * 1024), 16, 0, 0);
       }
     }
   }
@@ -406,14 +414,15 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
     wl1 = int((uint32_t(last_tile) * ug + ug - 1) / per);
   }
 
-  f4_t acc[4][4];
+  constexpr int NB = nbw<FMT>();
+  f4_t acc[4][NB];
   int cur_tile = first_tile, cur_g = g0;
   int cur_mt = first_tile % p.tiles_m, cur_nt = first_tile / p.tiles_m;
   int g_begin = cur_g;
   TileCols tc = tile_cols<FMT>(p, cur_nt);
 
   // tq5: decoded pairs of the current segment.
-  uint32_t d5[4][16];
+  uint32_t d5[NB][16];
   char *wring = xs + kStages * kStageBytes;  // weight stages (kStages x w_stage_bytes)
   constexpr int kW = w_stage_bytes<FMT>();
 
@@ -448,7 +457,7 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < NB; ++b) acc[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
       if constexpr (FMT == 3) tc = tile_cols<FMT>(p, nt);
       g_begin = g;
     }
@@ -466,13 +475,13 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
     if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
     const char *st = xs + slot * kStageBytes;
     const char *wst = wring + slot * kW;
-    float sc[4];
+    float sc[NB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) sc[nb] = w_scale<FMT>(wst, nb);
+    for (int nb = 0; nb < NB; ++nb) sc[nb] = w_scale<FMT>(wst, nb);
     if constexpr (FMT != 3) {
-      uint32_t wd[4][2];
+      uint32_t wd[NB][2];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int h = 0; h < w_words<FMT>(); ++h) wd[nb][h] = w_word<FMT>(wst, nb, h);
       group_mma<FMT, BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
@@ -530,10 +539,10 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          __hip_atomic_store(piece + ((wave * 16 + a * 4 + b) * 4 + e) * 64 + lane, acc[a][b][e], __ATOMIC_RELAXED,
+          __hip_atomic_store(piece + ((wave * 4 * NB + a * NB + b) * 4 + e) * 64 + lane, acc[a][b][e], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's piece stores have completed
     __syncthreads();
@@ -542,11 +551,11 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
                   unsigned(wl - wf);
     __syncthreads();
     if (!last_flag) return;
-    f4_t sum[4][4];
+    f4_t sum[4][NB];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) sum[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < NB; ++b) sum[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
     for (int w2 = wf; w2 <= wl; ++w2) {
       // Piece 0 of workgroup w2 belongs to the first tile of its range.
       const int wh = int(uint32_t(w2) * uint32_t(p.per) / uint32_t(G)) == tile ? 0 : 1;
@@ -554,10 +563,10 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sum[a][b][e] += __hip_atomic_load(pc + ((wave * 16 + a * 4 + b) * 4 + e) * 64 + lane, __ATOMIC_RELAXED,
+            sum[a][b][e] += __hip_atomic_load(pc + ((wave * 4 * NB + a * NB + b) * 4 + e) * 64 + lane, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
     }
     store_tile<FMT>(p, mt, nt, sum);
