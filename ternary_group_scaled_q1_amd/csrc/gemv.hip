@@ -524,7 +524,7 @@ hipError_t launch_fmt(const LaunchArgs &a) {
     }
     const bool split = ws_ok && a.M >= 2 && (a.K >= 8192 || (a.M >= 4 && a.N < 65536));
     if (split) return launch_gemv_split(a);
-    if (a.M <= 1) return launch_mt<FMT, BF, 1, true, 2, RB>(a);
+    if (a.M <= 1) return launch_mt<FMT, BF, 1, true, 1, 2>(a);
     if (a.M <= 2) return launch_mt<FMT, BF, 2, true, 2, RB>(a);
     if (a.M <= 4) return launch_mt<FMT, BF, 4, true, 2, RB>(a);
     return launch_mt<FMT, BF, 8, true, 2, RB>(a);
