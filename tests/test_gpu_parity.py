@@ -238,6 +238,20 @@ def test_workload_sweep_lm_head_q1():
 
 # ------------------------------------------------ bf16 x over a wide range ----
 @pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_bf16_x_wide_dynamic_range(fmt):
+    """The prefill path with bf16 activations spread over 2^-40 .. 2^8 inside
+    every 32-value block (exact operands: every element within the bound)."""
+    g = np.random.default_rng(310)
+    M, N, K = 140, 96, 1408
+    codes = _codes(g, fmt, N, K)
+    sc = synth.scales_absnormal(g, N, K // 128)
+    mag = np.exp2(g.uniform(-40, 8, size=(M, K)))
+    x = synth.f64_to_bf16_bits(mag * np.where(g.random((M, K)) < 0.5, -1.0, 1.0))
+    y = gu.run("gemm", fmt, gu.w_tensor(lb.pack(fmt, codes, sc)), x, "bf16", "f32", N, K)
+    gu.check(y, codes, sc, x, "bf16", f"gemm wide range {fmt}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [1, 2, 3, 8])
 def test_bf16_x_wide_dynamic_range(fmt, M):
     """bf16 activations whose magnitudes spread over 2^-40 .. 2^8 inside every
@@ -411,7 +425,7 @@ def test_gemv_multi_fused(fmt, xdt):
     t = gu.torch()
     g = np.random.default_rng(700)
     cases = [(1, [17, 300, 64], 1280), (3, [5120, 1024, 1024], 640), (16, [48, 0, 130], 2048),
-             (9, [16, 16, 16, 16], 17408), (2, [4100], 384)]
+             (9, [16, 16, 16, 16], 17408), (2, [4100], 384), (20, [33, 64], 1024)]
     for M, Ns, K in cases:
         print(f"multi {fmt} {xdt} M={M} Ns={Ns} K={K}", flush=True)
         mats = []
