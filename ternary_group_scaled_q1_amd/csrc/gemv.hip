@@ -229,17 +229,15 @@ template <int FMT, int MP, int R, int E>
 __device__ __forceinline__ void compute_fp4(const GemvParams &p, const char *lds, const Unit<FMT, R> &u, int c_local,
                                             float (&yacc)[R][4]) {
   const int lane = threadIdx.x & 63, qa = lane >> 4, r = lane & 15;
-  const bool arow = r < 2 * MP;
-  const int rr = arow ? r : 0;
+  // Lanes of A rows past 2 MP read row 0 again: an A row only feeds the same
+  // row of the product, and those rows are never stored.
+  const int rr = r < 2 * MP ? r : 0;
   const char *xa = lds + p.off_x + (c_local * 4 * 2 * MP + rr) * kRowBytes + qa * 32;
   const uint8_t *sa = reinterpret_cast<const uint8_t *>(lds + p.off_corr) + (c_local * 4 * MP + (rr >> 1)) * 4 + qa;
-  const u4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    u4_t a0 = *reinterpret_cast<const u4_t *>(xa + g * 2 * MP * kRowBytes);
-    u4_t a1 = *reinterpret_cast<const u4_t *>(xa + g * 2 * MP * kRowBytes + 16);
-    a0 = arow ? a0 : z;
-    a1 = arow ? a1 : z;
+    const u4_t a0 = *reinterpret_cast<const u4_t *>(xa + g * 2 * MP * kRowBytes);
+    const u4_t a1 = *reinterpret_cast<const u4_t *>(xa + g * 2 * MP * kRowBytes + 16);
     const int sc = sa[g * MP * 4];
 #pragma unroll
     for (int r2 = 0; r2 < R; ++r2) {
@@ -279,21 +277,27 @@ struct Cursor {
   int it, st, kl;
 };
 
-__device__ __forceinline__ void advance(Cursor &c, int U, int n_stages) {
+// Returns true when the cursor moved to the next tile set.
+__device__ __forceinline__ bool advance(Cursor &c, int U, int n_stages) {
   if (++c.kl == U) {
     c.kl = 0;
     if (++c.st == n_stages) {
       c.st = 0;
       ++c.it;
+      return true;
     }
   }
+  return false;
 }
 
 // Each wave walks a flat sequence of units (tile set, chunk) with a ring of
 // D units in flight: the loads of unit i + D - 1 are issued before unit i is
 // computed, across chunk, stage and tile-set boundaries.
-// FP4 selects the fp8 x fp4 path (MT = token slots MP, at most 8).
-template <int FMT, bool BF, int MT, int R, int D, bool FP4>
+// FP4 selects the fp8 x fp4 path (MT = token slots MP, at most 8).  FULL:
+// every matrix has whole row tiles and K whole chunks; the loads then take
+// tile addresses resolved once per tile set and step a fixed stride per
+// chunk (the general path resolves the tile and its ragged shape per unit).
+template <int FMT, bool BF, int MT, int R, int D, bool FP4, bool FULL>
 __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
   // Accumulator elements that can hold a token (fp4: A rows, two per token).
   constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
@@ -328,15 +332,25 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
     return c.it * rows_total + my_row < p.tilesets && chunk(c) < p.chunks;
   };
 
+  // The load side: its cursor, the tile set it reads (FULL) and one unit's
+  // loads.  Units outside the sequence re-read chunk 0 of the current set.
+  Cursor ld = {0, 0, 0};
+  TileSet<R> lts;
+  if constexpr (FULL) resolve_tiles<FMT, R>(p, lts, uni(tile0(ld)));
+  auto load = [&](Unit<FMT, R> &u, bool in_seq) {
+    const bool v = in_seq && is_valid(ld);
+    if constexpr (FULL) load_full<FMT, R>(lts, u, uni(v ? chunk(ld) : 0));
+    else load_unit<FMT, R>(p, u, uni(tile0(ld)), uni(chunk(ld)), v);
+    if (advance(ld, U, p.n_stages)) {
+      if constexpr (FULL) resolve_tiles<FMT, R>(p, lts, uni(tile0(ld)));
+    }
+  };
+
   // First D - 1 units' loads go out before x is staged.
   float yacc[R][4];
   Unit<FMT, R> ring[D];
-  Cursor ld = {0, 0, 0};
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d) {
-    load_unit<FMT, R>(p, ring[d], uni(tile0(ld)), uni(chunk(ld)), d < total && is_valid(ld));
-    advance(ld, U, p.n_stages);
-  }
+  for (int d = 0; d < D - 1; ++d) load(ring[d], d < total);
   if (!restage) {
     if constexpr (FP4) stage_fp4<FMT, MT>(p, lds, 0, p.chunks);
     else stage_x<FMT, BF, MTS>(p, lds, 0, p.chunks);
@@ -348,9 +362,13 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int i = i0 + d;
-      if (i >= total) break;
-      load_unit<FMT, R>(p, ring[(d + D - 1) % D], uni(tile0(ld)), uni(chunk(ld)), i + D - 1 < total && is_valid(ld));
-      advance(ld, U, p.n_stages);
+      // Every step issues its loads and no step leaves the loop early: each
+      // path through the body then issues the same loads, so the wait before
+      // a unit's MFMAs covers that unit only (wait counts are in issue order,
+      // and the compiler keeps the fewest loads in flight that any path to
+      // the wait leaves).
+      load(ring[(d + D - 1) % D], i + D - 1 < total);
+      if (i >= total) continue;
 
       const int t0 = uni(tile0(cu));
       const int k_first = cu.st == 0 && cu.kl == 0;
@@ -414,7 +432,7 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
 
 // Host-side choice of (R, S): the smallest per-wave work (the makespan:
 // tile sets per wave-row x R x chunks per wave), then fewer barriers.
-template <int FMT, bool BF, int MT, int R, int D, bool FP4>
+template <int FMT, bool BF, int MT, int R, int D, bool FP4, bool FULL>
 double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) {
   constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
   p = GemvParams{};
@@ -427,7 +445,7 @@ double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) 
   p.tilesets = (p.tiles + R - 1) / R;
   p.y_f16 = a.y_f16;
   const int cus = num_cus();
-  const void *kern = reinterpret_cast<const void *>(&gemv_kernel<FMT, BF, MT, R, D, FP4>);
+  const void *kern = reinterpret_cast<const void *>(&gemv_kernel<FMT, BF, MT, R, D, FP4, FULL>);
   auto map = [&](int S, int SC) { return FP4 ? lds_map_fp4(MT, S, SC, R, E) : lds_map(MT, S, SC, R, E); };
   // x bytes a stage of SC chunks occupies.
   auto xbytes = [&](int SC) { return FP4 ? SC * 4 * (2 * MT * kRowBytes + 4 * MT) : MT * SC * 1024; };
@@ -474,8 +492,8 @@ double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) 
   return best * (R == 1 ? 1.1 : 1.0);
 }
 
-template <int FMT, bool BF, int MT, bool FP4, int RA, int RB>
-hipError_t launch_mt(const LaunchArgs &a) {
+template <int FMT, bool BF, int MT, bool FP4, int RA, int RB, bool FULL>
+hipError_t launch_mt_full(const LaunchArgs &a) {
   GemvParams p1, p2;
   int g1, g2, l1, l2;
   // Ring depth: three units in flight for q1 (1 KB per tile each), two for
@@ -483,13 +501,27 @@ hipError_t launch_mt(const LaunchArgs &a) {
   // SIMD fit in registers.
   constexpr int DA = (FMT == 1 && RA < 4) ? 3 : 2;
   constexpr int DB = (FMT == 1 && RB < 4) ? 3 : 2;
-  const double c1 = make_plan<FMT, BF, MT, RA, DA, FP4>(a, p1, g1, l1);
-  const double c2 = make_plan<FMT, BF, MT, RB, DB, FP4>(a, p2, g2, l2);
+  const double c1 = make_plan<FMT, BF, MT, RA, DA, FP4, FULL>(a, p1, g1, l1);
+  const double c2 = make_plan<FMT, BF, MT, RB, DB, FP4, FULL>(a, p2, g2, l2);
   if (c1 < c2)
-    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, RA, DA, FP4>), dim3(g1), dim3(kThreads), l1, a.stream, p1);
+    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, RA, DA, FP4, FULL>), dim3(g1), dim3(kThreads), l1, a.stream, p1);
   else
-    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, RB, DB, FP4>), dim3(g2), dim3(kThreads), l2, a.stream, p2);
+    hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, RB, DB, FP4, FULL>), dim3(g2), dim3(kThreads), l2, a.stream, p2);
   return hipGetLastError();
+}
+
+// Every matrix of the launch has whole row tiles and K whole chunks.
+inline bool full_units(const LaunchArgs &a) {
+  if (a.K % 512 != 0) return false;
+  for (int i = 0; i < a.nmat; ++i)
+    if (a.Ns[i] % 16 != 0) return false;
+  return true;
+}
+
+template <int FMT, bool BF, int MT, bool FP4, int RA, int RB>
+hipError_t launch_mt(const LaunchArgs &a) {
+  return full_units(a) ? launch_mt_full<FMT, BF, MT, FP4, RA, RB, true>(a)
+                       : launch_mt_full<FMT, BF, MT, FP4, RA, RB, false>(a);
 }
 
 // Path choice, from timings of the decode shapes on MI355X.

@@ -48,13 +48,18 @@ struct TileRef {
 // Each field read passes through readfirstlane before the selects: a select
 // between two fields read straight from the parameter block would be folded
 // into one load at a computed offset, which forces a copy of the whole block
-// into scratch memory.
+// into scratch memory.  The rebuilt address is made a global-memory pointer
+// first and only then a generic one: from a plain integer the compiler could
+// not tell global memory from LDS and would emit flat loads, whose waits
+// also cover every LDS access (each wait then drains all loads in flight).
 template <class T>
 __device__ __forceinline__ T *uni_ptr(T *ptr) {
   const uint64_t v = reinterpret_cast<uint64_t>(ptr);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
-  return reinterpret_cast<T *>((uint64_t(hi) << 32) | lo);
+  using GT = __attribute__((address_space(1))) T;
+  GT *g = (GT *)((uint64_t(hi) << 32) | lo);
+  return (T *)g;
 }
 
 __device__ __forceinline__ TileRef tile_ref(const MatSet &m, int vt) {
@@ -100,25 +105,23 @@ struct Unit {
 // Loads are issued without per-lane branches (ragged tiles clamp their
 // addresses and zero the values afterwards): a divergent branch around a
 // load makes the compiler wait for every outstanding load at the join, which
-// would drain the prefetch ring.  P provides ms (the matrices), G and tiles
-// (tiles of the launch).
+// would drain the prefetch ring.  Units that are not valid, and tiles past
+// the launch, re-read a valid unit instead of zeroing the registers: their
+// values are never used (no MFMA for invalid units, no store past the last
+// tile), and the registers of a unit in flight are then written by its own
+// loads only.  P provides ms (the matrices), G and tiles (tiles of the
+// launch).
 template <int FMT, int R, class P>
 __device__ __forceinline__ void load_unit(const P &p, Unit<FMT, R> &u, int t0, int c, bool valid) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, q = lane >> 4;
-  constexpr int WPU = Unit<FMT, R>::WPU;
   const int64_t unit = FMT == 1 ? 16 : 32;
+  c = valid ? c : 0;
+  t0 = valid ? t0 : 0;
   const int Gc = uni(min(4, p.G - 4 * c));
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int t = uni(t0 + r);
-    if (!valid || t >= p.tiles) {  // wave-uniform
-#pragma unroll
-      for (int i = 0; i < WPU; ++i) u.w[r][i] = 0;
-      u.s[r][0] = u.s[r][1] = 0;
-      continue;
-    }
-    const TileRef tr = tile_ref(p.ms, t);
+    const TileRef tr = tile_ref(p.ms, uni(min(t0 + r, p.tiles - 1)));
     const int RT = uni(min(16, tr.N - 16 * tr.t));
     const uint8_t *blk = tr.W + 16 * (int64_t)tr.t * p.G * unit + (int64_t)RT * 4 * c * unit;
     if (RT == 16 && Gc == 4 && (p.G & 3) == 0) {  // wave-uniform fast path
@@ -156,6 +159,49 @@ __device__ __forceinline__ void load_unit(const P &p, Unit<FMT, R> &u, int t0, i
       u.s[r][0] = h[0] | (h[1] << 16);
       u.s[r][1] = h[2] | (h[3] << 16);
     }
+  }
+}
+
+// Addresses of the R row tiles of one tile set, resolved once per set rather
+// than once per unit: the (uniform) start of each tile's packed block and
+// each lane's row of scales.  Tiles past the launch resolve to the last
+// tile; their sums are never stored.
+template <int R>
+struct TileSet {
+  const uint8_t *w[R];
+  const uint16_t *s[R];
+};
+
+template <int FMT, int R, class P>
+__device__ __forceinline__ void resolve_tiles(const P &p, TileSet<R> &ts, int t0) {
+  const int j = threadIdx.x & 15;
+  constexpr int64_t unit = FMT == 1 ? 16 : 32;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const TileRef tr = tile_ref(p.ms, uni(min(t0 + r, p.tiles - 1)));
+    ts.w[r] = tr.W + 16 * (int64_t)tr.t * p.G * unit;
+    ts.s[r] = tr.Sc + (int64_t)(16 * tr.t + j) * p.G;
+  }
+}
+
+// Unit (tile set, chunk c) when every tile has 16 rows and every chunk 4
+// groups: one 16-byte load per lane and 1 KB (tq2: two, 2 KB) per tile, at a
+// fixed stride per chunk, plus the lane's 4 scales.
+template <int FMT, int R>
+__device__ __forceinline__ void load_full(const TileSet<R> &ts, Unit<FMT, R> &u, int c) {
+  const int lane = threadIdx.x & 63;
+  constexpr int64_t cb = FMT == 1 ? 1024 : 2048;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const u4_t *wp = reinterpret_cast<const u4_t *>(ts.w[r] + c * cb) + lane;
+    const u4_t v0 = __builtin_nontemporal_load(wp);
+    u.w[r][0] = v0.x; u.w[r][1] = v0.y; u.w[r][2] = v0.z; u.w[r][3] = v0.w;
+    if constexpr (FMT == 2) {
+      const u4_t v1 = __builtin_nontemporal_load(wp + 64);
+      u.w[r][4] = v1.x; u.w[r][5] = v1.y; u.w[r][6] = v1.z; u.w[r][7] = v1.w;
+    }
+    const u2_t sv = *reinterpret_cast<const u2_t *>(ts.s[r] + 4 * c);
+    u.s[r][0] = sv.x; u.s[r][1] = sv.y;
   }
 }
 
