@@ -96,42 +96,97 @@ inline LdsMap lds_map_fp4(int MP, int S, int SC, int R, int E) {
   return m;
 }
 
-// Stage chunks [c0, c0 + nc) of x for the fp8 x fp4 path: one thread per
-// (token slot m, group, lane quarter q) splits that quarter's 32 values
-// (split_x_quarter) into A rows 2m (hi) and 2m + 1 (lo) of the group and
-// its E8M0 scale byte.  The quarter's values sit at hardware k 32q + n; the
-// A operand holds k < 64 in bytes 0..15 and k >= 64 in bytes 16..31 of lane
-// quarter (k % 64) / 16, so nibbles 0..15 go to lane quarter 2(q % 2) and
-// 16..31 to 2(q % 2) + 1.  Tokens m >= M and groups past K stage as zeros.
+// x staging runs in two steps, so that the loads of each thread's first
+// item go out before the weight prefetch: XFirst holds that item as loaded,
+// and the staging pass converts and writes it, then loads and writes any
+// further items one by one.  A wait for x counts only the loads issued
+// before it, so the weight loads stay in flight while x is converted.
+template <bool FP4>
+struct XFirst {
+  static constexpr int kCells = FP4 ? 1 : 4;  // exact operands: up to 4 passes' cells
+  u4_t v[FP4 ? 4 : kCells];
+};
+
+// fp8 x fp4 item it: token slot m, group gl of the pass, lane quarter q.
+// Items past the pass (m >= MP) and tokens past M read x[0] and stage zeros.
+template <int MP>
+__device__ __forceinline__ const uint16_t *fp4_item(const GemvParams &p, int it, int c0, int nc, bool &in) {
+  const int q = it & 3, rest = it >> 2;
+  const int gl = rest % (4 * nc), m = rest / (4 * nc);
+  in = m < p.M && 4 * c0 + gl < p.G;
+  return p.X + (in ? (int64_t)m * p.K + 128 * (4 * c0 + gl) + 8 * q : 0);
+}
+
+template <int MP>
+__device__ __forceinline__ void fp4_item_load(const GemvParams &p, int it, int c0, int nc, u4_t (&raw)[4]) {
+  bool in;
+  const uint16_t *src = fp4_item<MP>(p, it, c0, nc, in);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const u4_t *>(src + 32 * u);
+}
+
+// Splits the item's 32 values (split_x_regs) into A rows 2m (hi) and 2m + 1
+// (lo) of its group and writes its E8M0 scale byte.  The quarter's values sit
+// at hardware k 32q + n; the A operand holds k < 64 in bytes 0..15 and
+// k >= 64 in bytes 16..31 of lane quarter (k % 64) / 16, so nibbles 0..15 go
+// to lane quarter 2(q % 2) and 16..31 to 2(q % 2) + 1.
 template <int FMT, int MP>
-__device__ void stage_fp4(const GemvParams &p, char *lds, int c0, int nc) {
-  const int g0 = 4 * c0;
+__device__ __forceinline__ void fp4_item_write(const GemvParams &p, char *lds, int it, int c0, int nc,
+                                               const u4_t (&raw)[4]) {
+  const int q = it & 3, rest = it >> 2;
+  const int gl = rest % (4 * nc), m = rest / (4 * nc);
+  bool in;
+  fp4_item<MP>(p, it, c0, nc, in);
+  const u4_t z = {0u, 0u, 0u, 0u};
+  u4_t x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) x[u] = in ? raw[u] : z;
+  XQuarter xq;
+  split_x_regs<FMT>(x, xq);
+  char *row = lds + p.off_x + (gl * 2 * MP + 2 * m) * kRowBytes;
+  const int qa = 2 * (q & 1), half = 16 * (q >> 1);
+  *reinterpret_cast<u4_t *>(row + qa * 32 + half) = xq.h0;
+  *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = xq.h1;
+  *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = xq.l0;
+  *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = xq.l1;
+  reinterpret_cast<uint8_t *>(lds + p.off_corr)[(gl * MP + m) * 4 + q] = xq.sb;
+}
+
+// Stage chunks [c0, c0 + nc) of x for the fp8 x fp4 path: one item per
+// (token slot, group, lane quarter); tokens m >= M and groups past K stage as
+// zeros.  PRE: the thread's first item was loaded into first.
+template <int FMT, int MP, bool PRE>
+__device__ void stage_fp4(const GemvParams &p, char *lds, int c0, int nc, const XFirst<true> &first) {
   const int items = MP * 4 * nc * 4;
-  for (int it = threadIdx.x; it < items; it += kThreads) {
-    const int q = it & 3, rest = it >> 2;
-    const int gl = rest % (4 * nc), m = rest / (4 * nc);
-    const bool in = m < p.M && g0 + gl < p.G;
-    const uint16_t *src = p.X + (in ? (int64_t)m * p.K + 128 * (g0 + gl) + 8 * q : 0);
-    XQuarter xq;
-    split_x_quarter<FMT>(src, in, xq);
-    char *row = lds + p.off_x + (gl * 2 * MP + 2 * m) * kRowBytes;
-    const int qa = 2 * (q & 1), half = 16 * (q >> 1);
-    *reinterpret_cast<u4_t *>(row + qa * 32 + half) = xq.h0;
-    *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = xq.h1;
-    *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = xq.l0;
-    *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = xq.l1;
-    reinterpret_cast<uint8_t *>(lds + p.off_corr)[(gl * MP + m) * 4 + q] = xq.sb;
+  int it = threadIdx.x;
+  if constexpr (PRE) {
+    if (it < items) fp4_item_write<FMT, MP>(p, lds, it, c0, nc, first.v);
+    it += kThreads;
   }
+  for (; it < items; it += kThreads) {
+    u4_t raw[4];
+    fp4_item_load<MP>(p, it, c0, nc, raw);
+    fp4_item_write<FMT, MP>(p, lds, it, c0, nc, raw);
+  }
+}
+
+// Cell idx of the exact-operand staging: token slot m, k-octet oct.
+template <int MTS>
+__device__ __forceinline__ const u4_t *x_cell(const GemvParams &p, int idx, int c0, int nc, bool &in) {
+  const int m = idx / (nc * 64), oct = idx - m * (nc * 64);
+  const int k = c0 * 512 + oct * 8;
+  in = idx < MTS * nc * 64 && k < p.K && m < p.M;
+  return reinterpret_cast<const u4_t *>(p.X + (in ? (int64_t)m * p.K + k : 0));
 }
 
 // Stage chunks [c0, c0 + nc) of x: cell (oct, m) holds x[m][k0 + 8 oct .. + 8] at
 // byte off_x + (oct * MTS + m) * 16 (zeros past K and for m >= M).  One thread
 // per (group, token slot) also sums the group's activations at k % 4 in {2, 3}:
 // the q1 operand feeds those weights as t + 1, so minus that sum is stored in
-// corr[group][token] and seeds the group's accumulator.
-template <int FMT, bool BF, int MTS>
-__device__ void stage_x(const GemvParams &p, char *lds, int c0, int nc) {
-  const int k0 = c0 * 512;
+// corr[group][token] and seeds the group's accumulator.  PRE: the thread's
+// first cell was loaded into first.
+template <int FMT, bool BF, int MTS, bool PRE>
+__device__ void stage_x(const GemvParams &p, char *lds, int c0, int nc, const XFirst<false> &first) {
   uint4 *xl = reinterpret_cast<uint4 *>(lds + p.off_x);
   float *corr = reinterpret_cast<float *>(lds + p.off_corr);
   // One thread per (token slot, k-octet); the 16 octets of a group sit in 16
@@ -140,11 +195,12 @@ __device__ void stage_x(const GemvParams &p, char *lds, int c0, int nc) {
   for (int base = 0; base < cells; base += kThreads) {
     const int idx = base + threadIdx.x;
     const int m = idx / (nc * 64), oct = idx - m * (nc * 64);
-    const int k = k0 + oct * 8;
     const bool live = idx < cells;
-    const bool in = live && k < p.K && m < p.M;
-    const u4_t *src = reinterpret_cast<const u4_t *>(p.X + (in ? (int64_t)m * p.K + k : 0));
-    u4_t v = *src;
+    bool in;
+    const u4_t *src = x_cell<MTS>(p, idx, c0, nc, in);
+    u4_t v;
+    if (PRE && base < XFirst<false>::kCells * kThreads) v = first.v[base / kThreads];
+    else v = *src;
     const u4_t z = {0u, 0u, 0u, 0u};
     v = in ? v : z;
     if (live) *reinterpret_cast<u4_t *>(xl + oct * MTS + m) = v;
@@ -346,14 +402,26 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
     }
   };
 
-  // First D - 1 units' loads go out before x is staged.
+  // x of the whole K (when it fits): the thread's first item is loaded, then
+  // the first D - 1 units' weights, then x is converted and staged.
   float yacc[R][4];
   Unit<FMT, R> ring[D];
+  XFirst<FP4> xf;
+  if (!restage) {
+    if constexpr (FP4) fp4_item_load<MT>(p, threadIdx.x, 0, p.chunks, xf.v);
+    else {
+#pragma unroll
+      for (int i = 0; i < XFirst<false>::kCells; ++i) {
+        bool in;
+        xf.v[i] = *x_cell<MTS>(p, threadIdx.x + i * kThreads, 0, p.chunks, in);
+      }
+    }
+  }
 #pragma unroll
   for (int d = 0; d < D - 1; ++d) load(ring[d], d < total);
   if (!restage) {
-    if constexpr (FP4) stage_fp4<FMT, MT>(p, lds, 0, p.chunks);
-    else stage_x<FMT, BF, MTS>(p, lds, 0, p.chunks);
+    if constexpr (FP4) stage_fp4<FMT, MT, true>(p, lds, 0, p.chunks, xf);
+    else stage_x<FMT, BF, MTS, true>(p, lds, 0, p.chunks, xf);
     __syncthreads();
   }
 
@@ -382,8 +450,8 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
       if (restage && cu.kl == 0) {
         __syncthreads();
         const int c0 = cu.st * p.SC;
-        if constexpr (FP4) stage_fp4<FMT, MT>(p, lds, c0, min(p.SC, p.chunks - c0));
-        else stage_x<FMT, BF, MTS>(p, lds, c0, min(p.SC, p.chunks - c0));
+        if constexpr (FP4) stage_fp4<FMT, MT, false>(p, lds, c0, min(p.SC, p.chunks - c0), xf);
+        else stage_x<FMT, BF, MTS, false>(p, lds, c0, min(p.SC, p.chunks - c0), xf);
         __syncthreads();
       }
       if (is_valid(cu)) {

@@ -303,15 +303,42 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
                 unsigned(p.KS - 1);
   __syncthreads();
   if (!last_flag) return;
-  // Last workgroup of the block: Y = sum over ranges in range order.
+  // Last workgroup of the block: Y = sum over ranges in range order.  The
+  // partials come from the device's coherence point, so a thread issues the
+  // loads of 4 ranges for each of 4 outputs before it adds any of them
+  // (addresses clamped, values past KS unused) instead of paying that latency
+  // once per range.
   const int n0 = rb * 8 * R * 16;
   const int rows = min(8 * R * 16, p.NV - n0);
-  for (int idx = threadIdx.x; idx < p.M * rows; idx += kSThreads) {
-    const int m = idx / rows, n = n0 + idx % rows;
-    float v = 0.f;
-    for (int k2 = 0; k2 < p.KS; ++k2)
-      v += __hip_atomic_load(p.part + ((int64_t)k2 * p.M + m) * p.NV + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    store_y(tile_ref(p.ms, n >> 4), n & 15, m, v * mul, p.y_f16);
+  const int outs = p.M * rows;
+  constexpr int kOut = 4, kRanges = 4;
+  for (int base = 0; base < outs; base += kOut * kSThreads) {
+    int pm[kOut], pn[kOut];
+    float v[kOut];
+#pragma unroll
+    for (int o = 0; o < kOut; ++o) {
+      const int idx = min(base + o * kSThreads + int(threadIdx.x), outs - 1);
+      pm[o] = idx / rows;
+      pn[o] = n0 + idx % rows;
+      v[o] = 0.f;
+    }
+    for (int k0 = 0; k0 < p.KS; k0 += kRanges) {
+      float pv[kOut][kRanges];
+#pragma unroll
+      for (int o = 0; o < kOut; ++o)
+#pragma unroll
+        for (int k = 0; k < kRanges; ++k)
+          pv[o][k] = __hip_atomic_load(p.part + ((int64_t)min(k0 + k, p.KS - 1) * p.M + pm[o]) * p.NV + pn[o],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int o = 0; o < kOut; ++o)
+#pragma unroll
+        for (int k = 0; k < kRanges; ++k)
+          if (k0 + k < p.KS) v[o] += pv[o][k];
+    }
+#pragma unroll
+    for (int o = 0; o < kOut; ++o)
+      if (base + o * kSThreads + int(threadIdx.x) < outs) store_y(tile_ref(p.ms, pn[o] >> 4), pn[o] & 15, pm[o], v[o] * mul, p.y_f16);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
