@@ -592,18 +592,20 @@ hipError_t launch_mt(const LaunchArgs &a) {
                        : launch_mt_full<FMT, BF, MT, FP4, RA, RB, false>(a);
 }
 
-// Path choice, from timings of the decode shapes on MI355X.
+// Path choice, from timings of the decode shapes on MI355X (the split
+// kernel can run without a workspace only when it need not cut K, which its
+// plan ensures for 65536 rows and more).
 // Binary weights with bf16 x (fp8 x fp4 kernels):
-//  * one token, or small x: the workgroup-staged kernel above (x of the
-//    whole K fits in LDS at once, no second kernel stage);
-//  * more tokens with a long K, or 9..16 tokens: the 2-D split (row blocks x
-//    K ranges, x converted once per block, gemv_split.hip), which needs the
-//    caller's workspace to split K across workgroups;
-//  * 9..16 tokens on a small matrix: x loaded straight into registers
-//    (gemv_wide.hip).
-// Exact f16 / bf16 operands (ternary weights, fp16 x): the 2-D split for 2+
-// tokens on long rows or tall matrices (x staged as it is), else the staged
-// kernel for up to 4 tokens and the register kernel beyond.
+//  * one token: the workgroup-staged kernel above (x of the whole K in LDS);
+//  * 2..8 tokens: the staged kernel, or the 2-D split (row blocks x K
+//    ranges, x converted once per block, gemv_split.hip) on long rows, on
+//    4+ tokens below 65536 rows, and on 5+ tokens of very tall matrices;
+//  * 9..16 tokens: the 2-D split; without a workspace on a small matrix, x
+//    loaded straight into registers (gemv_wide.hip).
+// Exact f16 / bf16 operands (ternary weights, fp16 x): the staged kernel for
+// up to 4 tokens unless the rows are long or the matrix tall, the 2-D split
+// for 5..8 tokens on 8192+ rows or long rows and for 9..16 tokens, else the
+// register kernel.
 //
 // The fp8 x fp4 kernels (the staged one with FP4, and the split) hold each
 // 32-value activation block at one shared exponent: values within 2^7 of
@@ -615,23 +617,22 @@ hipError_t launch_mt(const LaunchArgs &a) {
 template <int FMT, bool BF>
 hipError_t launch_fmt(const LaunchArgs &a) {
   const bool ws_ok = a.ws && a.ws_bytes >= gemv_split_workspace_bytes(a.M, a.N, a.K);
+  const bool split_ok = ws_ok || a.N >= 65536;
   if constexpr (BF && FMT == 1) {
     constexpr int RB = 4;
-    if (a.M > 8) {
-      if (a.N <= 8192 && a.K <= 8192) return launch_gemv_wide(a);
-      if (ws_ok || a.N >= 65536) return launch_gemv_split(a);
-      return launch_gemv_wide(a);
-    }
-    const bool split = ws_ok && a.M >= 2 && (a.K >= 8192 || (a.M >= 4 && a.N < 65536));
+    if (a.M > 8) return split_ok ? launch_gemv_split(a) : launch_gemv_wide(a);
+    const bool split = a.M >= 2 && ((ws_ok && (a.K >= 8192 || (a.M >= 4 && a.N < 65536))) ||
+                                    (a.M > 4 && a.N >= 65536));
     if (split) return launch_gemv_split(a);
     if (a.M <= 1) return launch_mt<FMT, BF, 1, true, 1, 2>(a);
     if (a.M <= 2) return launch_mt<FMT, BF, 2, true, 2, RB>(a);
     if (a.M <= 4) return launch_mt<FMT, BF, 4, true, 2, RB>(a);
     return launch_mt<FMT, BF, 8, true, 2, RB>(a);
   } else {
+    if (a.M > 8) return split_ok ? launch_gemv_split(a) : launch_gemv_wide(a);
     if (a.M >= 2) {
-      const bool split = a.K >= 8192 || (a.N >= 24576 && (a.M > 4 || a.N < 65536));
-      if (split && (ws_ok || a.N >= 65536)) return launch_gemv_split(a);
+      const bool split = a.K >= 8192 || (a.M > 4 ? a.N >= 8192 : (a.N >= 24576 && a.N < 65536));
+      if (split && split_ok) return launch_gemv_split(a);
     }
     if (a.M <= 1) return launch_mt<FMT, BF, 1, false, 1, 2>(a);
     if (a.M <= 4) return launch_mt<FMT, BF, 4, false, 1, 2>(a);

@@ -49,63 +49,62 @@ struct WUnit {
   u4_t x[4];       // A operand of the four k-steps
 };
 
-// Loads of one unit, without per-lane branches around them (a divergent
-// branch around a load makes the compiler drain every load in flight at the
-// join).  Ragged tiles clamp their addresses and zero the values afterwards;
-// token rows >= M read row 0 and are zeroed.
+// Per tile set: the tile starts (uniform) and each lane's scale row, resolved
+// once per set (tiles past the launch resolve to the last tile; their sums
+// are never stored).
+template <int R>
+struct WTiles {
+  const uint8_t *w[R];
+  const uint16_t *s[R];
+  int rt[R];  // rows of each tile (16 but in a matrix's last tile)
+};
+
 template <int FMT, int R>
-__device__ __forceinline__ void load_wunit(const WideParams &p, WUnit<FMT, R> &u, int t0, int g, bool valid) {
+__device__ __forceinline__ void resolve_wtiles(const WideParams &p, WTiles<R> &ts, int t0) {
+  const int j = threadIdx.x & 15;
+  const int64_t unit = FMT == 1 ? 16 : 32;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const TileRef tr = tile_ref(p.ms, uni(min(t0 + r, p.tiles - 1)));
+    const int RT = uni(min(16, tr.N - 16 * tr.t));
+    ts.w[r] = tr.W + 16 * (int64_t)tr.t * p.G * unit;
+    ts.s[r] = tr.Sc + (int64_t)(16 * tr.t + min(j, RT - 1)) * p.G;
+    ts.rt[r] = RT;
+  }
+}
+
+// Loads of one unit (group g of the tile set), without branches around them
+// and without touching the loaded values: a divergent branch around a load,
+// or a value used at once, makes the compiler wait for every load in flight
+// (the wait counts are in issue order).  Units outside the sequence re-read
+// group 0.  Lanes of rows past a ragged tile, and of token rows past M, read
+// row 0 / token 0 again: an A row (token) or B column (row) only feeds its
+// own output, and those outputs are never stored.
+template <int FMT, int R>
+__device__ __forceinline__ void load_wunit(const WideParams &p, const WTiles<R> &ts, WUnit<FMT, R> &u, int g) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, q = lane >> 4;
-  const u4_t z = {0u, 0u, 0u, 0u};
-  if (!valid) {  // wave-uniform
+  const uint16_t *xr = p.X + (j < p.M ? (int64_t)j * p.K : 0) + 128 * g + 8 * q;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int i = 0; i < WUnit<FMT, R>::WPG; ++i) u.w[r][i] = 0;
-      u.s[r] = 0;
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) u.x[s] = z;
-    return;
-  }
-  const bool tok = j < p.M;
-  const uint16_t *xr = p.X + (tok ? (int64_t)j * p.K : 0) + 128 * g + 8 * q;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const u4_t v = *reinterpret_cast<const u4_t *>(xr + 32 * s);
-    u.x[s] = tok ? v : z;
-  }
+  for (int s = 0; s < 4; ++s) u.x[s] = *reinterpret_cast<const u4_t *>(xr + 32 * s);
   const int c = g >> 2, gc = g & 3;
   const int Gc = uni(min(4, p.G - 4 * c));
   const int64_t unit = FMT == 1 ? 16 : 32;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int t = uni(t0 + r);
-    if (t >= p.tiles) {  // wave-uniform
-#pragma unroll
-      for (int i = 0; i < WUnit<FMT, R>::WPG; ++i) u.w[r][i] = 0;
-      u.s[r] = 0;
-      continue;
-    }
-    const TileRef tr = tile_ref(p.ms, t);
-    const int RT = uni(min(16, tr.N - 16 * tr.t));
-    const bool row_ok = j < RT;
+    const int RT = ts.rt[r];
     const int jj = min(j, RT - 1);
-    const uint32_t *blk =
-        reinterpret_cast<const uint32_t *>(tr.W + 16 * (int64_t)tr.t * p.G * unit + (int64_t)RT * 4 * c * unit);
+    const uint32_t *blk = reinterpret_cast<const uint32_t *>(ts.w[r] + (int64_t)RT * 4 * c * unit);
     if constexpr (FMT == 1) {
-      const uint32_t w = __builtin_nontemporal_load(blk + (q * RT + jj) * Gc + gc);
-      u.w[r][0] = row_ok ? w : 0u;
+      u.w[r][0] = __builtin_nontemporal_load(blk + (q * RT + jj) * Gc + gc);
     } else {
       const int hh = gc >> 1, Gh = min(2, Gc - 2 * hh);
       const u2_t w = __builtin_nontemporal_load(
           reinterpret_cast<const u2_t *>(blk + RT * 16 * hh + ((q * RT + jj) * Gh + (gc - 2 * hh)) * 2));
-      u.w[r][0] = row_ok ? w.x : 0u;
-      u.w[r][1] = row_ok ? w.y : 0u;
+      u.w[r][0] = w.x;
+      u.w[r][1] = w.y;
     }
-    const uint32_t sv = tr.Sc[(int64_t)(16 * tr.t + jj) * p.G + g];
-    u.s[r] = row_ok ? sv : 0u;
+    u.s[r] = ts.s[r][g];
   }
 }
 
@@ -171,18 +170,34 @@ __global__ void __launch_bounds__(kThreads, 2) gemv_wide_kernel(WideParams p) {
   auto group = [&](int i) { return g_begin + i % GS; };
   auto valid = [&](int i) { return (i / GS) * rows_total + my_row < p.tilesets && group(i) < p.G; };
 
+  // The load side walks (tile set, group) with its own cursor and resolves
+  // the tile addresses when it enters a tile set.
+  int ld_i = 0, ld_k = 0;
+  WTiles<R> lts;
+  resolve_wtiles<FMT, R>(p, lts, uni(tile0(0)));
+  auto load = [&](WUnit<FMT, R> &u) {
+    const bool v = ld_i < total && valid(ld_i);
+    load_wunit<FMT, R>(p, lts, u, uni(v ? group(ld_i) : 0));
+    ++ld_i;
+    if (++ld_k == GS) {
+      ld_k = 0;
+      resolve_wtiles<FMT, R>(p, lts, uni(tile0(ld_i)));
+    }
+  };
+
   WUnit<FMT, R> ring[D];
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d) load_wunit<FMT, R>(p, ring[d], uni(tile0(d)), uni(group(d)), d < total && valid(d));
+  for (int d = 0; d < D - 1; ++d) load(ring[d]);
 
   float yacc[R][4];
   for (int i0 = 0; i0 < total; i0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int i = i0 + d;
-      if (i >= total) break;
-      const int nx = i + D - 1;
-      load_wunit<FMT, R>(p, ring[(d + D - 1) % D], uni(tile0(nx)), uni(group(nx)), nx < total && valid(nx));
+      // Every step issues its loads and none leaves the loop early, so the
+      // wait before a unit's MFMAs covers that unit only.
+      load(ring[(d + D - 1) % D]);
+      if (i >= total) continue;
       const int k = i % GS;
       if (k == 0) {
 #pragma unroll
