@@ -75,7 +75,8 @@ __host__ __device__ constexpr int split_buf_bytes(int MP, int GP, int MODE) {
 // Raw x of one (token, group, lane quarter) item, held between its load and
 // its conversion.
 struct RawQ {
-  u4_t v[4];
+  u4_t v[4];  // as loaded: zeroed only when converted, so the load waits nowhere
+  bool in;    // the item holds x (a token below M, a group of the pass)
 };
 
 template <int MP>
@@ -83,27 +84,27 @@ __device__ __forceinline__ void load_raw(const SplitParams &p, RawQ &r, int g0, 
   const int q = item & 3, rest = item >> 2;
   const int gl = rest % p.GP, m = rest / p.GP;
   live = item < MP * p.GP * 4;
-  const bool in = live && m < p.M && gl < np_groups;
-  const uint16_t *src = p.X + (in ? (int64_t)m * p.K + 128 * (g0 + gl) + 8 * q : 0);
-  const u4_t z = {0u, 0u, 0u, 0u};
+  r.in = live && m < p.M && gl < np_groups;
+  const uint16_t *src = p.X + (r.in ? (int64_t)m * p.K + 128 * (g0 + gl) + 8 * q : 0);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const u4_t x = *reinterpret_cast<const u4_t *>(src + 32 * u);
-    r.v[u] = in ? x : z;
-  }
+  for (int u = 0; u < 4; ++u) r.v[u] = *reinterpret_cast<const u4_t *>(src + 32 * u);
 }
 
 template <int FMT, int MP, int MODE>
 __device__ __forceinline__ void convert_raw(const SplitParams &p, const RawQ &r, char *buf, int item) {
   const int q = item & 3, rest = item >> 2;
   const int gl = rest % p.GP, m = rest / p.GP;
+  const u4_t z = {0u, 0u, 0u, 0u};
+  u4_t v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = r.in ? r.v[u] : z;
   if constexpr (MODE != kFp4) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<u4_t *>(buf + (((gl * 4 + u) * 4 + q) * MP + m) * 16) = r.v[u];
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u4_t *>(buf + (((gl * 4 + u) * 4 + q) * MP + m) * 16) = v[u];
     return;
   }
   XQuarter xq;
-  split_x_regs<FMT>(r.v, xq);
+  split_x_regs<FMT>(v, xq);
   char *row = buf + (gl * 2 * MP + 2 * m) * kRowBytes;
   const int qa = 2 * (q & 1), half = 16 * (q >> 1);
   *reinterpret_cast<u4_t *>(row + qa * 32 + half) = xq.h0;
@@ -190,7 +191,11 @@ __device__ __forceinline__ void compute_chunk_ex(const SplitParams &p, const cha
   }
 }
 
-template <int FMT, int MP, int R, int MODE>
+// FULL: every matrix has whole row tiles and K whole chunks; a wave's tiles
+// are fixed for the launch, so their addresses are resolved once and each
+// chunk is one load per tile at a fixed stride (the general path resolves
+// the tile and its ragged shape per chunk).
+template <int FMT, int MP, int R, int MODE, bool FULL>
 __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p) {
   // Accumulator sets per tile: fp4 A rows hold (token, piece) pairs, 8 tokens
   // per MFMA; exact operands hold 16 tokens per MFMA.
@@ -207,16 +212,28 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
   const int t0 = uni(rb * 8 * R + wave * R);
   const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
 
-  // Weights: two chunks in flight, in two named units.
-  Unit<FMT, R> u0, u1;
-  load_unit<FMT, R>(p, u0, t0, c0, true);
-  if (nchunks > 1) load_unit<FMT, R>(p, u1, t0, c0 + 1, true);
-
-  // x: pass 0 staged now; the raw x of pass 1 goes out before pass 0 is used.
+  // x of pass 0 is loaded first, then the first two chunks of weights, so
+  // that waiting for x (an in-order count) leaves the weights in flight.
   const int npass = (ng + p.GP - 1) / p.GP;
+  const int cpp = p.GP / 4;  // chunks per pass
   RawQ raw;
   bool live;
   load_raw<MP>(p, raw, g0, min(p.GP, ng), threadIdx.x, live);
+
+  // Weights: a ring of two units.  Every step computes one chunk and issues
+  // the load of the chunk two ahead, clamped to the range's last chunk, so
+  // that every path through the loop issues the same loads and the wait
+  // before a chunk's MFMAs covers that chunk only.
+  TileSet<R> ts;
+  if constexpr (FULL) resolve_tiles<FMT, R>(p, ts, t0);
+  auto load = [&](Unit<FMT, R> &u, int c) {
+    if constexpr (FULL) load_full<FMT, R>(ts, u, c0 + c);
+    else load_unit<FMT, R>(p, u, t0, c0 + c, true);
+  };
+  Unit<FMT, R> ring[2];
+  load(ring[0], 0);
+  load(ring[1], min(1, nchunks - 1));
+
   if (live) convert_raw<FMT, MP, MODE>(p, raw, lds, threadIdx.x);
   if constexpr (MODE != kFp4) {
     if (threadIdx.x == 0) {
@@ -225,6 +242,8 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
     }
   }
   __syncthreads();
+  // The raw x of pass 1 goes out while pass 0 is multiplied.
+  if (npass > 1) load_raw<MP>(p, raw, g0 + p.GP, min(p.GP, ng - p.GP), threadIdx.x, live);
 
   float yacc[R][TB][4];
 #pragma unroll
@@ -234,34 +253,28 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
 #pragma unroll
       for (int e = 0; e < 4; ++e) yacc[r][tb][e] = 0.f;
 
-  int c = 0;  // chunk index inside the K range
-  for (int ps = 0; ps < npass; ++ps) {
-    const int pg0 = ps * p.GP;  // first group of this pass (range-relative)
-    const int png = min(p.GP, ng - pg0);
-    char *cur = lds + (ps & 1) * p.buf_bytes;
-    char *nxt = lds + ((ps + 1) & 1) * p.buf_bytes;
-    const bool more = ps + 1 < npass;
-    if (more) load_raw<MP>(p, raw, g0 + pg0 + p.GP, min(p.GP, ng - pg0 - p.GP), threadIdx.x, live);
-    // Chunks of this pass (GP is a multiple of 4, so passes hold whole chunks).
-    for (int cc = 0; cc < (png + 3) / 4; cc += 2) {
-      if constexpr (MODE == kFp4) compute_chunk<FMT, MP, R, TB>(p, cur, u0, 4 * cc, min(4, png - 4 * cc), yacc);
-      else compute_chunk_ex<FMT, MP, R, MODE>(p, cur, u0, 4 * cc, min(4, png - 4 * cc), yacc);
-      if (c + 2 < nchunks) load_unit<FMT, R>(p, u0, t0, c0 + c + 2, true);
-      ++c;
-      if (cc + 1 >= (png + 3) / 4) {
-        // Odd chunk count in this pass: the next pass starts on u1.
-        Unit<FMT, R> t = u0;
-        u0 = u1;
-        u1 = t;
-        break;
+  for (int c = 0; c < nchunks; c += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int cc = c + h;  // chunk inside the K range
+      if (cc < nchunks) {
+        const int ps = cc / cpp, cl = cc - ps * cpp;
+        if (ps > 0 && cl == 0) {
+          // First chunk of pass ps: its x, loaded during pass ps - 1, goes into
+          // the buffer of pass ps - 2 (every wave left that pass before the
+          // previous barrier); then the raw x of pass ps + 1 goes out.
+          if (live) convert_raw<FMT, MP, MODE>(p, raw, lds + (ps & 1) * p.buf_bytes, threadIdx.x);
+          __syncthreads();
+          const int nx = (ps + 1) * p.GP;
+          if (ps + 1 < npass) load_raw<MP>(p, raw, g0 + nx, min(p.GP, ng - nx), threadIdx.x, live);
+        }
+        const char *cur = lds + (ps & 1) * p.buf_bytes;
+        const int png = min(p.GP, ng - ps * p.GP);
+        if constexpr (MODE == kFp4) compute_chunk<FMT, MP, R, TB>(p, cur, ring[h], 4 * cl, min(4, png - 4 * cl), yacc);
+        else compute_chunk_ex<FMT, MP, R, MODE>(p, cur, ring[h], 4 * cl, min(4, png - 4 * cl), yacc);
       }
-      if constexpr (MODE == kFp4) compute_chunk<FMT, MP, R, TB>(p, cur, u1, 4 * (cc + 1), min(4, png - 4 * (cc + 1)), yacc);
-      else compute_chunk_ex<FMT, MP, R, MODE>(p, cur, u1, 4 * (cc + 1), min(4, png - 4 * (cc + 1)), yacc);
-      if (c + 2 < nchunks) load_unit<FMT, R>(p, u1, t0, c0 + c + 2, true);
-      ++c;
+      load(ring[h], min(cc + 2, nchunks - 1));
     }
-    if (more && live) convert_raw<FMT, MP, MODE>(p, raw, nxt, threadIdx.x);
-    __syncthreads();
   }
 
   // This lane's outputs: (tile r, token m, value).  fp4: element e of lane
@@ -376,7 +389,7 @@ struct SplitPlan {
 
 // Per-wave work of the busiest workgroup slot, in (tile, group) units, with
 // charges for staging x, for workgroup start-up and for the partial sums.
-template <int FMT, int MP, int R, int MODE>
+template <int FMT, int MP, int R, int MODE, bool FULL>
 void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
   SplitParams p{};
   p.ms = mat_set(a);
@@ -389,7 +402,7 @@ void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
   p.GP = pass_groups(MP, p.G, MODE);
   p.buf_bytes = split_buf_bytes(MP, p.GP, MODE);
   const int lds = 2 * p.buf_bytes;
-  const void *kern = reinterpret_cast<const void *>(&gemv_split_kernel<FMT, MP, R, MODE>);
+  const void *kern = reinterpret_cast<const void *>(&gemv_split_kernel<FMT, MP, R, MODE, FULL>);
   const int slots = num_cus() * resident_blocks(kern, kSThreads, lds);
   for (int GK = 4; GK < p.G + 4; GK += 4) {
     const int gk = GK < p.G ? GK : p.G;
@@ -416,12 +429,12 @@ void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
   }
 }
 
-template <int FMT, int MP, int MODE>
-hipError_t launch_split_mp(const LaunchArgs &a) {
+template <int FMT, int MP, int MODE, bool FULL>
+hipError_t launch_split_full(const LaunchArgs &a) {
   SplitPlan b1, b2, b4;
-  plan_split<FMT, MP, 1, MODE>(a, a.ws_bytes, b1);
-  plan_split<FMT, MP, 2, MODE>(a, a.ws_bytes, b2);
-  plan_split<FMT, MP, 4, MODE>(a, a.ws_bytes, b4);
+  plan_split<FMT, MP, 1, MODE, FULL>(a, a.ws_bytes, b1);
+  plan_split<FMT, MP, 2, MODE, FULL>(a, a.ws_bytes, b2);
+  plan_split<FMT, MP, 4, MODE, FULL>(a, a.ws_bytes, b4);
   int R = 1;
   SplitPlan *b = &b1;
   if (b2.cost < b->cost) { b = &b2; R = 2; }
@@ -431,15 +444,31 @@ hipError_t launch_split_mp(const LaunchArgs &a) {
     b->p.part = reinterpret_cast<float *>(static_cast<char *>(a.ws) + kPartOffset);
   }
   if (R == 1)
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream,
+                       b->p);
   else if (R == 2)
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2, MODE>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2, MODE, FULL>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream,
+                       b->p);
   else
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4, MODE>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream, b->p);
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4, MODE, FULL>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream,
+                       b->p);
   return hipGetLastError();
 }
 
 // Exact modes stage 1, 4 or 16 token slots (cells per token slot).
+// Every matrix of the launch has whole row tiles and K whole chunks.
+inline bool split_full(const LaunchArgs &a) {
+  if (a.K % 512 != 0) return false;
+  for (int i = 0; i < a.nmat; ++i)
+    if (a.Ns[i] % 16 != 0) return false;
+  return true;
+}
+
+template <int FMT, int MP, int MODE>
+hipError_t launch_split_mp(const LaunchArgs &a) {
+  return split_full(a) ? launch_split_full<FMT, MP, MODE, true>(a) : launch_split_full<FMT, MP, MODE, false>(a);
+}
+
 template <int FMT, int MODE>
 hipError_t launch_split_fmt(const LaunchArgs &a) {
   if constexpr (MODE == kFp4) {
