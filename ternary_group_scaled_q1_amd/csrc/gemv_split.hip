@@ -384,13 +384,13 @@ struct SplitPlan {
   SplitParams p;
   int grid = 0;
   int lds = 0;
-  double cost = 1e300;
 };
 
-// Per-wave work of the busiest workgroup slot, in (tile, group) units, with
-// charges for staging x, for workgroup start-up and for the partial sums.
+// Parameters of the launch with R row tiles per wave and K cut into ranges
+// of gk groups (false if the workspace, the partial-sum area or the counters
+// cannot hold that cut).
 template <int FMT, int MP, int R, int MODE, bool FULL>
-void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
+bool make_split(const LaunchArgs &a, int gk, SplitPlan &pl) {
   SplitParams p{};
   p.ms = mat_set(a);
   p.X = a.X;
@@ -401,61 +401,65 @@ void plan_split(const LaunchArgs &a, int64_t ws_bytes, SplitPlan &best) {
   p.row_blocks = (p.tiles + 8 * R - 1) / (8 * R);
   p.GP = pass_groups(MP, p.G, MODE);
   p.buf_bytes = split_buf_bytes(MP, p.GP, MODE);
-  const int lds = 2 * p.buf_bytes;
-  const void *kern = reinterpret_cast<const void *>(&gemv_split_kernel<FMT, MP, R, MODE, FULL>);
-  const int slots = num_cus() * resident_blocks(kern, kSThreads, lds);
-  for (int GK = 4; GK < p.G + 4; GK += 4) {
-    const int gk = GK < p.G ? GK : p.G;
-    const int KS = (p.G + gk - 1) / gk;
-    if (KS > kMaxKS) continue;
-    if (KS > 1 && (gk % 4 || (int64_t)KS * a.M * p.NV * 4 > kMaxPartBytes || p.row_blocks > kMaxCounters ||
-                   split_ws_bytes(a.M, p.NV, KS) > ws_bytes))
-      continue;
-    const int64_t wgs = (int64_t)p.row_blocks * KS;
-    const double rounds = double((wgs + slots - 1) / slots);
-    const double stage = 8.0 * ((gk + p.GP - 1) / p.GP);        // per pass: convert + barrier
-    const double work = double(R) * gk * (MODE == kFp4 ? (MP > 8 ? 2.0 : 1.0) : 2.0);  // MFMA sets per wave
-    const double reduce = KS > 1 ? 6.0 + 0.02 * KS * MP * R : 0.0;
-    const double cost = rounds * (work + stage + 12.0 + reduce);
-    if (cost < best.cost) {
-      best.cost = cost;
-      best.p = p;
-      best.p.GK = gk;
-      best.p.KS = KS;
-      best.grid = int(wgs);
-      best.lds = lds;
-    }
-    if (KS == 1) break;
-  }
+  gk = gk < p.G ? gk : p.G;
+  const int KS = (p.G + gk - 1) / gk;
+  if (KS > kMaxKS) return false;
+  if (KS > 1 && (gk % 4 || (int64_t)KS * a.M * p.NV * 4 > kMaxPartBytes || p.row_blocks > kMaxCounters ||
+                 split_ws_bytes(a.M, p.NV, KS) > a.ws_bytes))
+    return false;
+  p.GK = gk;
+  p.KS = KS;
+  pl.p = p;
+  pl.grid = p.row_blocks * KS;
+  pl.lds = 2 * p.buf_bytes;
+  return true;
 }
 
+// Plan, from timings of the decode shapes at 2..16 tokens on MI355X: a CU
+// that holds two workgroups runs each about 1.45x slower, and a workgroup's
+// time is a fixed part (x staging, the K-range reduction, launch) plus a
+// part per group of its K range.  So: the fewest row tiles per wave whose
+// row blocks fit one per CU, then the most K ranges that keep the grid
+// within the CUs (each range shortens every workgroup).  Matrices too tall
+// for that take two tiles per wave and the whole of K (fewer rows per wave
+// would only add waves that wait their turn; more hold too many registers).
 template <int FMT, int MP, int MODE, bool FULL>
 hipError_t launch_split_full(const LaunchArgs &a) {
-  SplitPlan b1, b2, b4;
-  plan_split<FMT, MP, 1, MODE, FULL>(a, a.ws_bytes, b1);
-  plan_split<FMT, MP, 2, MODE, FULL>(a, a.ws_bytes, b2);
-  plan_split<FMT, MP, 4, MODE, FULL>(a, a.ws_bytes, b4);
-  int R = 1;
-  SplitPlan *b = &b1;
-  if (b2.cost < b->cost) { b = &b2; R = 2; }
-  if (b4.cost < b->cost) { b = &b4; R = 4; }
-  if (b->p.KS > 1) {
-    b->p.count = static_cast<unsigned *>(a.ws);
-    b->p.part = reinterpret_cast<float *>(static_cast<char *>(a.ws) + kPartOffset);
+  const int cus = num_cus();
+  const int tiles = int((a.N + 15) / 16), G = int(a.K / kGroup);
+  const int R = (tiles + 7) / 8 <= cus ? 1 : ((tiles + 15) / 16 <= cus ? 2 : ((tiles + 31) / 32 <= cus ? 4 : 2));
+  const int blocks = (tiles + 8 * R - 1) / (8 * R);
+  SplitPlan pl;
+  bool ok = false;
+  if (blocks <= cus) {
+    // Most ranges first: gk = 4, 8, ... groups (a multiple of 4).
+    for (int gk = 4; gk < G + 4 && !ok; gk += 4) {
+      const int ks = (G + gk - 1) / gk;
+      if ((int64_t)blocks * ks > cus && gk < G) continue;
+      if (R == 1) ok = make_split<FMT, MP, 1, MODE, FULL>(a, gk, pl);
+      else if (R == 2) ok = make_split<FMT, MP, 2, MODE, FULL>(a, gk, pl);
+      else ok = make_split<FMT, MP, 4, MODE, FULL>(a, gk, pl);
+    }
+  } else {
+    ok = make_split<FMT, MP, 2, MODE, FULL>(a, G, pl);
+  }
+  if (!ok) return hipErrorInvalidValue;
+  if (pl.p.KS > 1) {
+    pl.p.count = static_cast<unsigned *>(a.ws);
+    pl.p.part = reinterpret_cast<float *>(static_cast<char *>(a.ws) + kPartOffset);
   }
   if (R == 1)
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream,
-                       b->p);
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL>), dim3(pl.grid), dim3(kSThreads), pl.lds, a.stream,
+                       pl.p);
   else if (R == 2)
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2, MODE, FULL>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream,
-                       b->p);
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2, MODE, FULL>), dim3(pl.grid), dim3(kSThreads), pl.lds, a.stream,
+                       pl.p);
   else
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4, MODE, FULL>), dim3(b->grid), dim3(kSThreads), b->lds, a.stream,
-                       b->p);
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4, MODE, FULL>), dim3(pl.grid), dim3(kSThreads), pl.lds, a.stream,
+                       pl.p);
   return hipGetLastError();
 }
 
-// Exact modes stage 1, 4 or 16 token slots (cells per token slot).
 // Every matrix of the launch has whole row tiles and K whole chunks.
 inline bool split_full(const LaunchArgs &a) {
   if (a.K % 512 != 0) return false;
