@@ -498,8 +498,12 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
   }
 }
 
-// Host-side choice of (R, S): the smallest per-wave work (the makespan:
-// tile sets per wave-row x R x chunks per wave), then fewer barriers.
+// Host-side choice of (R, S, grid), from timings of the decode shapes at one
+// token on MI355X: a workgroup costs a fixed part (x staging) worth about two
+// units plus its waves' units (one more per tile set when waves split K),
+// and a CU that holds n workgroups runs each about 1 + 0.45 (n - 1) times
+// slower.  So every (S, grid cap of 1, 2, ... workgroups per CU) is costed
+// as (units per wave + 2) x that factor, and the cheapest wins.
 template <int FMT, bool BF, int MT, int R, int D, bool FP4, bool FULL>
 double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) {
   constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
@@ -539,25 +543,29 @@ double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) 
     q.off_corr = m.corr; q.off_x = m.x; q.off_red = m.red;
     const int P = kWaves / S;
     const int per_cu = resident_blocks(kern, kThreads, m.total);
-    const int g = max(1, min((q.tilesets + P - 1) / P, cus * per_cu));
-    const int64_t rows = (int64_t)g * P;
-    // Makespan in units of (tile, chunk) work per wave, with a small charge
-    // for workgroup barriers (K split or streamed stages).
-    const double units = double((q.tilesets + rows - 1) / rows) * R * ((p.chunks + S - 1) / S);
-    const double cost = units * ((S > 1 || q.n_stages > 1) ? 1.05 : 1.0);
-    if (cost < best) {
-      best = cost;
-      bp = q;
-      bgrid = g;
-      blds = m.total;
+    const int want = (q.tilesets + P - 1) / P;
+    for (int n = 1; n <= per_cu; ++n) {
+      const int g = max(1, min(want, cus * n));
+      const int64_t rows = (int64_t)g * P;
+      const int64_t its = (q.tilesets + rows - 1) / rows;
+      // Waves that split K add their sums through LDS once per tile set
+      // (two barriers): about one unit each.
+      const double units = double(its) * R * ((p.chunks + S - 1) / S) + (S > 1 ? double(its) : 0.0);
+      const int share = (g + cus - 1) / cus;
+      const double cost = (units + 2.0) * (1.0 + 0.45 * (share - 1));
+      if (cost < best) {
+        best = cost;
+        bp = q;
+        bgrid = g;
+        blds = m.total;
+      }
+      if (g == want) break;
     }
   }
   p = bp;
   grid = bgrid;
   lds_bytes = blds;
-  // One row tile per unit reads the x operand from LDS once per MFMA instead
-  // of once per R.
-  return best * (R == 1 ? 1.1 : 1.0);
+  return best;
 }
 
 template <int FMT, bool BF, int MT, bool FP4, int RA, int RB, bool FULL>
