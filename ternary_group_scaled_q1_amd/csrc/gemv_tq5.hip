@@ -334,6 +334,224 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
   }
 }
 
+// Addresses of the R tiles of one tile set, resolved once per set: the
+// tile's start, the lane's row of scales and the tile's rows (tiles past the
+// launch resolve to the last tile; their sums are never stored).
+template <int R>
+struct T5Tiles {
+  const uint8_t *w[R];
+  const uint16_t *s[R];
+  int rt[R];
+};
+
+template <int R>
+__device__ __forceinline__ void t5_resolve(const T5Params &p, T5Tiles<R> &ts, int t0) {
+  const int j = threadIdx.x & 15;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const TileRef tr = tile_ref(p.ms, uni(min(t0 + r, p.tiles - 1)));
+    const int RT = uni(min(16, tr.N - 16 * tr.t));
+    ts.w[r] = tr.W + 16 * (int64_t)tr.t * p.rowbytes;
+    ts.s[r] = tr.Sc + (int64_t)(16 * tr.t + min(j, RT - 1)) * p.G;
+    ts.rt[r] = RT;
+  }
+}
+
+// Loads of unit (tile set, segment seg) with neither branches nor masks, so
+// that each step of the ring issues the same loads: the row tail's segment
+// (read by the per-weight path) re-reads the last full segment, or the
+// tile's first bytes when a row has no full segment (the scales plane
+// follows the packed bytes, so 32 bytes from a tile's start stay inside the
+// blob); rows past a ragged tile re-read its last row and groups past K the
+// last group's scale.  None of those values reaches a stored output.
+template <int R>
+__device__ __forceinline__ void t5_load_ts(const T5Params &p, const T5Tiles<R> &ts, T5Unit<R> &u, int seg) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  const int sf = uni(max(min(seg, p.s_full - 1), 0));
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int RT = ts.rt[r];
+    const int jj = min(j, RT - 1);
+    const uint8_t *sb = p.s_full > 0 ? ts.w[r] + (int64_t)RT * 128 * sf + (q * RT + jj) * 16 : ts.w[r];
+    const int hb = p.s_full > 0 ? RT * 64 : 0;
+    u.a[r] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(sb));
+    u.b[r] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(sb + hb));
+#pragma unroll
+    for (int i = 0; i < 5; ++i) u.s[r][i] = ts.s[r][min(5 * seg + i, p.G - 1)];
+  }
+}
+
+// One token with x staged in LDS: the units of a wave form a ring of three,
+// stepped by compile-time slots (no register moves between units), every
+// step issues its loads and none leaves the loop early, so the wait before a
+// unit's MFMAs covers that unit only.  The x of the whole K is loaded into
+// registers before the first weights and written to LDS after them.
+template <bool BF, int R>
+__global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_one_kernel(T5Params p) {
+  constexpr int D = 3;
+  constexpr int kXPre = 4;  // x cells per thread loaded before the weights
+  __shared__ uint16_t lut[256];
+  __shared__ float red[kT5Waves * R * 4 * 64];
+  extern __shared__ __align__(16) char xl[];
+
+  const int wave = uni(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int S = uni(p.S), P = kT5Waves / S;
+  const int pr = uni(wave / S), s = uni(wave - pr * S);
+  const int rows_total = gridDim.x * P;
+  const int my_row = pr * gridDim.x + blockIdx.x;
+  const int iters = (p.tilesets + rows_total - 1) / rows_total;
+  const int SS = uni(p.SS);
+  const int total = uni(iters * SS);
+  const int seg0 = s * SS;
+
+  auto tile0 = [&](int i) { return ((i / SS) * rows_total + my_row) * R; };
+  auto segment = [&](int i) { return seg0 + i % SS; };
+  auto valid = [&](int i) { return i < total && (i / SS) * rows_total + my_row < p.tilesets && segment(i) < p.nseg; };
+
+  // x cells (8 values each) of the first kXPre passes over the workgroup.
+  const int cells = p.K / 8;
+  u4_t xpre[kXPre];
+#pragma unroll
+  for (int c = 0; c < kXPre; ++c)
+    xpre[c] = reinterpret_cast<const u4_t *>(p.X)[min(int(threadIdx.x) + c * kT5Threads, cells - 1)];
+
+  // The load side: its cursor and the tile set it reads.
+  int ld_i = 0, ld_k = 0;
+  T5Tiles<R> lts;
+  t5_resolve<R>(p, lts, uni(tile0(0)));
+  auto load = [&](T5Unit<R> &u) {
+    const bool v = valid(ld_i);
+    t5_load_ts<R>(p, lts, u, uni(v ? segment(ld_i) : seg0));
+    ++ld_i;
+    if (++ld_k == SS) {
+      ld_k = 0;
+      t5_resolve<R>(p, lts, uni(tile0(ld_i)));
+    }
+  };
+  T5Unit<R> ring[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) load(ring[d]);
+
+#pragma unroll
+  for (int c = 0; c < kXPre; ++c) {
+    const int cell = int(threadIdx.x) + c * kT5Threads;
+    if (cell < cells) reinterpret_cast<u4_t *>(xl)[cell] = xpre[c];
+  }
+  for (int cell = int(threadIdx.x) + kXPre * kT5Threads; cell < cells; cell += kT5Threads)
+    reinterpret_cast<u4_t *>(xl)[cell] = reinterpret_cast<const u4_t *>(p.X)[cell];
+  if (threadIdx.x == 0) *reinterpret_cast<u4_t *>(xl + p.K * 2) = u4_t{0u, 0u, 0u, 0u};
+  for (int v = threadIdx.x; v < 256; v += kT5Threads) {
+    uint32_t f = 0;
+    int dgt = v;
+    for (int i = 0; i < 5; ++i) {
+      const int di = dgt % 3;
+      dgt /= 3;
+      f |= (uint32_t(di == 0) << (15 - 2 * i)) | (uint32_t(di != 1) << (14 - 2 * i));
+    }
+    lut[v] = uint16_t(v < 243 ? f : 0);
+  }
+  __syncthreads();
+
+  float yacc[R][4];
+  for (int i0 = 0; i0 < total; i0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = i0 + d;
+      load(ring[(d + D - 1) % D]);
+      if (i >= total) continue;
+      const T5Unit<R> &cur = ring[d];
+      const int seg = uni(segment(i));
+      const int t0 = uni(tile0(i));
+      if (i % SS == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yacc[r][e] = 0.f;
+      }
+      if (valid(i)) {  // wave-uniform
+        const int ng = uni(min(5, p.G - 5 * seg));
+        u4_t xc[4];
+        if (seg < p.s_full) {  // full segment: five groups through the table
+          uint32_t dd[R][16];
+#pragma unroll
+          for (int r = 0; r < R; ++r) t5_decode(cur.a[r], cur.b[r], lut, dd[r]);
+#pragma unroll
+          for (int gi = 0; gi < 5; ++gi) {
+            t5_lds_x(p, xl, xc, 5 * seg + gi);
+            f4_t acc[R];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                u4_t bop;
+                bop.x = tq5_pair(dd[r][4 * u + 0], gi);
+                bop.y = tq5_pair(dd[r][4 * u + 1], gi);
+                bop.z = tq5_pair(dd[r][4 * u + 2], gi);
+                bop.w = tq5_pair(dd[r][4 * u + 3], gi);
+                acc[r] = u == 0 ? mfma16x16x32_zero<BF>(xc[u], bop) : mfma16x16x32<BF>(xc[u], bop, acc[r]);
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const float sc = half_to_float(cur.s[r][gi]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) yacc[r][e] = fmaf(sc, acc[r][e], yacc[r][e]);
+            }
+          }
+        } else {  // tail segment: ng < 5 groups, row-major bytes
+          for (int gi = 0; gi < ng; ++gi) {
+            t5_lds_x(p, xl, xc, 5 * seg + gi);
+            f4_t acc[R];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                const int t = t0 + r < p.tiles ? t0 + r : 0;
+                const u4_t bop = t5_tail_operand(p, tile_ref(p.ms, t), gi, u);
+                acc[r] = u == 0 ? mfma16x16x32_zero<BF>(xc[u], bop) : mfma16x16x32<BF>(xc[u], bop, acc[r]);
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const uint16_t sh = gi == 0 ? cur.s[r][0] : gi == 1 ? cur.s[r][1] : gi == 2 ? cur.s[r][2] : cur.s[r][3];
+              const float sc = half_to_float(sh);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) yacc[r][e] = fmaf(sc, acc[r][e], yacc[r][e]);
+            }
+          }
+        }
+      }
+      if (i % SS == SS - 1) {
+        const bool ts_ok = (i / SS) * rows_total + my_row < p.tilesets;
+        if (S == 1) {
+          if (ts_ok) t5_store<R>(p, t0, yacc);
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[((wave * R + r) * 4 + e) * 64 + lane] = yacc[r][e];
+          __syncthreads();
+          if (s == 0 && ts_ok) {
+            float tot[R][4];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float v = 0.f;
+                for (int s2 = 0; s2 < S; ++s2) v += red[(((pr * S + s2) * R + r) * 4 + e) * 64 + lane];
+                tot[r][e] = v;
+              }
+            t5_store<R>(p, t0, tot);
+          }
+          __syncthreads();
+        }
+      }
+    }
+  }
+}
+
 // Plan: the (S, grid) with the smallest per-wave work (tile sets per
 // wave-row x R x segments per wave), with a small charge for the K split.
 template <class Kern>
@@ -388,10 +606,76 @@ hipError_t launch_tq5_x(const LaunchArgs &a) {
   return hipGetLastError();
 }
 
-// One token whose x fits in 64 KB of LDS: staged once per workgroup.
+// Plan of the one-token kernel, with the cost the other decode kernels use
+// (from timings on MI355X): a workgroup costs its waves' units (segments;
+// one more per tile set when waves split K) plus a fixed part worth about
+// two, and a CU holding n workgroups runs each ~1 + 0.45 (n - 1) times
+// slower; every (S, grid cap of 1, 2, ... workgroups per CU) is costed.
+template <class Kern>
+double plan_tq5_one(const LaunchArgs &a, int R, Kern kernel, int lds, T5Params &p, int &grid) {
+  p = T5Params{};
+  p.ms = mat_set(a);
+  p.X = a.X;
+  p.M = int(a.M); p.K = int(a.K); p.G = int(a.K / kGroup);
+  p.tiles = int((a.N + 15) / 16);
+  p.tilesets = (p.tiles + R - 1) / R;
+  const Tq5Geom g = tq5_geom(a.K);
+  p.s_full = int(g.s_full);
+  p.b_tail = int(g.b_tail);
+  p.rowbytes = int(g.rowbytes);
+  p.nseg = p.s_full + (g.L_tail > 0 ? 1 : 0);
+  p.y_f16 = a.y_f16;
+  const int cus = num_cus();
+  const int per_cu = resident_blocks(reinterpret_cast<const void *>(kernel), kT5Threads, lds);
+  double best = 1e300;
+  T5Params bp = p;
+  int bgrid = 1;
+  for (int S = 1; S <= 8; S *= 2) {
+    if (S > 1 && S > p.nseg) break;
+    const int P = kT5Waves / S;
+    const int SS = (p.nseg + S - 1) / S;
+    const int want = (p.tilesets + P - 1) / P;
+    for (int n = 1; n <= per_cu; ++n) {
+      const int gsz = max(1, min(want, cus * n));
+      const int64_t rows = (int64_t)gsz * P;
+      const int64_t its = (p.tilesets + rows - 1) / rows;
+      const double units = double(its) * R * SS + (S > 1 ? double(its) : 0.0);
+      const int share = (gsz + cus - 1) / cus;
+      const double cost = (units + 2.0) * (1.0 + 0.45 * (share - 1));
+      if (cost < best) {
+        best = cost;
+        bp = p;
+        bp.S = S;
+        bp.SS = SS;
+        bgrid = gsz;
+      }
+      if (gsz == want) break;
+    }
+  }
+  p = bp;
+  grid = bgrid;
+  return best;
+}
+
+template <bool BF>
+hipError_t launch_tq5_one(const LaunchArgs &a) {
+  T5Params p1, p2;
+  int g1, g2;
+  const int lds = t5_xlds_bytes(a.K);
+  const double c1 = plan_tq5_one(a, 1, &gemv_tq5_one_kernel<BF, 1>, lds, p1, g1);
+  const double c2 = plan_tq5_one(a, 2, &gemv_tq5_one_kernel<BF, 2>, lds, p2, g2);
+  if (c1 <= c2)
+    hipLaunchKernelGGL((gemv_tq5_one_kernel<BF, 1>), dim3(g1), dim3(kT5Threads), lds, a.stream, p1);
+  else
+    hipLaunchKernelGGL((gemv_tq5_one_kernel<BF, 2>), dim3(g2), dim3(kT5Threads), lds, a.stream, p2);
+  return hipGetLastError();
+}
+
+// One token whose x fits in 64 KB of LDS: staged once per workgroup (the
+// ring kernel above); else x read into registers one group ahead.
 template <bool BF>
 hipError_t launch_tq5_t(const LaunchArgs &a) {
-  if (a.M == 1 && t5_xlds_bytes(a.K) <= 64 * 1024) return launch_tq5_x<BF, true>(a);
+  if (a.M == 1 && t5_xlds_bytes(a.K) <= 64 * 1024) return launch_tq5_one<BF>(a);
   return launch_tq5_x<BF, false>(a);
 }
 

@@ -458,3 +458,19 @@ def test_gemv_multi_fused(fmt, xdt):
         for i, ((codes, sc, _), y) in enumerate(zip(mats, ys)):
             if Ns[i]:
                 gu.check(y.cpu().numpy().astype(np.float64), codes, sc, x, xdt, f"multi no-ws {fmt} mat {i}")
+
+
+@pytest.mark.parametrize("fmt", ["q1", "tq2"])
+@pytest.mark.parametrize("M", [8, 16])
+def test_split_tall_matrix_four_tiles_per_wave(fmt, M):
+    """69632 rows: the 2-D split's row blocks of one or two tiles per wave
+    exceed the CUs, so it takes four (and cuts K); also a ragged last tile
+    of the same height (the general load path)."""
+    g = np.random.default_rng(910 + M)
+    K = 2048
+    for N in (69632, 69632 - 7):
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        x = synth.x_normal(g, M, K, "bf16")
+        y = gu.run("gemv", fmt, gu.w_tensor(lb.pack(fmt, codes, sc)), x, "bf16", "f32", N, K)
+        gu.check(y, codes, sc, x, "bf16", f"tall split {fmt} M={M} N={N}")
