@@ -112,6 +112,13 @@ __device__ __forceinline__ f4_t mfma_f8f4(u4_t a0, u4_t a1, u4_t b, int sa) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, z, 0, 4, 0, sa, 0, 0x7F7F7F7F);
 }
 
+// The same, added to the fp32 tile c.
+__device__ __forceinline__ f4_t mfma_f8f4_acc(u4_t a0, u4_t a1, u4_t b, int sa, f4_t c) {
+  const i8v_t A = {int(a0.x), int(a0.y), int(a0.z), int(a0.w), int(a1.x), int(a1.y), int(a1.z), int(a1.w)};
+  const i8v_t B = {int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 0, 4, 0, sa, 0, 0x7F7F7F7F);
+}
+
 // q1 word -> 32 fp4 weights: nibble i of dword d takes bit 4i + 3 - d;
 // bit 1 -> +1.0 (0x2), bit 0 -> -1.0 (0xA).
 __device__ __forceinline__ u4_t q1_fp4(uint32_t w) {

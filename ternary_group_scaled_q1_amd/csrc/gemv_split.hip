@@ -105,23 +105,26 @@ __device__ __forceinline__ void convert_raw(const SplitParams &p, const RawQ &r,
   }
   XQuarter xq;
   split_x_regs<FMT>(v, xq);
-  char *row = buf + (gl * 2 * MP + 2 * m) * kRowBytes;
+  // A rows of group gl: (token, piece) pairs 2m + piece up to 8 tokens; at 16
+  // tokens the hi pieces of all tokens, then the lo pieces.
+  char *row = buf + (gl * 2 * MP + (MP > 8 ? m : 2 * m)) * kRowBytes;
+  char *lrow = row + (MP > 8 ? MP : 1) * kRowBytes;
   const int qa = 2 * (q & 1), half = 16 * (q >> 1);
   *reinterpret_cast<u4_t *>(row + qa * 32 + half) = xq.h0;
   *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = xq.h1;
-  *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = xq.l0;
-  *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = xq.l1;
+  *reinterpret_cast<u4_t *>(lrow + qa * 32 + half) = xq.l0;
+  *reinterpret_cast<u4_t *>(lrow + (qa + 1) * 32 + half) = xq.l1;
   reinterpret_cast<uint8_t *>(buf + p.GP * 2 * MP * kRowBytes)[(gl * MP + m) * 4 + q] = xq.sb;
 }
 
-// One chunk (4 groups at buffer group offset gb) for R tiles.  Lane 16qa + r
-// of token block tb reads A row 16 tb + r (token 8 tb + r / 2, piece r % 2).
-template <int FMT, int MP, int R, int TB>
+// One chunk (4 groups at buffer group offset gb) for R tiles, up to 8 tokens:
+// lane 16qa + r reads A row r (token r / 2, piece r % 2), so one MFMA per
+// (tile, group) covers both pieces.
+template <int FMT, int MP, int R>
 __device__ __forceinline__ void compute_chunk(const SplitParams &p, const char *buf, const Unit<FMT, R> &u, int gb,
-                                              int ng, float (&yacc)[R][TB][4]) {
-  constexpr int ROWS = 2 * MP < 16 ? 2 * MP : 16;  // A rows per token block
+                                              int ng, float (&yacc)[R][1][4]) {
   const int lane = threadIdx.x & 63, qa = lane >> 4, r = lane & 15;
-  const bool arow = r < ROWS;
+  const bool arow = r < 2 * MP;
   const int rr = arow ? r : 0;
   const u4_t z = {0u, 0u, 0u, 0u};
   const uint8_t *scb = reinterpret_cast<const uint8_t *>(buf + p.GP * 2 * MP * kRowBytes);
@@ -129,29 +132,55 @@ __device__ __forceinline__ void compute_chunk(const SplitParams &p, const char *
   for (int gi = 0; gi < 4; ++gi) {
     if (gi >= ng) break;  // wave-uniform: groups past K in the last chunk
     const int gl = gb + gi;
-    u4_t a0[TB], a1[TB];
-    int sa[TB];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const char *xa = buf + (gl * 2 * MP + 16 * tb + rr) * kRowBytes + qa * 32;
-      const u4_t v0 = *reinterpret_cast<const u4_t *>(xa);
-      const u4_t v1 = *reinterpret_cast<const u4_t *>(xa + 16);
-      a0[tb] = arow ? v0 : z;
-      a1[tb] = arow ? v1 : z;
-      sa[tb] = scb[(gl * MP + 8 * tb + (rr >> 1)) * 4 + qa];
-    }
+    const char *xa = buf + (gl * 2 * MP + rr) * kRowBytes + qa * 32;
+    const u4_t v0 = *reinterpret_cast<const u4_t *>(xa);
+    const u4_t v1 = *reinterpret_cast<const u4_t *>(xa + 16);
+    const u4_t a0 = arow ? v0 : z;
+    const u4_t a1 = arow ? v1 : z;
+    const int sa = scb[(gl * MP + (rr >> 1)) * 4 + qa];
 #pragma unroll
     for (int r2 = 0; r2 < R; ++r2) {
       u4_t b;
       if constexpr (FMT == 1) b = q1_fp4(u.w[r2][gi]);
       else b = tq2_fp4(u.w[r2][2 * gi], u.w[r2][2 * gi + 1]);
       const float s = half_to_float(uint16_t(u.s[r2][gi >> 1] >> (16 * (gi & 1))));
+      const f4_t d = mfma_f8f4(a0, a1, b, sa);
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        const f4_t d = mfma_f8f4(a0[tb], a1[tb], b, sa[tb]);
+      for (int e = 0; e < 4; ++e) yacc[r2][0][e] = fmaf(s, d[e], yacc[r2][0][e]);
+    }
+  }
+}
+
+// The same at 16 tokens: lane 16qa + r reads the hi-piece row of token r, then
+// its lo-piece row; the two MFMAs of a (tile, group) share the weights and the
+// x scales and chain into one fp32 tile (token 4qa + e in element e), so the
+// group's FP16 scale takes one multiply-add per output instead of one per
+// piece.
+template <int FMT, int MP, int R>
+__device__ __forceinline__ void compute_chunk16(const SplitParams &p, const char *buf, const Unit<FMT, R> &u, int gb,
+                                                int ng, float (&yacc)[R][1][4]) {
+  const int lane = threadIdx.x & 63, qa = lane >> 4, r = lane & 15;
+  const uint8_t *scb = reinterpret_cast<const uint8_t *>(buf + p.GP * 2 * MP * kRowBytes);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) yacc[r2][tb][e] = fmaf(s, d[e], yacc[r2][tb][e]);
-      }
+  for (int gi = 0; gi < 4; ++gi) {
+    if (gi >= ng) break;  // wave-uniform: groups past K in the last chunk
+    const int gl = gb + gi;
+    const char *xh = buf + (gl * 2 * MP + r) * kRowBytes + qa * 32;
+    const char *xl = xh + MP * kRowBytes;
+    const u4_t h0 = *reinterpret_cast<const u4_t *>(xh);
+    const u4_t h1 = *reinterpret_cast<const u4_t *>(xh + 16);
+    const u4_t l0 = *reinterpret_cast<const u4_t *>(xl);
+    const u4_t l1 = *reinterpret_cast<const u4_t *>(xl + 16);
+    const int sa = scb[(gl * MP + r) * 4 + qa];
+#pragma unroll
+    for (int r2 = 0; r2 < R; ++r2) {
+      u4_t b;
+      if constexpr (FMT == 1) b = q1_fp4(u.w[r2][gi]);
+      else b = tq2_fp4(u.w[r2][2 * gi], u.w[r2][2 * gi + 1]);
+      const float s = half_to_float(uint16_t(u.s[r2][gi >> 1] >> (16 * (gi & 1))));
+      const f4_t d = mfma_f8f4_acc(l0, l1, b, sa, mfma_f8f4(h0, h1, b, sa));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yacc[r2][0][e] = fmaf(s, d[e], yacc[r2][0][e]);
     }
   }
 }
@@ -197,9 +226,9 @@ __device__ __forceinline__ void compute_chunk_ex(const SplitParams &p, const cha
 // the tile and its ragged shape per chunk).
 template <int FMT, int MP, int R, int MODE, bool FULL>
 __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p) {
-  // Accumulator sets per tile: fp4 A rows hold (token, piece) pairs, 8 tokens
-  // per MFMA; exact operands hold 16 tokens per MFMA.
-  constexpr int TB = MODE == kFp4 && MP > 8 ? 2 : 1;
+  // One fp32 tile per row tile: fp4 A rows hold (token, piece) pairs for up
+  // to 8 tokens, or at 16 tokens one token per row with the pieces chained;
+  // exact operands hold 16 tokens per MFMA.
   extern __shared__ __align__(16) char lds[];
   __shared__ int last_flag;
   const int wave = uni(threadIdx.x >> 6);
@@ -245,13 +274,11 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
   // The raw x of pass 1 goes out while pass 0 is multiplied.
   if (npass > 1) load_raw<MP>(p, raw, g0 + p.GP, min(p.GP, ng - p.GP), threadIdx.x, live);
 
-  float yacc[R][TB][4];
+  float yacc[R][1][4];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) yacc[r][tb][e] = 0.f;
+    for (int e = 0; e < 4; ++e) yacc[r][0][e] = 0.f;
 
   for (int c = 0; c < nchunks; c += 2) {
 #pragma unroll
@@ -270,25 +297,24 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
         }
         const char *cur = lds + (ps & 1) * p.buf_bytes;
         const int png = min(p.GP, ng - ps * p.GP);
-        if constexpr (MODE == kFp4) compute_chunk<FMT, MP, R, TB>(p, cur, ring[h], 4 * cl, min(4, png - 4 * cl), yacc);
+        if constexpr (MODE == kFp4 && MP > 8) compute_chunk16<FMT, MP, R>(p, cur, ring[h], 4 * cl, min(4, png - 4 * cl), yacc);
+        else if constexpr (MODE == kFp4) compute_chunk<FMT, MP, R>(p, cur, ring[h], 4 * cl, min(4, png - 4 * cl), yacc);
         else compute_chunk_ex<FMT, MP, R, MODE>(p, cur, ring[h], 4 * cl, min(4, png - 4 * cl), yacc);
       }
       load(ring[h], min(cc + 2, nchunks - 1));
     }
   }
 
-  // This lane's outputs: (tile r, token m, value).  fp4: element e of lane
-  // 16qa + j, token block tb, is A row 4qa + e (token 8 tb + 2 qa + e / 2,
-  // piece e % 2; the pieces add here); exact: token 4q + e.
+  // This lane's outputs: (tile r, token m, value).  fp4 up to 8 tokens:
+  // element e of lane 16qa + j is A row 4qa + e (token 2 qa + e / 2, piece
+  // e % 2; the pieces add here); fp4 at 16 tokens and exact: token 4q + e.
   const int j = lane & 15, qa = lane >> 4;
   auto each_output = [&](auto f) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if constexpr (MODE == kFp4) {
+      if constexpr (MODE == kFp4 && MP <= 8) {
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) f(r, 8 * tb + 2 * qa + tt, yacc[r][tb][2 * tt] + yacc[r][tb][2 * tt + 1]);
+        for (int tt = 0; tt < 2; ++tt) f(r, 2 * qa + tt, yacc[r][0][2 * tt] + yacc[r][0][2 * tt + 1]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) f(r, 4 * qa + e, yacc[r][0][e]);
