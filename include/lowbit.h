@@ -22,10 +22,11 @@
  *  multiple of 128.
  *
  * Blob ("packed weights"): headerless, exactly packed_bytes_lowbit(fmt,N,K)
- * bytes: plane A (signs / codes / trit bytes in the device layout v1, an
+ * bytes: plane A (signs / codes / trit bytes in the device layout v2, an
  * arrangement of the bits chosen for 128-bit coalesced loads and cheap
- * in-register decode) followed by plane B, the FP16 scale bit patterns
- * row-major [N][K/128].  pack_* writes it, unpack_lowbit inverts it exactly.
+ * in-register decode) followed by plane B, the N*K/128 FP16 scale bit
+ * patterns in the order of the kernels' units (16 rows x 4 groups, or 5 for
+ * tq5, contiguous).  pack_* writes it, unpack_lowbit inverts it exactly.
  *
  * Product: for m < M, n < N
  *     Y[m][n] = sum_k X[m][k] * t[n][k] * s[n][k/128]
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 3
+#define LOWBIT_ABI_VERSION 4
 
 typedef enum { LOWBIT_Q1_G128 = 1, LOWBIT_TQ2_G128 = 2, LOWBIT_TQ5_G128 = 3 } lowbit_format;
 typedef enum { LOWBIT_F16 = 1, LOWBIT_BF16 = 2, LOWBIT_F32 = 3 } lowbit_dtype;

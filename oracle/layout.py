@@ -19,10 +19,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
   invalid); a base-3 byte holds digits d_i = t_i + 1 little-endian
   (value = sum d_i 3^i, so a valid byte is 0..242);
 * the blob is headerless: plane A (signs / codes / trit bytes) followed by
-  plane B (the FP16 scales, row-major [N][K/128]); no padding.
+  plane B (the N*K/128 FP16 scales); no padding.
 
-Device layout v1 of plane A (the arrangement the GPU kernels read)
-------------------------------------------------------------------
+Device layout v2 (the arrangement the GPU kernels read)
+-------------------------------------------------------
+Plane A:
 Rows are cut into tiles of 16 (tile T holds rows 16T .. 16T+R_T-1,
 R_T = min(16, N-16T)); tiles are stored one after another.  Inside a tile the
 groups are cut into chunks of 4 (chunk c holds groups 4c .. 4c+G_c-1,
@@ -50,6 +51,14 @@ tq5: each row's K trits are cut into segments of 640 (5 groups) plus a tail
     byte ((q*R_T + j)*16 + w%16) of half-block w//16, where w = 8u + e and
     (u, q, e) come from b as above.  The tail segment of a tile is row-major:
     row j at R_T*128*S_full + j*B_tail.
+Plane B (FP16 values, index = 2-byte slot after plane A): the scales follow
+the units that read them.  Tile T holds the R_T*G scales of its rows from
+index 16*T*G on; inside it the groups are cut into chunks of W (W = 4 for q1
+and tq2, the chunks of plane A; W = 5 for tq5, its 640-trit segments), chunk
+c (G_c = min(W, G-W*c) groups) starts at R_T*W*c inside the tile and holds
+row j's G_c scales at j*G_c.  So the scale of (n, g) sits at
+    16*T*G + R_T*W*c + j*G_c + (g - W*c),   c = g // W,
+and the scales one unit (16 rows x one chunk) needs are contiguous.
 """
 from __future__ import annotations
 
@@ -148,6 +157,20 @@ def tq5_byte_digit(n, k, N: int, K: int):
     return np.where(full, off_full, off_tail), np.where(full, i_full, i_tail)
 
 
+def scale_chunk_groups(fmt: str) -> int:
+    return 5 if fmt == "tq5" else 4
+
+
+def scale_index(fmt: str, n, g, N: int, K: int):
+    """Index (in FP16 values) in plane B of the scale of row n, group g."""
+    G = n_groups(K)
+    W = scale_chunk_groups(fmt)
+    T, j, R = _tile(n, N)
+    c = g // W
+    Gc = np.minimum(W, G - W * c)
+    return 16 * T * G + R * W * c + j * Gc + (g - W * c)
+
+
 # ----------------------------------------------------------- pack/unpack ----
 def _row_blocks(N: int, rows_per_block: int = 1024):
     step = max(16, rows_per_block - rows_per_block % 16)
@@ -193,7 +216,12 @@ def pack(fmt: str, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
             acc = np.bincount((off - lo).ravel(), weights=contrib.ravel().astype(np.float64))
             val[lo:lo + acc.size] += np.rint(acc).astype(np.int64)
         plane[:] = val.astype(np.uint8)
-    return np.concatenate([plane, scales.reshape(-1).view(np.uint8)])
+    sc_plane = np.zeros(N * G, dtype=np.uint16)
+    gg = np.arange(G, dtype=np.int64)[None, :]
+    for n0, n1 in _row_blocks(N):
+        nn = np.arange(n0, n1, dtype=np.int64)[:, None]
+        sc_plane[scale_index(fmt, nn, gg, N, K)] = scales[n0:n1]
+    return np.concatenate([plane, sc_plane.view(np.uint8)])
 
 
 class FormatError(ValueError):
@@ -212,7 +240,8 @@ def unpack(fmt: str, blob, N: int, K: int, rows=None):
         raise FormatError("blob shorter than packed_bytes")
     rows = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     a_bytes = plane_a_bytes(fmt, N, K)
-    sc = blob[a_bytes:a_bytes + N * G * 2].view(np.uint16).reshape(N, G)[rows].copy()
+    sc_plane = blob[a_bytes:a_bytes + N * G * 2].view(np.uint16)
+    sc = sc_plane[scale_index(fmt, rows[:, None], np.arange(G, dtype=np.int64)[None, :], N, K)]
     codes = np.zeros((rows.size, K), dtype=np.int8)
     kk = np.arange(K, dtype=np.int64)[None, :]
     for r0 in range(0, rows.size, 1024):

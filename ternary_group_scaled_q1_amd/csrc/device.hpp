@@ -144,7 +144,7 @@ __device__ __forceinline__ u4_t tq2_fp4(uint32_t w0, uint32_t w1) {
 
 // Which in-group weight (8u + e: k = 32u + 8q + e for lane quarter q) feeds
 // fp4 nibble n of a lane's operand (the inverses of q1_fp4 / tq2_fp4 over the
-// bit positions of device layout v1).
+// bit positions of device layout v2).
 __device__ constexpr int fp4_src(int fmt, int n) {
   const int d = n / 8, i = n % 8;
   if (fmt == 1) {

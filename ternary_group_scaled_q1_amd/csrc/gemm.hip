@@ -84,11 +84,6 @@ struct GemmParams {
   int s_full, L_tail, b_tail, rowbytes;
 };
 
-__device__ __forceinline__ uint16_t load_scale(const GemmParams &p, int n, int g) {
-  const uint8_t *b = p.Sc + ((int64_t)n * p.G + g) * 2;
-  return uint16_t(b[0] | (uint16_t(b[1]) << 8));
-}
-
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -260,7 +255,8 @@ struct Feed {
   const uint8_t *wb[2];     // n-blocks H wm + i the wave loads: tile block start (tq5: + lane part)
   uint32_t wl[2];           // q1: 4 woff, tq2: 8 woff (woff = lane word index q RR + j)
   int RR[2];                // rows of the block (>= 1)
-  const uint8_t *scrow;     // this lane's scale row
+  const uint8_t *sctile;    // plane B start of this lane's scale tile
+  int sRR, sjj;             // that tile's rows, this lane's row in it
 };
 
 // Activation blocks (16 rows x one k-step, 1 KB) each wave loads per item:
@@ -298,7 +294,9 @@ __device__ __forceinline__ void feed_tile(const GemmParams &p, Feed<FMT> &f) {
     }
   }
   const ColBlock cs = col_block<FMT>(p, f.nt, wn, (nbw<FMT>() / 2) * wm + ((lane >> 4) % (nbw<FMT>() / 2)));
-  f.scrow = p.Sc + (int64_t)(16 * cs.T + min(j, cs.RR - 1)) * p.G * 2;
+  f.sctile = p.Sc + 32 * (int64_t)cs.T * p.G;
+  f.sRR = cs.RR;
+  f.sjj = min(j, cs.RR - 1);
 }
 
 template <int FMT>
@@ -343,7 +341,11 @@ __device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> 
       }
     }
   }
-  __builtin_amdgcn_global_load_lds((const void *)(f.scrow + 2 * g),
+  // Plane B: chunk sc of W groups (4; tq5: its 5-group segments) starts at
+  // RR W sc in the tile, the lane's row at sjj Gs.
+  constexpr int W = FMT == 3 ? 5 : 4;
+  const int sc = g / W, gs = g - W * sc, Gs = min(W, p.G - W * sc);
+  __builtin_amdgcn_global_load_lds((const void *)(f.sctile + 2 * (f.sRR * W * sc + f.sjj * Gs + gs)),
                                    (lds_void *)(wst + w_scale_off<FMT>() + wave * 256), 2, 0, 0);
   if constexpr (FMT == 3) {
     const int seg = g / 5;

@@ -1,5 +1,5 @@
 // Pieces shared by the GEMV kernels: wave-uniform values, the per-lane unit
-// of packed weights (R row tiles x one chunk of 4 groups in device layout v1)
+// of packed weights (R row tiles x one chunk of 4 groups in device layout v2)
 // and its branch-free load.
 #pragma once
 #include "device.hpp"
@@ -16,7 +16,7 @@ __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlan
 // a launch over several matrices that share x walks one tile range.
 struct MatSet {
   const uint8_t *W[kMaxMats];   // plane A
-  const uint16_t *Sc[kMaxMats];  // plane B: FP16 scales [N][G]
+  const uint16_t *Sc[kMaxMats];  // plane B: FP16 scales (unit order, layout.hpp)
   void *Y[kMaxMats];             // [M][N]
   int N[kMaxMats];
   int tile_end[kMaxMats];        // tiles of matrices 0..i; the total past the last
@@ -124,20 +124,22 @@ __device__ __forceinline__ void load_unit(const P &p, Unit<FMT, R> &u, int t0, i
     const TileRef tr = tile_ref(p.ms, uni(min(t0 + r, p.tiles - 1)));
     const int RT = uni(min(16, tr.N - 16 * tr.t));
     const uint8_t *blk = tr.W + 16 * (int64_t)tr.t * p.G * unit + (int64_t)RT * 4 * c * unit;
-    if (RT == 16 && Gc == 4 && (p.G & 3) == 0) {  // wave-uniform fast path
+    // The unit's scales: 16 T G + RT 4 c, row j at j Gc (plane B).
+    const uint16_t *sblk = tr.Sc + 16 * (int64_t)tr.t * p.G + RT * 4 * c;
+    if (RT == 16 && Gc == 4) {  // wave-uniform fast path
       const u4_t v0 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk) + lane);
       u.w[r][0] = v0.x; u.w[r][1] = v0.y; u.w[r][2] = v0.z; u.w[r][3] = v0.w;
       if constexpr (FMT == 2) {
         const u4_t v1 = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(blk + 1024) + lane);
         u.w[r][4] = v1.x; u.w[r][5] = v1.y; u.w[r][6] = v1.z; u.w[r][7] = v1.w;
       }
-      const u2_t sv = *reinterpret_cast<const u2_t *>(tr.Sc + (int64_t)(16 * tr.t + j) * p.G + 4 * c);
+      const u2_t sv = *reinterpret_cast<const u2_t *>(sblk + 4 * j);
       u.s[r][0] = sv.x; u.s[r][1] = sv.y;
     } else {
       const bool row_ok = j < RT;
       const int jj = min(j, RT - 1);
       const uint32_t *base = reinterpret_cast<const uint32_t *>(blk);
-      const uint16_t *srow = tr.Sc + (int64_t)(16 * tr.t + jj) * p.G + 4 * c;
+      const uint16_t *srow = sblk + jj * Gc;
       uint32_t h[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -164,8 +166,8 @@ __device__ __forceinline__ void load_unit(const P &p, Unit<FMT, R> &u, int t0, i
 
 // Addresses of the R row tiles of one tile set, resolved once per set rather
 // than once per unit: the (uniform) start of each tile's packed block and
-// each lane's row of scales.  Tiles past the launch resolve to the last
-// tile; their sums are never stored.
+// each lane's scales in the tile's first chunk.  Tiles past the launch
+// resolve to the last tile; their sums are never stored.
 template <int R>
 struct TileSet {
   const uint8_t *w[R];
@@ -180,7 +182,7 @@ __device__ __forceinline__ void resolve_tiles(const P &p, TileSet<R> &ts, int t0
   for (int r = 0; r < R; ++r) {
     const TileRef tr = tile_ref(p.ms, uni(min(t0 + r, p.tiles - 1)));
     ts.w[r] = tr.W + 16 * (int64_t)tr.t * p.G * unit;
-    ts.s[r] = tr.Sc + (int64_t)(16 * tr.t + j) * p.G;
+    ts.s[r] = tr.Sc + 16 * (int64_t)tr.t * p.G + 4 * j;
   }
 }
 
@@ -200,7 +202,7 @@ __device__ __forceinline__ void load_full(const TileSet<R> &ts, Unit<FMT, R> &u,
       const u4_t v1 = __builtin_nontemporal_load(wp + 64);
       u.w[r][4] = v1.x; u.w[r][5] = v1.y; u.w[r][6] = v1.z; u.w[r][7] = v1.w;
     }
-    const u2_t sv = *reinterpret_cast<const u2_t *>(ts.s[r] + 4 * c);
+    const u2_t sv = *reinterpret_cast<const u2_t *>(ts.s[r] + 64 * c);
     u.s[r][0] = sv.x; u.s[r][1] = sv.y;
   }
 }

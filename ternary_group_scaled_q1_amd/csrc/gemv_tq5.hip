@@ -3,7 +3,7 @@
 //
 // Base-3 packing stores 5 trits in a byte (cnblogs.com page, section 2.4),
 // 1.725 bits per weight against 2.125 for 2-bit slots, so the same HBM rate
-// streams 23% more weights.  In device layout v1 a row is cut into 640-trit
+// streams 23% more weights.  In device layout v2 a row is cut into 640-trit
 // segments (5 groups): byte w = 8u + e of lane (q, j)'s 32 segment bytes holds
 // the weight at in-group offset 32u + 8q + e of all five groups, digit i for
 // group i.  A unit of work is R row tiles x one segment: per tile a lane loads
@@ -86,12 +86,13 @@ __device__ __forceinline__ void t5_load(const T5Params &p, T5Unit<R> &u, int t0,
       u.a[r] = row_ok ? va : z;
       u.b[r] = row_ok ? vb : z;
     }
-    const uint16_t *srow = tr.Sc + (int64_t)(16 * tr.t + jj) * p.G;
+    // Plane B: the segment's scales start at 16 T G + RT 5 seg, row jj at jj Gs.
+    const int Gs = uni(min(5, p.G - 5 * seg));
+    const uint16_t *srow = tr.Sc + 16 * (int64_t)tr.t * p.G + RT * 5 * seg + jj * Gs;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
-      const int g = 5 * seg + i;
-      const uint16_t v = srow[min(g, p.G - 1)];
-      u.s[r][i] = row_ok && g < p.G ? v : uint16_t(0);
+      const uint16_t v = srow[min(i, Gs - 1)];
+      u.s[r][i] = row_ok && i < Gs ? v : uint16_t(0);
     }
   }
 }
@@ -335,8 +336,8 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
 }
 
 // Addresses of the R tiles of one tile set, resolved once per set: the
-// tile's start, the lane's row of scales and the tile's rows (tiles past the
-// launch resolve to the last tile; their sums are never stored).
+// tile's start in both planes and the tile's rows (tiles past the launch
+// resolve to the last tile; their sums are never stored).
 template <int R>
 struct T5Tiles {
   const uint8_t *w[R];
@@ -346,13 +347,12 @@ struct T5Tiles {
 
 template <int R>
 __device__ __forceinline__ void t5_resolve(const T5Params &p, T5Tiles<R> &ts, int t0) {
-  const int j = threadIdx.x & 15;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const TileRef tr = tile_ref(p.ms, uni(min(t0 + r, p.tiles - 1)));
     const int RT = uni(min(16, tr.N - 16 * tr.t));
     ts.w[r] = tr.W + 16 * (int64_t)tr.t * p.rowbytes;
-    ts.s[r] = tr.Sc + (int64_t)(16 * tr.t + min(j, RT - 1)) * p.G;
+    ts.s[r] = tr.Sc + 16 * (int64_t)tr.t * p.G;
     ts.rt[r] = RT;
   }
 }
@@ -362,13 +362,16 @@ __device__ __forceinline__ void t5_resolve(const T5Params &p, T5Tiles<R> &ts, in
 // (read by the per-weight path) re-reads the last full segment, or the
 // tile's first bytes when a row has no full segment (the scales plane
 // follows the packed bytes, so 32 bytes from a tile's start stay inside the
-// blob); rows past a ragged tile re-read its last row and groups past K the
-// last group's scale.  None of those values reaches a stored output.
+// blob); rows past a ragged tile re-read its last row, groups past K the
+// segment's last scale and units past the row its last segment's scales.
+// None of those values reaches a stored output.
 template <int R>
 __device__ __forceinline__ void t5_load_ts(const T5Params &p, const T5Tiles<R> &ts, T5Unit<R> &u, int seg) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, q = lane >> 4;
   const int sf = uni(max(min(seg, p.s_full - 1), 0));
+  const int ss = uni(max(min(seg, p.nseg - 1), 0));  // segment of the scales
+  const int Gs = uni(min(5, p.G - 5 * ss));
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int RT = ts.rt[r];
@@ -378,7 +381,7 @@ __device__ __forceinline__ void t5_load_ts(const T5Params &p, const T5Tiles<R> &
     u.a[r] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(sb));
     u.b[r] = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(sb + hb));
 #pragma unroll
-    for (int i = 0; i < 5; ++i) u.s[r][i] = ts.s[r][min(5 * seg + i, p.G - 1)];
+    for (int i = 0; i < 5; ++i) u.s[r][i] = ts.s[r][RT * 5 * ss + jj * Gs + min(i, Gs - 1)];
   }
 }
 

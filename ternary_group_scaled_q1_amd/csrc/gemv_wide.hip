@@ -49,9 +49,9 @@ struct WUnit {
   u4_t x[4];       // A operand of the four k-steps
 };
 
-// Per tile set: the tile starts (uniform) and each lane's scale row, resolved
-// once per set (tiles past the launch resolve to the last tile; their sums
-// are never stored).
+// Per tile set: the tile starts in both planes (uniform), resolved once per
+// set (tiles past the launch resolve to the last tile; their sums are never
+// stored).
 template <int R>
 struct WTiles {
   const uint8_t *w[R];
@@ -61,14 +61,13 @@ struct WTiles {
 
 template <int FMT, int R>
 __device__ __forceinline__ void resolve_wtiles(const WideParams &p, WTiles<R> &ts, int t0) {
-  const int j = threadIdx.x & 15;
   const int64_t unit = FMT == 1 ? 16 : 32;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const TileRef tr = tile_ref(p.ms, uni(min(t0 + r, p.tiles - 1)));
     const int RT = uni(min(16, tr.N - 16 * tr.t));
     ts.w[r] = tr.W + 16 * (int64_t)tr.t * p.G * unit;
-    ts.s[r] = tr.Sc + (int64_t)(16 * tr.t + min(j, RT - 1)) * p.G;
+    ts.s[r] = tr.Sc + 16 * (int64_t)tr.t * p.G;
     ts.rt[r] = RT;
   }
 }
@@ -104,7 +103,7 @@ __device__ __forceinline__ void load_wunit(const WideParams &p, const WTiles<R> 
       u.w[r][0] = w.x;
       u.w[r][1] = w.y;
     }
-    u.s[r] = ts.s[r][g];
+    u.s[r] = ts.s[r][RT * 4 * c + jj * Gc + gc];  // plane B: chunk c, row jj
   }
 }
 

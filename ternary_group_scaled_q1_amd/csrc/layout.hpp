@@ -1,4 +1,4 @@
-// Device layout v1 geometry, shared by the host packer and the HIP kernels.
+// Device layout v2 geometry, shared by the host packer and the HIP kernels.
 //
 // Plane A is cut into row tiles of 16 rows (R_T = min(16, N - 16T) rows in
 // tile T) and, inside a tile, into chunks of 4 groups of 128 weights
@@ -66,6 +66,21 @@ inline int64_t plane_a_bytes(int fmt, int64_t N, int64_t K) {
   if (fmt == 1) return N * K / 8;
   if (fmt == 2) return N * K / 4;
   return N * ((K + 4) / 5);
+}
+
+// Plane B, the FP16 scales after plane A, in the order of the units that read
+// them: tile T holds its R_T*G scales from index 16*T*G on; inside it the
+// groups are cut into chunks of W (4 for q1 / tq2: plane A's chunks; 5 for
+// tq5: its 640-trit segments), chunk c (G_c = min(W, G - W c) groups) starts
+// at R_T*W*c and holds row j's G_c scales at j*G_c.  The 16 rows x W scales
+// of a full unit are then one contiguous run of 16*W values.
+__host__ __device__ constexpr int scale_chunk_groups(int fmt) { return fmt == 3 ? 5 : 4; }
+
+__host__ __device__ inline int64_t scale_index(int64_t N, int64_t G, int W, int64_t n, int64_t g) {
+  const int64_t T = n / 16, j = n % 16, c = g / W;
+  const int64_t R = N - 16 * T < 16 ? N - 16 * T : 16;
+  const int64_t Gc = G - W * c < W ? G - W * c : W;
+  return 16 * T * G + R * W * c + j * Gc + (g - W * c);
 }
 
 }  // namespace lowbit

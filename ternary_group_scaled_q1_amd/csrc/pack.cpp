@@ -1,10 +1,11 @@
-// Host packer / unpacker: codes + FP16 scales <-> device layout v1 blob.
+// Host packer / unpacker: codes + FP16 scales <-> device layout v2 blob.
 //
 // Value maps: Binary g128 stores bit 1 for +scale and bit 0 for -scale
 // (lnrk.cn page, Binary g128 section); Ternary g128 stores t in {-1,0,+1}
 // either as the 2-bit code t + 1 (2-bit slots, ksqn.cn page) or as base-3
 // digits t + 1, five per byte (cnblogs.com page, section 2.4).  The
-// arrangement of bits is the device layout v1 described in layout.hpp.
+// arrangement of bits and scales is the device layout v2 described in
+// layout.hpp.
 #include <algorithm>
 #include <atomic>
 #include <cmath>
@@ -203,6 +204,28 @@ static bool unpack_tq5(const uint8_t *plane, const Geom &g, int8_t *codes) {
   return ok;
 }
 
+// Row-major scales [N][G] <-> plane B: row j's G_c scales of a chunk are
+// contiguous on both sides.  Plane B may be only 2-byte aligned (tq5).
+static void scatter_scales(int fmt, const Geom &g, const uint16_t *rows, uint8_t *pb) {
+  const int W = scale_chunk_groups(fmt);
+  parallel_for(g.N, [&](int64_t n) {
+    for (int64_t c = 0; c * W < g.G; ++c) {
+      const int64_t gc = std::min<int64_t>(W, g.G - W * c);
+      std::memcpy(pb + 2 * scale_index(g.N, g.G, W, n, W * c), rows + n * g.G + W * c, size_t(2 * gc));
+    }
+  });
+}
+
+static void gather_scales(int fmt, const Geom &g, const uint8_t *pb, uint16_t *rows) {
+  const int W = scale_chunk_groups(fmt);
+  parallel_for(g.N, [&](int64_t n) {
+    for (int64_t c = 0; c * W < g.G; ++c) {
+      const int64_t gc = std::min<int64_t>(W, g.G - W * c);
+      std::memcpy(rows + n * g.G + W * c, pb + 2 * scale_index(g.N, g.G, W, n, W * c), size_t(2 * gc));
+    }
+  });
+}
+
 static int check_fmt_shape(int fmt, int64_t N, int64_t K) {
   if (fmt < 1 || fmt > 3) return LOWBIT_ERR_ENUM;
   if (N < 0 || K < 0 || K % kGroup) return LOWBIT_ERR_SHAPE;
@@ -222,7 +245,7 @@ static int pack_any(int fmt, const int8_t *codes, const uint16_t *scales, int64_
   uint8_t *plane = static_cast<uint8_t *>(out);
   if (fmt == 3) pack_tq5(codes, g, plane);
   else pack_bits(fmt, [&](int64_t n, int64_t k) { return codes[n * K + k]; }, g, plane);
-  std::memcpy(plane + plane_a_bytes(fmt, N, K), scales, size_t(N * g.G * 2));
+  scatter_scales(fmt, g, scales, plane + plane_a_bytes(fmt, N, K));
   return LOWBIT_OK;
 }
 
@@ -333,7 +356,7 @@ int import_mlx_q1_g128(const uint32_t *wq, const void *scales, const void *biase
   uint8_t *plane = static_cast<uint8_t *>(out);
   pack_bits(1, [&](int64_t n, int64_t k) -> int8_t { return ((wq[n * words + k / 32] >> (k % 32)) & 1) ? 1 : -1; },
             g, plane);
-  std::memcpy(plane + plane_a_bytes(1, N, K), sc.data(), size_t(N * g.G * 2));
+  scatter_scales(1, g, sc.data(), plane + plane_a_bytes(1, N, K));
   return LOWBIT_OK;
 }
 
@@ -354,7 +377,7 @@ int unpack_lowbit(int fmt, const void *packed, int64_t packed_bytes, int64_t N, 
     if (fmt == 3) unpack_tq5(plane, g, codes_out);
     else unpack_bits(fmt, plane, g, codes_out);
   }
-  if (scales_out) std::memcpy(scales_out, plane + plane_a_bytes(fmt, N, K), size_t(N * g.G * 2));
+  if (scales_out) gather_scales(fmt, g, plane + plane_a_bytes(fmt, N, K), scales_out);
   return LOWBIT_OK;
 }
 

@@ -154,6 +154,22 @@ def test_golden_layout_positions():
         assert diff.tolist() == [byte], row
 
 
+def test_golden_scale_positions():
+    for row in _golden_rows("scale_positions.txt"):
+        fmt, N, K, n, g, want = row[0], int(row[1]), int(row[2]), int(row[3]), int(row[4]), int(row[6])
+        assert int(layout.scale_index(fmt, np.int64(n), np.int64(g), N, K)) == want, row
+        # and the scale really lands there: one distinct scale at (n, g)
+        G = K // 128
+        codes = np.full((N, K), -1 if fmt == "q1" else 0, np.int8)
+        sc = np.full((N, G), 0x3C00, np.uint16)
+        sc[n, g] = 0x4248
+        blob = layout.pack(fmt, codes, sc)
+        plane_b = blob[layout.plane_a_bytes(fmt, N, K):].view(np.uint16)
+        assert np.nonzero(plane_b != 0x3C00)[0].tolist() == [want], row
+        _, back = layout.unpack(fmt, blob, N, K)
+        assert np.array_equal(back, sc)
+
+
 SHAPES = [(1, 128), (2, 256), (15, 384), (16, 512), (17, 640), (31, 768), (33, 1152),
           (16, 1280), (5, 2048), (40, 896)]
 
@@ -176,6 +192,17 @@ def test_address_map_is_a_bijection(fmt):
             assert np.unique(key).size == N * K and off.min() >= 0 and off.max() < a
             # every byte is used by one row and the row's bytes are contiguous per tile
             assert np.unique(off).size == a
+        # plane B: every (row, group) has its own slot, and the scales of one
+        # unit (a tile's rows x one chunk of W groups) fill a contiguous range
+        G = K // 128
+        W = layout.scale_chunk_groups(fmt)
+        nn, gg = np.meshgrid(np.arange(N, dtype=np.int64), np.arange(G, dtype=np.int64), indexing="ij")
+        si = layout.scale_index(fmt, nn, gg, N, K)
+        assert np.array_equal(np.sort(si.ravel()), np.arange(N * G))
+        for T in range(-(-N // 16)):
+            for c in range(-(-G // W)):
+                blk = si[16 * T:16 * T + 16, W * c:W * c + W]
+                assert blk.max() - blk.min() + 1 == blk.size
 
 
 @pytest.mark.parametrize("fmt", layout.FORMATS)
