@@ -97,6 +97,11 @@ def gen_weights_gpu(torch, lb, fmt, layers, seed):
     return buf, offs
 
 
+def progress(msg):
+    """One line per set-up phase on stderr (the result line stays alone on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.print_source_digest:
@@ -120,6 +125,7 @@ def main():
     import ternary_group_scaled_q1_amd as lb
 
     lb.load()
+    progress("library loaded")
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -131,6 +137,7 @@ def main():
     layers = sweep_layers()
     weights = {f: gen_weights_gpu(torch, lb, f, layers, args.seed)
                for f in ("q1", "tq2") if args.only in (None, f"{f}_M1", f"{f}_M16")}
+    progress(f"weights packed on the GPU: {', '.join(weights) or 'none'}")
     gx = torch.Generator(device="cuda")
     gx.manual_seed(args.seed + 99)
     xs = {(m, K): torch.randn((m, K), device=dev, generator=gx).to(torch.bfloat16)
@@ -180,6 +187,7 @@ def main():
             sweep(fmt, m)
         graphs[(fmt, m)] = g
     torch.cuda.synchronize()
+    progress(f"sweep graphs captured: {len(graphs)}")
 
     # ------------------------------------------------------- prefill GEMMs
     gemm_data = {}
@@ -224,6 +232,7 @@ def main():
                 e1.record(stream)
                 ev[p].append((e0, e1))
 
+    progress("timing")
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
