@@ -340,15 +340,17 @@ def platform_probes(torch, dev):
 
 
 def _source_digest():
-    """sha256 over the kernel sources and the launch planner (any change to
-    them invalidates counters taken earlier)."""
+    """sha256 over the code of the kernel sources and the launch planner, with
+    line comments and blank lines left out (any change to the code
+    invalidates counters taken earlier; a change to a comment does not)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_group_scaled_q1_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                code = [ln.split("//", 1)[0].rstrip() for ln in f]
+            h.update(name.encode() + b"\0" + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()
 
 

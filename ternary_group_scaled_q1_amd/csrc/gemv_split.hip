@@ -28,8 +28,9 @@
 // counter, and the last workgroup reads only after it saw the count.
 //
 // Per (row tile, group) the weights decode to fp4 (q1: +-1, tq2: 2t) with a
-// shift and one bitwise op per 8 weights, one scaled 16x16x128 MFMA per
-// block of 8 tokens takes x as A rows (token, piece), and the group's FP16
+// shift and one bitwise op per 8 weights; up to 8 tokens one scaled
+// 16x16x128 MFMA takes x as A rows (token, piece), at 16 tokens two chained
+// MFMAs take the hi and then the lo pieces of all 16 tokens; the group's FP16
 // scale is applied to the fresh fp32 tile (exact products), as on the
 // aberweb.com page, section 4.1: the signs are decoded inside the kernel and
 // no dense weight tensor exists.
