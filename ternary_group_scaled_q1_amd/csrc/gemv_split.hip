@@ -4,7 +4,7 @@
 // operands on v_mfma_f32_16x16x32 with x staged in LDS as it is (the same
 // work split).
 //
-// A workgroup owns a row block (8 waves x R row tiles of 16 rows) and one
+// A workgroup owns a row block (8 or 12 waves x R row tiles of 16 rows) and one
 // K range of the matrix.  It converts the x of its K range once into LDS as
 // exact fp8 pieces with per-32 E8M0 scales (split_x_quarter in device.hpp),
 // in passes of GP groups that are double buffered: while the waves multiply
@@ -43,8 +43,9 @@ namespace lowbit {
 
 namespace {
 
+// Waves per workgroup: 8, or 12 for launches whose row tiles exceed 8 per CU
+// but not 12 (three tiles per SIMD instead of four at two tiles per wave).
 constexpr int kSWaves = 8;
-constexpr int kSThreads = 64 * kSWaves;
 
 struct SplitParams {
   MatSet ms;           // the matrices (row tiles numbered across them)
@@ -56,7 +57,7 @@ struct SplitParams {
   int GK;          // groups per K range (a multiple of 4 when KS > 1)
   int KS;          // K ranges
   int GP;          // groups per staging pass (a multiple of 4)
-  int row_blocks;  // ceil(tiles / (8 R))
+  int row_blocks;  // ceil(tiles / (NW R))
   int y_f16;
   int buf_bytes;   // LDS bytes of one staging buffer
 };
@@ -225,8 +226,9 @@ __device__ __forceinline__ void compute_chunk_ex(const SplitParams &p, const cha
 // are fixed for the launch, so their addresses are resolved once and each
 // chunk is one load per tile at a fixed stride (the general path resolves
 // the tile and its ragged shape per chunk).
-template <int FMT, int MP, int R, int MODE, bool FULL>
-__global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p) {
+template <int FMT, int MP, int R, int MODE, bool FULL, int NW>
+__global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(SplitParams p) {
+  constexpr int kThreads = 64 * NW;
   // One fp32 tile per row tile: fp4 A rows hold (token, piece) pairs for up
   // to 8 tokens, or at 16 tokens one token per row with the pieces chained;
   // exact operands hold 16 tokens per MFMA.
@@ -239,7 +241,7 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
   const int ng = uni(min(p.GK, p.G - g0));  // groups of this K range
   const int nchunks = (ng + 3) / 4;
   const int c0 = g0 / 4;
-  const int t0 = uni(rb * 8 * R + wave * R);
+  const int t0 = uni(rb * NW * R + wave * R);
   const float mul = FMT == 1 ? 1.f : 0.5f;  // ternary operands carry 2t
 
   // x of pass 0 is loaded first, then the first two chunks of weights, so
@@ -348,16 +350,16 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
   // loads of 4 ranges for each of 4 outputs before it adds any of them
   // (addresses clamped, values past KS unused) instead of paying that latency
   // once per range.
-  const int n0 = rb * 8 * R * 16;
-  const int rows = min(8 * R * 16, p.NV - n0);
+  const int n0 = rb * NW * R * 16;
+  const int rows = min(NW * R * 16, p.NV - n0);
   const int outs = p.M * rows;
   constexpr int kOut = 4, kRanges = 4;
-  for (int base = 0; base < outs; base += kOut * kSThreads) {
+  for (int base = 0; base < outs; base += kOut * kThreads) {
     int pm[kOut], pn[kOut];
     float v[kOut];
 #pragma unroll
     for (int o = 0; o < kOut; ++o) {
-      const int idx = min(base + o * kSThreads + int(threadIdx.x), outs - 1);
+      const int idx = min(base + o * kThreads + int(threadIdx.x), outs - 1);
       pm[o] = idx / rows;
       pn[o] = n0 + idx % rows;
       v[o] = 0.f;
@@ -378,16 +380,17 @@ __global__ void __launch_bounds__(kSThreads, 2) gemv_split_kernel(SplitParams p)
     }
 #pragma unroll
     for (int o = 0; o < kOut; ++o)
-      if (base + o * kSThreads + int(threadIdx.x) < outs) store_y(tile_ref(p.ms, pn[o] >> 4), pn[o] & 15, pm[o], v[o] * mul, p.y_f16);
+      if (base + o * kThreads + int(threadIdx.x) < outs) store_y(tile_ref(p.ms, pn[o] >> 4), pn[o] & 15, pm[o], v[o] * mul, p.y_f16);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Largest pass (groups, a multiple of 4) whose x fits in one item per thread
-// and whose two buffers fit in 64 KB of LDS.
-inline int pass_groups(int MP, int G, int MODE) {
+// and whose two buffers fit in 80 KB of LDS (two workgroups per CU fit in
+// the 160 KB of a gfx950 CU).
+inline int pass_groups(int MP, int G, int MODE, int threads) {
   int gp = 4;
-  while (gp + 4 <= 128 && MP * (gp + 4) * 4 <= kSThreads && 2 * split_buf_bytes(MP, gp + 4, MODE) <= 66 * 1024) gp += 4;
+  while (gp + 4 <= 128 && MP * (gp + 4) * 4 <= threads && 2 * split_buf_bytes(MP, gp + 4, MODE) <= 80 * 1024) gp += 4;
   const int g4 = (G + 3) / 4 * 4;
   return gp < g4 ? gp : g4;
 }
@@ -416,7 +419,7 @@ struct SplitPlan {
 // Parameters of the launch with R row tiles per wave and K cut into ranges
 // of gk groups (false if the workspace, the partial-sum area or the counters
 // cannot hold that cut).
-template <int FMT, int MP, int R, int MODE, bool FULL>
+template <int FMT, int MP, int R, int MODE, bool FULL, int NW>
 bool make_split(const LaunchArgs &a, int gk, SplitPlan &pl) {
   SplitParams p{};
   p.ms = mat_set(a);
@@ -425,8 +428,8 @@ bool make_split(const LaunchArgs &a, int gk, SplitPlan &pl) {
   p.tiles = int((a.N + 15) / 16);
   p.NV = 16 * p.tiles;
   p.y_f16 = a.y_f16;
-  p.row_blocks = (p.tiles + 8 * R - 1) / (8 * R);
-  p.GP = pass_groups(MP, p.G, MODE);
+  p.row_blocks = (p.tiles + NW * R - 1) / (NW * R);
+  p.GP = pass_groups(MP, p.G, MODE, 64 * NW);
   p.buf_bytes = split_buf_bytes(MP, p.GP, MODE);
   gk = gk < p.G ? gk : p.G;
   const int KS = (p.G + gk - 1) / gk;
@@ -447,43 +450,54 @@ bool make_split(const LaunchArgs &a, int gk, SplitPlan &pl) {
 // time is a fixed part (x staging, the K-range reduction, launch) plus a
 // part per group of its K range.  So: the fewest row tiles per wave whose
 // row blocks fit one per CU, then the most K ranges that keep the grid
-// within the CUs (each range shortens every workgroup).  Matrices too tall
-// for that take two tiles per wave and the whole of K (fewer rows per wave
-// would only add waves that wait their turn; more hold too many registers).
+// within the CUs (each range shortens every workgroup).  Between 8 and 12
+// row tiles per CU a workgroup of 12 waves with one tile each keeps three
+// tiles per SIMD where 8 waves of two tiles would hold four.  Matrices too
+// tall for that take two tiles per wave and the whole of K (fewer rows per
+// wave would only add waves that wait their turn; more hold too many
+// registers).
 template <int FMT, int MP, int MODE, bool FULL>
 hipError_t launch_split_full(const LaunchArgs &a) {
   const int cus = num_cus();
   const int tiles = int((a.N + 15) / 16), G = int(a.K / kGroup);
-  const int R = (tiles + 7) / 8 <= cus ? 1 : ((tiles + 15) / 16 <= cus ? 2 : ((tiles + 31) / 32 <= cus ? 4 : 2));
-  const int blocks = (tiles + 8 * R - 1) / (8 * R);
+  int NW = kSWaves, R = 1;
+  if ((tiles + 7) / 8 <= cus) R = 1;
+  else if ((tiles + 11) / 12 <= cus) NW = 12;
+  else R = (tiles + 15) / 16 <= cus ? 2 : ((tiles + 31) / 32 <= cus ? 4 : 2);
+  const int blocks = (tiles + NW * R - 1) / (NW * R);
   SplitPlan pl;
+  auto make = [&](int gk) {
+    if (NW == 12) return make_split<FMT, MP, 1, MODE, FULL, 12>(a, gk, pl);
+    if (R == 1) return make_split<FMT, MP, 1, MODE, FULL, kSWaves>(a, gk, pl);
+    if (R == 2) return make_split<FMT, MP, 2, MODE, FULL, kSWaves>(a, gk, pl);
+    return make_split<FMT, MP, 4, MODE, FULL, kSWaves>(a, gk, pl);
+  };
   bool ok = false;
   if (blocks <= cus) {
     // Most ranges first: gk = 4, 8, ... groups (a multiple of 4).
     for (int gk = 4; gk < G + 4 && !ok; gk += 4) {
       const int ks = (G + gk - 1) / gk;
       if ((int64_t)blocks * ks > cus && gk < G) continue;
-      if (R == 1) ok = make_split<FMT, MP, 1, MODE, FULL>(a, gk, pl);
-      else if (R == 2) ok = make_split<FMT, MP, 2, MODE, FULL>(a, gk, pl);
-      else ok = make_split<FMT, MP, 4, MODE, FULL>(a, gk, pl);
+      ok = make(gk);
     }
   } else {
-    ok = make_split<FMT, MP, 2, MODE, FULL>(a, G, pl);
+    R = 2;
+    ok = make(G);
   }
   if (!ok) return hipErrorInvalidValue;
   if (pl.p.KS > 1) {
     pl.p.count = static_cast<unsigned *>(a.ws);
     pl.p.part = reinterpret_cast<float *>(static_cast<char *>(a.ws) + kPartOffset);
   }
-  if (R == 1)
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL>), dim3(pl.grid), dim3(kSThreads), pl.lds, a.stream,
-                       pl.p);
+  const dim3 grid(pl.grid), block(64 * NW);
+  if (NW == 12)
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL, 12>), grid, block, pl.lds, a.stream, pl.p);
+  else if (R == 1)
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL, kSWaves>), grid, block, pl.lds, a.stream, pl.p);
   else if (R == 2)
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2, MODE, FULL>), dim3(pl.grid), dim3(kSThreads), pl.lds, a.stream,
-                       pl.p);
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2, MODE, FULL, kSWaves>), grid, block, pl.lds, a.stream, pl.p);
   else
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4, MODE, FULL>), dim3(pl.grid), dim3(kSThreads), pl.lds, a.stream,
-                       pl.p);
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4, MODE, FULL, kSWaves>), grid, block, pl.lds, a.stream, pl.p);
   return hipGetLastError();
 }
 
