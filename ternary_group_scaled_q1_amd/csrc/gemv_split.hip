@@ -34,6 +34,8 @@
 // scale is applied to the fresh fp32 tile (exact products), as on the
 // aberweb.com page, section 4.1: the signs are decoded inside the kernel and
 // no dense weight tensor exists.
+#include <type_traits>
+
 #include "device.hpp"
 #include "gemv_common.hpp"
 #include "kernels.hpp"
@@ -347,41 +349,48 @@ __global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(Sp
   if (!last_flag) return;
   // Last workgroup of the block: Y = sum over ranges in range order.  The
   // partials come from the device's coherence point, so a thread issues the
-  // loads of 4 ranges for each of 4 outputs before it adds any of them
+  // loads of KR ranges for each of 4 outputs before it adds any of them
   // (addresses clamped, values past KS unused) instead of paying that latency
-  // once per range.
+  // once per range; KR = 4 up to 4 ranges (no duplicate loads for the common
+  // 2 or 3), else 8.
   const int n0 = rb * NW * R * 16;
   const int rows = min(NW * R * 16, p.NV - n0);
   const int outs = p.M * rows;
-  constexpr int kOut = 4, kRanges = 4;
-  for (int base = 0; base < outs; base += kOut * kThreads) {
-    int pm[kOut], pn[kOut];
-    float v[kOut];
+  constexpr int kOut = 4;
+  auto reduce = [&](auto kr) {
+    constexpr int KR = decltype(kr)::value;
+    for (int base = 0; base < outs; base += kOut * kThreads) {
+      int pm[kOut], pn[kOut];
+      float v[kOut];
 #pragma unroll
-    for (int o = 0; o < kOut; ++o) {
-      const int idx = min(base + o * kThreads + int(threadIdx.x), outs - 1);
-      pm[o] = idx / rows;
-      pn[o] = n0 + idx % rows;
-      v[o] = 0.f;
-    }
-    for (int k0 = 0; k0 < p.KS; k0 += kRanges) {
-      float pv[kOut][kRanges];
+      for (int o = 0; o < kOut; ++o) {
+        const int idx = min(base + o * kThreads + int(threadIdx.x), outs - 1);
+        pm[o] = idx / rows;
+        pn[o] = n0 + idx % rows;
+        v[o] = 0.f;
+      }
+      for (int k0 = 0; k0 < p.KS; k0 += KR) {
+        float pv[kOut][KR];
+#pragma unroll
+        for (int o = 0; o < kOut; ++o)
+#pragma unroll
+          for (int k = 0; k < KR; ++k)
+            pv[o][k] = __hip_atomic_load(p.part + ((int64_t)min(k0 + k, p.KS - 1) * p.M + pm[o]) * p.NV + pn[o],
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int o = 0; o < kOut; ++o)
+#pragma unroll
+          for (int k = 0; k < KR; ++k)
+            if (k0 + k < p.KS) v[o] += pv[o][k];
+      }
 #pragma unroll
       for (int o = 0; o < kOut; ++o)
-#pragma unroll
-        for (int k = 0; k < kRanges; ++k)
-          pv[o][k] = __hip_atomic_load(p.part + ((int64_t)min(k0 + k, p.KS - 1) * p.M + pm[o]) * p.NV + pn[o],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int o = 0; o < kOut; ++o)
-#pragma unroll
-        for (int k = 0; k < kRanges; ++k)
-          if (k0 + k < p.KS) v[o] += pv[o][k];
+        if (base + o * kThreads + int(threadIdx.x) < outs)
+          store_y(tile_ref(p.ms, pn[o] >> 4), pn[o] & 15, pm[o], v[o] * mul, p.y_f16);
     }
-#pragma unroll
-    for (int o = 0; o < kOut; ++o)
-      if (base + o * kThreads + int(threadIdx.x) < outs) store_y(tile_ref(p.ms, pn[o] >> 4), pn[o] & 15, pm[o], v[o] * mul, p.y_f16);
-  }
+  };
+  if (p.KS <= 4) reduce(std::integral_constant<int, 4>{});
+  else reduce(std::integral_constant<int, 8>{});
   if (threadIdx.x == 0) __hip_atomic_store(p.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
