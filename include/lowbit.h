@@ -173,17 +173,24 @@ int gemv_multi_lowbit(int fmt, int count, const void *const *Ws, const int64_t *
  * (tile, 128-weight group) work items are cut into one contiguous range per
  * workgroup slot, and tiles split between two ranges are summed through this
  * memory (64 KiB of arrival counters, then two fp32 output tiles per slot:
- * 128 x 256 for q1 and tq2, 128 x 128 for tq5).  Depends on the format and
- * on the device's compute-unit count (256 assumed when no device is
- * visible).  Returns a negative status on a bad format or shape. */
+ * 128 x 256 for q1 and tq2, 128 x 128 for tq5).  For q1 it also holds bf16 x
+ * converted once per call into two fp8 pieces per value with one power-of-two
+ * scale per 32 values (2 bytes + 1/32 byte per value of x padded to 128-row
+ * tiles), which the q1 kernel multiplies against fp4 +-1 weights: that is
+ * exact for every value within 2^7 of its 32-value block's largest, and
+ * keeps the error below 2^-12 of the bound's sum otherwise.  Depends on the
+ * format, on M and K for q1, and on the device's compute-unit count (256
+ * assumed when no device is visible).  Returns a negative status on a bad
+ * format or shape. */
 int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* Prefill GEMM: Y = X W^T for large batches (M = prompt tokens).  Same
  * arguments and rules as gemv_lowbit, including the workspace: caller-owned,
  * 16-byte aligned, zero-filled before its first use (every call leaves its
  * counters zero again), one per concurrently running call.  With at least
- * gemm_workspace_bytes_lowbit() bytes the work is balanced across the chip;
- * with less, or NULL, each workgroup takes whole tiles.  Results are
+ * gemm_workspace_bytes_lowbit() bytes the work is balanced across the chip
+ * (and q1 with bf16 x takes the fp8-piece path); with less, or NULL, each
+ * workgroup takes whole tiles with exact bf16 operands.  Results are
  * deterministic for a given workspace size either way. */
 int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype,
                 int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,

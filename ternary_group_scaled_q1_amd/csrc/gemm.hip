@@ -71,6 +71,8 @@ struct GemmParams {
   const uint8_t *W;
   const uint8_t *Sc;  // plane B (may be only 2-byte aligned for tq5)
   const uint16_t *X;
+  const uint8_t *XP;  // fp8 x pieces (q1, bf16 x): [tile_m][group] 32 KB blocks
+  const uint8_t *XS;  // their E8M0 scales: [tile_m][group][row block] 64 bytes
   void *Y;
   float *part;      // [slot][2] pieces of split tiles (stream-K)
   unsigned *count;  // [tiles] arrival counters
@@ -141,9 +143,13 @@ constexpr int w_scale_off() { return nwn<FMT>() * nbw<FMT>() * w_words<FMT>() * 
 template <int FMT>
 constexpr int w_raw_off() { return w_scale_off<FMT>() + 2 * nwn<FMT>() * 256; }
 
+// q1 with fp8 x pieces: the item's 512 E8M0 x scales (8 row blocks x 64).
+template <int FMT>
+constexpr int w_xscale_off() { return w_raw_off<FMT>() + (FMT == 3 ? kRawBytes : 0); }
+
 template <int FMT>
 constexpr int w_stage_bytes() {
-  return w_scale_off<FMT>() + 2 * nwn<FMT>() * 256 + (FMT == 3 ? kRawBytes : 0);
+  return w_xscale_off<FMT>() + (FMT == 1 ? 512 : 0);
 }
 
 template <int FMT>
@@ -192,6 +198,40 @@ __device__ __forceinline__ void group_mma(const char *st, const float (&sc)[nbw<
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[mb][nb][e] = fmaf(sc[nb], cg[mb][nb][e], acc[mb][nb][e]);
+}
+
+// q1 with fp8 x pieces: one group on v_mfma_scale_f32_16x16x128_f8f6f4.
+// Row block mb of stage st is four 1 KB blocks (hi piece halves 0 and 1, lo
+// piece halves 0 and 1; lane l's 16 bytes at 16 l), its E8M0 scales 64
+// bytes of the weight stage (lane 16 kb + r: row r, k-block kb).  The
+// weights decode to fp4 +-1 (q1_fp4) once per n-block; the hi and lo MFMAs
+// of a (row block, n-block) chain into one fresh tile that is added as
+// s * tile, as in the bf16 path.
+template <int FMT>
+__device__ __forceinline__ void group_mma_xp(const char *st, const char *wst, const float (&sc)[nbw<FMT>()],
+                                             const uint32_t (&wd)[nbw<FMT>()][2], f4_t (&acc)[4][nbw<FMT>()]) {
+  constexpr int NB = nbw<FMT>();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / nwn<FMT>();
+  u4_t b[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) b[nb] = q1_fp4(wd[nb][0]);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int rb = wm * 4 + mb;
+    const char *blk = st + rb * 4096 + lane * 16;
+    const u4_t h0 = *reinterpret_cast<const u4_t *>(blk);
+    const u4_t h1 = *reinterpret_cast<const u4_t *>(blk + 1024);
+    const u4_t l0 = *reinterpret_cast<const u4_t *>(blk + 2048);
+    const u4_t l1 = *reinterpret_cast<const u4_t *>(blk + 3072);
+    const int sa = *reinterpret_cast<const uint8_t *>(wst + w_xscale_off<FMT>() + rb * 64 + lane);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const f4_t d = mfma_f8f4_acc(l0, l1, b[nb], sa, mfma_f8f4(h0, h1, b[nb], sa));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[mb][nb][e] = fmaf(sc[nb], d[e], acc[mb][nb][e]);
+    }
+  }
 }
 
 template <int FMT>
@@ -314,8 +354,10 @@ __device__ __forceinline__ void feed_next(const GemmParams &p, Feed<FMT> &f) {
 
 // All loads of item f into activation stage xst and weight stage wst:
 // weights first, then the XB activation loads of the wave.  tq5 loads the
-// raw bytes of a segment only with `raw` (the item that decodes them).
-template <int FMT>
+// raw bytes of a segment only with `raw` (the item that decodes them).  XP:
+// the activations are the item's 32 KB block of fp8 x pieces (the same 32
+// 1 KB blocks per item), and waves 0 and 1 first load its 512 x scales.
+template <int FMT, bool XP>
 __device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> &f, char *xst, char *wst, bool raw) {
   constexpr int XB = x_blocks<FMT>();
   const int wave = uni(threadIdx.x >> 6);
@@ -362,13 +404,26 @@ __device__ __forceinline__ void feed_issue(const GemmParams &p, const Feed<FMT> 
       }
     }
   }
+  if constexpr (XP) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)f.mt * p.G + g;
+    if (wave < 2)
+      __builtin_amdgcn_global_load_lds((const void *)(p.XS + item * 512 + wave * 256 + lane * 4),
+                                       (lds_void *)(wst + w_xscale_off<FMT>() + wave * 256), 4, 0, 0);
+    const uint8_t *xb = p.XP + item * 32768 + lane * 16;
 #pragma unroll
-  for (int i = 0; i < XB; ++i)
-    __builtin_amdgcn_global_load_lds((const void *)(f.xrow[i >> 2] + 128 * g + 32 * (i & 3)),
-                                     (lds_void *)(xst + (wave * XB + i) * 1024), 16, 0, 0);
+    for (int i = 0; i < XB; ++i)
+      __builtin_amdgcn_global_load_lds((const void *)(xb + (wave * XB + i) * 1024),
+                                       (lds_void *)(xst + (wave * XB + i) * 1024), 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < XB; ++i)
+      __builtin_amdgcn_global_load_lds((const void *)(f.xrow[i >> 2] + 128 * g + 32 * (i & 3)),
+                                       (lds_void *)(xst + (wave * XB + i) * 1024), 16, 0, 0);
+  }
 }
 
-template <int FMT, bool BF>
+template <int FMT, bool BF, bool XP>
 __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
   extern __shared__ __align__(16) char xs[];  // kStages x (activations, then weights)
   __shared__ uint16_t lut[256];
@@ -438,9 +493,9 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
   feed_tile<FMT>(p, feed);
   int feed_it = 0;
   auto raw_for = [&]() { return FMT == 3 && (feed_it == 0 || feed.g % 5 == 0); };
-  feed_issue<FMT>(p, feed, xs, wring, raw_for());
+  feed_issue<FMT, XP>(p, feed, xs, wring, raw_for());
   if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
-  feed_issue<FMT>(p, feed, xs + kStageBytes, wring + kW, raw_for());
+  feed_issue<FMT, XP>(p, feed, xs + kStageBytes, wring + kW, raw_for());
   if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
 
   auto step = [&](int it, int slot) {
@@ -472,7 +527,7 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
     // above, and this wave's reads of the stage refilled below were consumed
     // by its MFMAs of the previous item.
     __builtin_amdgcn_s_barrier();
-    feed_issue<FMT>(p, feed, xs + ((slot + 2) % kStages) * kStageBytes, wring + ((slot + 2) % kStages) * kW,
+    feed_issue<FMT, XP>(p, feed, xs + ((slot + 2) % kStages) * kStageBytes, wring + ((slot + 2) % kStages) * kW,
                     raw_for());
     if (feed_it + 1 < n) { feed_next<FMT>(p, feed); ++feed_it; }
     const char *st = xs + slot * kStageBytes;
@@ -486,10 +541,14 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int h = 0; h < w_words<FMT>(); ++h) wd[nb][h] = w_word<FMT>(wst, nb, h);
-      group_mma<FMT, BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
-        if constexpr (FMT == 1) return q1_operand_pm1<BF>(wd[nb][0], u);
-        else return tq2_operand(wd[nb][u >> 1], u);
-      });
+      if constexpr (XP) {
+        group_mma_xp<FMT>(st, wst, sc, wd, acc);
+      } else {
+        group_mma<FMT, BF>(st, sc, acc, [&](int u, int nb) -> u4_t {
+          if constexpr (FMT == 1) return q1_operand_pm1<BF>(wd[nb][0], u);
+          else return tq2_operand(wd[nb][u >> 1], u);
+        });
+      }
     } else {
       const int seg = g / 5, gs = g - 5 * seg;
       if (seg < p.s_full) {
@@ -586,6 +645,47 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
 
 int stream_k_slots() { return num_cus(); }
 
+// fp8 x pieces for the q1 GEMM with bf16 x, converted once per launch:
+// thread = item (row m of the padded token tiles, group g, lane quarter q),
+// the 32 values x[m][128 g + 32 u + 8 q + e] (u < 4, e < 8) as two e4m3
+// pieces and one E8M0 scale (split_x_quarter; rows past M are zeros).  They
+// form k-block q of the A operand of row r = m % 16 in row block mb =
+// (m % 128) / 16 of token tile mt: the first 16 bytes of each piece go to
+// lane 16 (2 (q & 1)) + r, the second 16 to the lane 16 above it, both in
+// half q / 2 of that lane's 32 bytes; the scale is byte 16 q + r of the row
+// block's 64.  Layout: XP [mt][g][mb][piece][half] 1 KB blocks (lane l at
+// 16 l), XS [mt][g][mb] 64 bytes.
+__global__ void x_pieces_kernel(const uint16_t *X, int M, int K, int G, int64_t items, uint8_t *XP, uint8_t *XS) {
+  const int64_t item = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (item >= items) return;
+  const int q = int(item & 3);
+  const int64_t rest = item >> 2;
+  const int g = int(rest % G);
+  const int m = int(rest / G);
+  const bool in = m < M;
+  XQuarter xq;
+  split_x_quarter<1>(X + (in ? (int64_t)m * K + 128 * g + 8 * q : 0), in, xq);
+  const int mt = m >> 7, mb = (m >> 4) & 7, r = m & 15;
+  const int64_t blk = (int64_t)mt * G + g;
+  uint8_t *b = XP + blk * 32768 + mb * 4096 + (q >> 1) * 1024;
+  const int l0 = 16 * (2 * (q & 1)) + r, l1 = l0 + 16;
+  *reinterpret_cast<u4_t *>(b + l0 * 16) = xq.h0;
+  *reinterpret_cast<u4_t *>(b + l1 * 16) = xq.h1;
+  *reinterpret_cast<u4_t *>(b + 2048 + l0 * 16) = xq.l0;
+  *reinterpret_cast<u4_t *>(b + 2048 + l1 * 16) = xq.l1;
+  XS[(blk * 8 + mb) * 64 + 16 * q + r] = xq.sb;
+}
+
+int64_t x_pieces_bytes(int64_t M, int64_t K) {
+  return (M + kBM - 1) / kBM * (K / kGroup) * (32768 + 512);
+}
+
+// Workspace offset of the x pieces: after the stream-K counters and pieces.
+template <int FMT>
+int64_t x_pieces_offset() {
+  return (kCounterBytes + (int64_t)stream_k_slots() * 2 * piece_floats<FMT>() * 4 + 255) / 256 * 256;
+}
+
 template <int FMT, bool BF>
 hipError_t launch_t(const LaunchArgs &a) {
   GemmParams p{};
@@ -616,14 +716,29 @@ hipError_t launch_t(const LaunchArgs &a) {
     grid = int(tiles);
   }
   const int lds = kStages * (kStageBytes + w_stage_bytes<FMT>());
-  hipLaunchKernelGGL((gemm_kernel<FMT, BF>), dim3(grid), dim3(threads_of<FMT>()), lds, a.stream, p);
+  if constexpr (FMT == 1 && BF) {
+    // Binary weights with bf16 x: x enters as fp8 pieces when the workspace
+    // holds them (exact enough for binary weights: see the GEMV split path).
+    const int64_t off = x_pieces_offset<FMT>();
+    if (a.ws && a.ws_bytes >= off + x_pieces_bytes(a.M, a.K)) {
+      p.XP = static_cast<const uint8_t *>(a.ws) + off;
+      p.XS = p.XP + (int64_t)p.tiles_m * p.G * 32768;
+      const int64_t items = (int64_t)p.tiles_m * kBM * p.G * 4;
+      hipLaunchKernelGGL(x_pieces_kernel, dim3(unsigned((items + 255) / 256)), dim3(256), 0, a.stream, p.X, p.M,
+                         p.K, p.G, items, const_cast<uint8_t *>(p.XP), const_cast<uint8_t *>(p.XS));
+      hipLaunchKernelGGL((gemm_kernel<FMT, BF, true>), dim3(grid), dim3(threads_of<FMT>()), lds, a.stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<FMT, BF, false>), dim3(grid), dim3(threads_of<FMT>()), lds, a.stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N; (void)K;
+  (void)N;
+  if (fmt == 1) return x_pieces_offset<1>() + x_pieces_bytes(M, K);  // + fp8 x pieces (bf16 x)
   const int64_t piece = fmt == 3 ? piece_floats<3>() : piece_floats<1>();
   return kCounterBytes + (int64_t)stream_k_slots() * 2 * piece * 4;
 }
