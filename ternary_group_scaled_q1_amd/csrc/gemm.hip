@@ -654,19 +654,20 @@ int stream_k_slots() { return num_cus(); }
 // lane 16 (2 (q & 1)) + r, the second 16 to the lane 16 above it, both in
 // half q / 2 of that lane's 32 bytes; the scale is byte 16 q + r of the row
 // block's 64.  Layout: XP [mt][g][mb][piece][half] 1 KB blocks (lane l at
-// 16 l), XS [mt][g][mb] 64 bytes.
+// 16 l), XS [mt][g][mb] 64 bytes.  A wave takes the 64 items (q, r) of one
+// (mt, g, mb), so each of its stores fills whole 256-byte runs.
 __global__ void x_pieces_kernel(const uint16_t *X, int M, int K, int G, int64_t items, uint8_t *XP, uint8_t *XS) {
   const int64_t item = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (item >= items) return;
-  const int q = int(item & 3);
-  const int64_t rest = item >> 2;
-  const int g = int(rest % G);
-  const int m = int(rest / G);
+  const int r = int(item & 15), q = int((item >> 4) & 3);
+  const int64_t rest = item >> 6;
+  const int mb = int(rest & 7);
+  const int64_t blk = rest >> 3;  // mt * G + g
+  const int g = int(blk % G), mt = int(blk / G);
+  const int m = mt * 128 + mb * 16 + r;
   const bool in = m < M;
   XQuarter xq;
   split_x_quarter<1>(X + (in ? (int64_t)m * K + 128 * g + 8 * q : 0), in, xq);
-  const int mt = m >> 7, mb = (m >> 4) & 7, r = m & 15;
-  const int64_t blk = (int64_t)mt * G + g;
   uint8_t *b = XP + blk * 32768 + mb * 4096 + (q >> 1) * 1024;
   const int l0 = 16 * (2 * (q & 1)) + r, l1 = l0 + 16;
   *reinterpret_cast<u4_t *>(b + l0 * 16) = xq.h0;
