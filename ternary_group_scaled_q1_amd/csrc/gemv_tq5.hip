@@ -609,68 +609,47 @@ hipError_t launch_tq5_x(const LaunchArgs &a) {
   return hipGetLastError();
 }
 
-// Plan of the one-token kernel, with the cost the other decode kernels use
-// (from timings on MI355X): a workgroup costs its waves' units (segments;
-// one more per tile set when waves split K) plus a fixed part worth about
-// two, and a CU holding n workgroups runs each ~1 + 0.45 (n - 1) times
-// slower; every (S, grid cap of 1, 2, ... workgroups per CU) is costed.
-template <class Kern>
-double plan_tq5_one(const LaunchArgs &a, int R, Kern kernel, int lds, T5Params &p, int &grid) {
+// Plan of the one-token kernel, from timings of the 27B-class decode shapes
+// on MI355X (every R, S and 1 or 2 workgroups per CU): one tile per wave and
+// two workgroups per CU.  When the tiles fill every wave slot of that grid
+// (the LM head) K stays whole; otherwise K is cut over the fewest waves S (a
+// power of two, at most 8) that leave each wave at most two of a row's
+// segments (gate/up 34816 x 5120: 21.5 us, against 27.4 us for the plan
+// that minimised the CU-sharing cost of the other decode kernels, which kept
+// K whole and put one workgroup on most CUs; the LM head 65.6 us with K
+// whole, 75.7 us cut over 4 waves).
+void plan_tq5_one(const LaunchArgs &a, const void *kernel, int lds, T5Params &p, int &grid) {
   p = T5Params{};
   p.ms = mat_set(a);
   p.X = a.X;
   p.M = int(a.M); p.K = int(a.K); p.G = int(a.K / kGroup);
   p.tiles = int((a.N + 15) / 16);
-  p.tilesets = (p.tiles + R - 1) / R;
+  p.tilesets = p.tiles;  // one tile per wave
   const Tq5Geom g = tq5_geom(a.K);
   p.s_full = int(g.s_full);
   p.b_tail = int(g.b_tail);
   p.rowbytes = int(g.rowbytes);
   p.nseg = p.s_full + (g.L_tail > 0 ? 1 : 0);
   p.y_f16 = a.y_f16;
-  const int cus = num_cus();
-  const int per_cu = resident_blocks(reinterpret_cast<const void *>(kernel), kT5Threads, lds);
-  double best = 1e300;
-  T5Params bp = p;
-  int bgrid = 1;
-  for (int S = 1; S <= 8; S *= 2) {
-    if (S > 1 && S > p.nseg) break;
-    const int P = kT5Waves / S;
-    const int SS = (p.nseg + S - 1) / S;
-    const int want = (p.tilesets + P - 1) / P;
-    for (int n = 1; n <= per_cu; ++n) {
-      const int gsz = max(1, min(want, cus * n));
-      const int64_t rows = (int64_t)gsz * P;
-      const int64_t its = (p.tilesets + rows - 1) / rows;
-      const double units = double(its) * R * SS + (S > 1 ? double(its) : 0.0);
-      const int share = (gsz + cus - 1) / cus;
-      const double cost = (units + 2.0) * (1.0 + 0.45 * (share - 1));
-      if (cost < best) {
-        best = cost;
-        bp = p;
-        bp.S = S;
-        bp.SS = SS;
-        bgrid = gsz;
-      }
-      if (gsz == want) break;
-    }
-  }
-  p = bp;
-  grid = bgrid;
-  return best;
+  const int per_cu = resident_blocks(kernel, kT5Threads, lds);
+  const int slots = num_cus() * min(per_cu, 2);  // workgroups resident at once
+  int S = 1;
+  if (p.tilesets < slots * kT5Waves)
+    while (S < 8 && (p.nseg + S - 1) / S > 2) S *= 2;
+  p.S = S;
+  p.SS = (p.nseg + S - 1) / S;
+  const int P = kT5Waves / S;  // tile sets per workgroup pass
+  const int want = (p.tilesets + P - 1) / P;
+  grid = max(1, min(want, slots));
 }
 
 template <bool BF>
 hipError_t launch_tq5_one(const LaunchArgs &a) {
-  T5Params p1, p2;
-  int g1, g2;
+  T5Params p;
+  int grid;
   const int lds = t5_xlds_bytes(a.K);
-  const double c1 = plan_tq5_one(a, 1, &gemv_tq5_one_kernel<BF, 1>, lds, p1, g1);
-  const double c2 = plan_tq5_one(a, 2, &gemv_tq5_one_kernel<BF, 2>, lds, p2, g2);
-  if (c1 <= c2)
-    hipLaunchKernelGGL((gemv_tq5_one_kernel<BF, 1>), dim3(g1), dim3(kT5Threads), lds, a.stream, p1);
-  else
-    hipLaunchKernelGGL((gemv_tq5_one_kernel<BF, 2>), dim3(g2), dim3(kT5Threads), lds, a.stream, p2);
+  plan_tq5_one(a, reinterpret_cast<const void *>(&gemv_tq5_one_kernel<BF, 1>), lds, p, grid);
+  hipLaunchKernelGGL((gemv_tq5_one_kernel<BF, 1>), dim3(grid), dim3(kT5Threads), lds, a.stream, p);
   return hipGetLastError();
 }
 
