@@ -395,6 +395,27 @@ def test_gemm_shared_workspace_and_split_tiles():
     assert not ws[:65536].any(), "stream-K counters must be left at zero"
 
 
+def test_gemm_q1_workspace_paths():
+    """Binary weights with bf16 x: a full workspace takes the fp8-piece path
+    (x converted once per call into the workspace), one byte less takes the
+    exact bf16 operands with stream-K, none takes whole tiles; all three meet
+    the bound, at several token tiles and a ragged last chunk of groups."""
+    t = gu.torch()
+    g = np.random.default_rng(720)
+    for M, N, K in [(300, 700, 5120), (129, 272, 1408), (16, 130, 640)]:
+        codes = _codes(g, "q1", N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        x = synth.x_normal(g, M, K, "bf16")
+        w, xd = gu.w_tensor(lb.pack("q1", codes, sc)), gu.x_tensor(x, "bf16")
+        need = lb.gemm_workspace_bytes("q1", M, N, K)
+        for label, ws in [("pieces", t.zeros(need, dtype=t.uint8, device="cuda")),
+                          ("stream-K", t.zeros(need - 1, dtype=t.uint8, device="cuda")), ("whole tiles", False)]:
+            print(f"q1 gemm {label} M={M} N={N} K={K}", flush=True)
+            y = lb.gemm("q1", w, xd, N, K, workspace=ws)
+            t.cuda.synchronize()
+            gu.check(y.cpu().numpy().astype(np.float64), codes, sc, x, "bf16", f"q1 gemm {label} M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
 def test_mlx_affine_import_product(path):
     """An MLX affine 1-bit g128 matrix imported into Binary g128 gives the
