@@ -188,25 +188,37 @@ __device__ __forceinline__ void split_x_regs(const u4_t (&x)[4], XQuarter &o) {
   for (int i = 0; i < 16; ++i) mx = max(mx, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
   const int ef = int(mx >> 7);  // exponent field of the largest magnitude
   const int sb = ef == 255 ? 255 : max(ef - 7, 0);
-  const float mul = __builtin_bit_cast(float, uint32_t(254 - min(sb, 253)) << 23);  // 2^(127 - sb)
+  // S = 2^(sb - 127) as an f32 (2^-127 is a denormal).  The scaled
+  // conversions of gfx950 divide by S on the way to fp8 and multiply by it
+  // on the way back; each takes or gives two values, and a pair of bf16
+  // goes to fp8 without a separate widening and scaling.
+  const float S = sb == 0 ? __builtin_bit_cast(float, 0x00400000u)
+                          : __builtin_bit_cast(float, uint32_t(min(sb, 254)) << 23);
+  typedef short s2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
   int hi[8], lo[8];
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
-    float f[4];
+    uint32_t h[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int sidx = fp4_src(FMT, 4 * w + b);  // 8u + e
-      const uint32_t word = v[sidx / 2];
-      f[b] = __builtin_bit_cast(float, (sidx & 1) ? (word & 0xFFFF0000u) : (word << 16)) * mul;
+      h[b] = (sidx & 1) ? (v[sidx / 2] >> 16) : (v[sidx / 2] & 0xFFFFu);
     }
-    hi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    hi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], hi[w], true);
-    const float r0 = f[0] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 0);
-    const float r1 = f[1] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 1);
-    const float r2 = f[2] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 2);
-    const float r3 = f[3] - __builtin_amdgcn_cvt_f32_fp8(hi[w], 3);
-    lo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
-    lo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, lo[w], true);
+    s2_t ph = {0, 0}, pl = {0, 0};
+    ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(ph, __builtin_bit_cast(bf2_t, h[0] | (h[1] << 16)), S, false);
+    ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(ph, __builtin_bit_cast(bf2_t, h[2] | (h[3] << 16)), S, true);
+    hi[w] = __builtin_bit_cast(int, ph);
+    const f2_t b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi[w], S, false);
+    const f2_t b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi[w], S, true);
+    const float r0 = __builtin_bit_cast(float, h[0] << 16) - b01.x;
+    const float r1 = __builtin_bit_cast(float, h[1] << 16) - b01.y;
+    const float r2 = __builtin_bit_cast(float, h[2] << 16) - b23.x;
+    const float r3 = __builtin_bit_cast(float, h[3] << 16) - b23.y;
+    pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, r0, r1, S, false);
+    pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, r2, r3, S, true);
+    lo[w] = __builtin_bit_cast(int, pl);
   }
   o.h0 = u4_t{uint32_t(hi[0]), uint32_t(hi[1]), uint32_t(hi[2]), uint32_t(hi[3])};
   o.h1 = u4_t{uint32_t(hi[4]), uint32_t(hi[5]), uint32_t(hi[6]), uint32_t(hi[7])};
