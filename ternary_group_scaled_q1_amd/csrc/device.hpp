@@ -183,9 +183,12 @@ __device__ __forceinline__ void split_x_regs(const u4_t (&x)[4], XQuarter &o) {
     v[4 * u + 2] = x[u].z;
     v[4 * u + 3] = x[u].w;
   }
-  uint32_t mx = 0;
+  // Largest magnitude: both halves of a word at once (packed 16-bit max).
+  typedef unsigned short u2h_t __attribute__((ext_vector_type(2)));
+  u2h_t m2 = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) mx = max(mx, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+  for (int i = 0; i < 16; ++i) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u2h_t, v[i] & 0x7FFF7FFFu));
+  const uint32_t mx = max(uint32_t(m2.x), uint32_t(m2.y));
   const int ef = int(mx >> 7);  // exponent field of the largest magnitude
   const int sb = ef == 255 ? 255 : max(ef - 7, 0);
   // S = 2^(sb - 127) as an f32 (2^-127 is a denormal).  The scaled
