@@ -483,18 +483,21 @@ def test_gemv_multi_fused(fmt, xdt):
 
 @pytest.mark.parametrize("fmt", ["q1", "tq2"])
 @pytest.mark.parametrize("M", [8, 16])
-def test_split_twelve_wave_row_blocks(fmt, M):
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+def test_split_twelve_wave_row_blocks(fmt, M, xdt):
     """34816 rows (2176 row tiles, more than 8 but at most 12 per CU): the
-    2-D split takes workgroups of 12 waves with one tile each; also a ragged
-    last tile of the same tile count (the general load path)."""
+    2-D split takes workgroups of 12 waves with one tile each (fp8 pieces
+    for q1 with bf16 x, exact operands otherwise); also a ragged last tile of
+    the same tile count (the general load path)."""
     g = np.random.default_rng(930 + M)
     K = 2048
     for N in (34816, 34816 - 7):
         codes = _codes(g, fmt, N, K)
         sc = synth.scales_absnormal(g, N, K // 128)
-        x = synth.x_normal(g, M, K, "bf16")
-        y = gu.run("gemv", fmt, gu.w_tensor(lb.pack(fmt, codes, sc)), x, "bf16", "f32", N, K)
-        gu.check(y, codes, sc, x, "bf16", f"12-wave split {fmt} M={M} N={N}")
+        x = synth.x_normal(g, M, K, xdt)
+        print(f"12-wave split {fmt} {xdt} M={M} N={N}", flush=True)
+        y = gu.run("gemv", fmt, gu.w_tensor(lb.pack(fmt, codes, sc)), x, xdt, "f32", N, K)
+        gu.check(y, codes, sc, x, xdt, f"12-wave split {fmt} {xdt} M={M} N={N}")
 
 
 @pytest.mark.parametrize("fmt", ["q1", "tq2"])
