@@ -1,0 +1,84 @@
+"""bench.py's host side on the CPU: the one-GPU guard, the kernel-source
+digest that ties counter summaries to the code they were taken on, the
+reading of a counter summary, and the host baseline leg.  Nothing here
+touches a GPU."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""  # no result line
+
+
+def _fake_tree(tmp_path, text):
+    csrc = tmp_path / "ternary_group_scaled_q1_amd" / "csrc"
+    csrc.mkdir(parents=True, exist_ok=True)
+    (csrc / "k.hip").write_text(text)
+    (csrc / "notes.txt").write_text("not a source file")
+    return tmp_path
+
+
+def test_source_digest_ignores_comments_only(tmp_path, monkeypatch):
+    code = "int f(int a) {\n  return a + 1;\n}\n"
+    monkeypatch.setattr(bench, "ROOT", str(_fake_tree(tmp_path, code)))
+    d0 = bench._source_digest()
+    _fake_tree(tmp_path, "// a header comment\n\nint f(int a) {  // trailing note\n\n  return a + 1;\n}\n")
+    assert bench._source_digest() == d0
+    _fake_tree(tmp_path, "int f(int a) {\n  return a + 2;\n}\n")
+    assert bench._source_digest() != d0
+    _fake_tree(tmp_path, code)
+    (tmp_path / "ternary_group_scaled_q1_amd" / "csrc" / "notes.txt").write_text("changed")
+    assert bench._source_digest() == d0  # only .hip / .hpp / .cpp count
+
+
+def _summary(tmp_path, digest, sweep="tq2_M16", fetch="1000", write="200"):
+    lines = ["# a counter summary", "", "| kernel | x |", "|---|---|",
+             "    a command line: with a colon", f"source_sha256: {digest}", f"sweep: {sweep}"]
+    if fetch is not None:
+        lines.append(f"fetch_bytes_per_launch: {fetch}")
+    if write is not None:
+        lines.append(f"write_bytes_per_launch: {write}")
+    p = tmp_path / "traffic.txt"
+    p.write_text("\n".join(lines) + "\n")
+    return str(p)
+
+
+def test_measured_traffic_reads_only_a_current_summary(tmp_path, monkeypatch):
+    digest = bench._source_digest()
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", _summary(tmp_path, digest))
+    assert bench.measured_traffic(("tq2", 16)) == (1200, 1000)
+    assert bench.measured_traffic(("q1", 16)) == (None, None)  # another sweep
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", _summary(tmp_path, "0" * 64))
+    assert bench.measured_traffic(("tq2", 16)) == (None, None)  # kernels changed since
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", _summary(tmp_path, digest, write=None))
+    assert bench.measured_traffic(("tq2", 16)) == (None, 1000)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
+    assert bench.measured_traffic(("tq2", 16)) == (None, None)
+
+
+def test_committed_summary_has_the_machine_readable_lines():
+    keys = {}
+    with open(bench.TRAFFIC_FILE) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith(("#", "|", " ")):
+                k, v = ln.split(":", 1)
+                keys[k.strip()] = v.strip()
+    assert len(keys["source_sha256"]) == 64
+    assert keys["sweep"] in {f"{f}_M{m}" for f in ("q1", "tq2") for m in (1, 16)}
+    assert int(keys["fetch_bytes_per_launch"]) > 0 and int(keys["write_bytes_per_launch"]) > 0
+
+
+def test_cpu_baseline_leg_reports_the_oracle():
+    r = bench.cpu_baseline(0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert r["value"] > 0 and r["cores"] >= 1
+    assert "512 of the 17408 rows" in r["sample"]
