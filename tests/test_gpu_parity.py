@@ -514,3 +514,35 @@ def test_split_tall_matrix_four_tiles_per_wave(fmt, M):
         x = synth.x_normal(g, M, K, "bf16")
         y = gu.run("gemv", fmt, gu.w_tensor(lb.pack(fmt, codes, sc)), x, "bf16", "f32", N, K)
         gu.check(y, codes, sc, x, "bf16", f"tall split {fmt} M={M} N={N}")
+
+
+@pytest.mark.parametrize("fmt", ["q1", "tq2"])
+@pytest.mark.parametrize("M", [4, 16])
+def test_split_most_k_ranges_reused_workspace(fmt, M):
+    """One row block and 62 groups: the 2-D split cuts K into 16 ranges of 4
+    groups and a last one of 2 (ragged chunk, general load path), so the
+    last workgroup adds two batches of 8 ranges.  The same workspace serves
+    three calls in a row (fp32 out, fp16 out, fp32 again): the arrival
+    counters must be back at zero after each, and the repeat is bit-equal."""
+    t = gu.torch()
+    g = np.random.default_rng(950 + M)
+    K = 62 * 128
+    for N in (16, 23):
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        x = synth.x_normal(g, M, K, "bf16")
+        blob = gu.w_tensor(lb.pack(fmt, codes, sc))
+        xd = gu.x_tensor(x, "bf16")
+        need = lb.gemv_workspace_bytes(fmt, M, N, K)
+        ws = t.zeros(max(need, 1), dtype=t.uint8, device="cuda")
+        ys = []
+        for odt in (t.float32, t.float16, t.float32):
+            print(f"most K ranges {fmt} M={M} N={N} out={odt}", flush=True)
+            y = lb.gemv(fmt, blob, xd, N, K, out_dtype=odt, workspace=ws)
+            t.cuda.synchronize()
+            ys.append(y.float().cpu().numpy().astype(np.float64))
+        for i, y in enumerate(ys):
+            gu.check(y, codes, sc, x, "bf16", f"most K ranges {fmt} M={M} N={N} call {i}")
+        assert np.array_equal(ys[0], ys[2])
+        if need:
+            assert int(ws[:4 * ((N + 15) // 16)].view(t.int32).abs().sum()) == 0  # counters reset
