@@ -194,9 +194,9 @@ def main():
     for i, (fmt, M, N, K, p0) in enumerate(GEMMS):
         if i not in gemm_ids:
             continue
-        codes, sc = synth.draw_matrix(args.seed, 4, i, N, K, p0)
+        codes, sc = synth.draw_matrix(args.seed, synth.WORKLOADS["prefill_gemm_512"]["stream"], i, N, K, p0)
         w = torch.from_numpy(lb.pack(fmt, codes, sc)).to(dev)
-        x = torch.from_numpy(synth.draw_x(args.seed, 4, i, M, K, "bf16").view(np.int16)).view(torch.bfloat16).to(dev)
+        x = torch.from_numpy(synth.draw_x(args.seed, synth.WORKLOADS["prefill_gemm_512"]["stream"], i, M, K, "bf16").view(np.int16)).view(torch.bfloat16).to(dev)
         y = torch.empty((M, N), device=dev, dtype=torch.float32)
         gemm_data[i] = (lb.FORMATS[fmt], w, x, y, M, N, K)
         del codes, sc
@@ -393,9 +393,10 @@ def cpu_baseline(budget_s):
     except Exception:
         cores = os.cpu_count() or 1
     N, K, rows = 17408, 5120, 512
-    codes, sc = synth.draw_matrix(0, 5, 0, rows, K, None)
+    sweep = synth.WORKLOADS["decode_sweep_27b"]["stream"]
+    codes, sc = synth.draw_matrix(0, sweep, 0, rows, K, None)
     blob = lb.pack("q1", codes, sc)
-    x = synth.draw_x(0, 5, 0, 1, K, "bf16")
+    x = synth.draw_x(0, sweep, 0, 1, K, "bf16")
     per_call_bytes = lb.packed_bytes("q1", rows, K) + K * 2 + rows * 4
     t0 = time.perf_counter()
     calls = 0

@@ -17,7 +17,7 @@ Conventions
   round-to-nearest-even: fp16 by numpy's float64 -> float16 cast, bf16 by
   numpy float64 -> float32 followed by RNE of the float32 to its top 16 bits.
   The rounded values *are* the inputs.
-* Every stream is ``numpy.random.default_rng([seed, cfg, matrix_id, field])``
+* Every stream is ``numpy.random.default_rng([seed, stream, matrix_id, field])``
   with field 0 = codes, 1 = scales, 2 = activations.
 """
 from __future__ import annotations
@@ -28,8 +28,8 @@ FIELD_CODES, FIELD_SCALES, FIELD_X = 0, 1, 2
 GROUP = 128
 
 
-def rng(seed: int, cfg: int, matrix_id: int, field: int) -> np.random.Generator:
-    return np.random.default_rng([int(seed), int(cfg), int(matrix_id), int(field)])
+def rng(seed: int, stream: int, matrix_id: int, field: int) -> np.random.Generator:
+    return np.random.default_rng([int(seed), int(stream), int(matrix_id), int(field)])
 
 
 # ---------------------------------------------------------------- codes ----
@@ -125,22 +125,24 @@ def codes_sign_aligned(x_bits_row: np.ndarray, N: int, dtype: str, p_zero: float
 
 
 # ------------------------------------------------ workload configurations --
-# The workloads the path is measured and checked on.  Shapes are (N, K);
-# ``x`` is the activation dtype; ``p_zero`` is None for binary codes.
-CONFIGS = {
-    1: dict(name="q1 GEMV 256x1024 M=1 (latency/correctness)", fmt="q1",
+# The workloads the path is measured and checked on, keyed by what they are.
+# Shapes are (N, K); ``x`` is the activation dtype; ``p_zero`` is None for
+# binary codes; ``stream`` is the workload's fixed id in the seeded draws
+# (draw_matrix / draw_x take it), so every draw stays put under any key.
+WORKLOADS = {
+    "q1_gemv_256x1024": dict(stream=1, name="q1 GEMV 256x1024 M=1 (latency/correctness)", fmt="q1",
             shapes=[(256, 1024)], M=[1], x="f16", y="f32", p_zero=None,
             scales=("uniform", 0.005, 0.05)),
-    2: dict(name="q1 GEMV decode, 8B-class layer shapes, M=1", fmt="q1",
+    "q1_decode_8b": dict(stream=2, name="q1 GEMV decode, 8B-class layer shapes, M=1", fmt="q1",
             shapes=[(24576, 4096), (4096, 12288), (151936, 4096)], M=[1], x="f16",
             y="f32", p_zero=None, scales=("absnormal", 0.02, 1e-3)),
-    3: dict(name="tq2 GEMV, 27B-class shapes, M in {1,4,8}", fmt="tq2",
+    "tq2_decode_27b": dict(stream=3, name="tq2 GEMV, 27B-class shapes, M in {1,4,8}", fmt="tq2",
             shapes=[(34816, 5120), (5120, 17408)], M=[1, 4, 8], x="bf16", y="f32",
             p_zero=0.3, scales=("absnormal", 0.02, 1e-3)),
-    4: dict(name="prefill GEMM M=512: q1 17408x5120 and tq5 5120x17408", fmt=["q1", "tq5"],
+    "prefill_gemm_512": dict(stream=4, name="prefill GEMM M=512: q1 17408x5120 and tq5 5120x17408", fmt=["q1", "tq5"],
             shapes=[(17408, 5120), (5120, 17408)], M=[512], x="bf16", y="f32",
             p_zero=[None, 1.0 / 3.0], scales=("absnormal", 0.02, 1e-3)),
-    5: dict(name="~25B-param decode weight sweep (64 blocks + LM head), M in {1,16}",
+    "decode_sweep_27b": dict(stream=5, name="~25B-param decode weight sweep (64 blocks + LM head), M in {1,16}",
             fmt=["q1", "tq2"], M=[1, 16], x="bf16", y="f32", p_zero=[None, 0.3],
             scales=("absnormal", 0.02, 1e-3),
             block=[(5120, 5120)] * 4 + [(17408, 5120), (17408, 5120), (5120, 17408)],
@@ -148,12 +150,12 @@ CONFIGS = {
 }
 
 
-def draw_matrix(seed: int, cfg: int, matrix_id: int, N: int, K: int, p_zero,
+def draw_matrix(seed: int, stream: int, matrix_id: int, N: int, K: int, p_zero,
                 scales=("absnormal", 0.02, 1e-3)):
     """(codes int8[N,K], scales uint16[N,K/128]) for one weight matrix."""
-    gc = rng(seed, cfg, matrix_id, FIELD_CODES)
+    gc = rng(seed, stream, matrix_id, FIELD_CODES)
     codes = codes_binary(gc, N, K) if p_zero is None else codes_ternary(gc, N, K, p_zero)
-    gs = rng(seed, cfg, matrix_id, FIELD_SCALES)
+    gs = rng(seed, stream, matrix_id, FIELD_SCALES)
     if scales[0] == "uniform":
         s = scales_uniform(gs, N, K // GROUP, scales[1], scales[2])
     else:
@@ -161,5 +163,5 @@ def draw_matrix(seed: int, cfg: int, matrix_id: int, N: int, K: int, p_zero,
     return codes, s
 
 
-def draw_x(seed: int, cfg: int, matrix_id: int, M: int, K: int, dtype: str) -> np.ndarray:
-    return x_normal(rng(seed, cfg, matrix_id, FIELD_X), M, K, dtype)
+def draw_x(seed: int, stream: int, matrix_id: int, M: int, K: int, dtype: str) -> np.ndarray:
+    return x_normal(rng(seed, stream, matrix_id, FIELD_X), M, K, dtype)

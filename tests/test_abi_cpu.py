@@ -59,13 +59,14 @@ def test_pack_matches_oracle_bit_exact(fmt):
         assert np.array_equal(c2, codes) and np.array_equal(s2, sc)
 
 
-@pytest.mark.parametrize("cfg,mid", [(2, 1), (3, 1), (4, 0), (4, 1)])
-def test_pack_matches_oracle_at_workload_shapes(cfg, mid):
-    c = synth.CONFIGS[cfg]
+@pytest.mark.parametrize("workload,mid", [("q1_decode_8b", 1), ("tq2_decode_27b", 1), ("prefill_gemm_512", 0),
+                                          ("prefill_gemm_512", 1)])
+def test_pack_matches_oracle_at_workload_shapes(workload, mid):
+    c = synth.WORKLOADS[workload]
     fmt = c["fmt"] if isinstance(c["fmt"], str) else c["fmt"][mid]
     p_zero = c["p_zero"] if not isinstance(c["p_zero"], list) else c["p_zero"][mid]
     N, K = c["shapes"][mid]
-    codes, sc = synth.draw_matrix(0, cfg, mid, N, K, p_zero)
+    codes, sc = synth.draw_matrix(0, c["stream"], mid, N, K, p_zero)
     blob = lb.pack(fmt, codes, sc)
     assert np.array_equal(blob, layout.pack(fmt, codes, sc))
 

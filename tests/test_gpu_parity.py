@@ -162,9 +162,10 @@ def test_degenerate_sizes():
 
 
 # ------------------------------------------------ full workload shapes ----
-def _sampled(fmt, N, K, M, xdt, path, cfg, mid, p_zero, rows=48, seed=0):
-    codes, sc = synth.draw_matrix(seed, cfg, mid, N, K, p_zero)
-    x = synth.draw_x(seed, cfg, mid, M, K, xdt)
+def _sampled(fmt, N, K, M, xdt, path, workload, mid, p_zero, rows=48, seed=0):
+    stream = synth.WORKLOADS[workload]["stream"]
+    codes, sc = synth.draw_matrix(seed, stream, mid, N, K, p_zero)
+    x = synth.draw_x(seed, stream, mid, M, K, xdt)
     w = gu.w_tensor(lb.pack(fmt, codes, sc))
     y = gu.run(path, fmt, w, x, xdt, "f32", N, K)
     g = np.random.default_rng(seed + 17)
@@ -177,35 +178,35 @@ def _sampled(fmt, N, K, M, xdt, path, cfg, mid, p_zero, rows=48, seed=0):
 
 @pytest.mark.parametrize("mid", [0, 1, 2])
 def test_workload_q1_decode_8b_shapes(mid):
-    N, K = synth.CONFIGS[2]["shapes"][mid]
+    N, K = synth.WORKLOADS["q1_decode_8b"]["shapes"][mid]
     print(f"q1 gemv N={N} K={K}", flush=True)
-    _sampled("q1", N, K, 1, "f16", "gemv", 2, mid, None)
+    _sampled("q1", N, K, 1, "f16", "gemv", "q1_decode_8b", mid, None)
 
 
 @pytest.mark.parametrize("mid", [0, 1])
 @pytest.mark.parametrize("M", [1, 4, 8])
 def test_workload_tq2_decode_27b_shapes(mid, M):
-    N, K = synth.CONFIGS[3]["shapes"][mid]
+    N, K = synth.WORKLOADS["tq2_decode_27b"]["shapes"][mid]
     print(f"tq2 gemv N={N} K={K} M={M}", flush=True)
-    _sampled("tq2", N, K, M, "bf16", "gemv", 3, mid, 0.3)
+    _sampled("tq2", N, K, M, "bf16", "gemv", "tq2_decode_27b", mid, 0.3)
 
 
 @pytest.mark.parametrize("mid", [0, 1])
 def test_workload_prefill_gemm(mid):
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS["prefill_gemm_512"]
     N, K = c["shapes"][mid]
     fmt, p0 = c["fmt"][mid], c["p_zero"][mid]
     print(f"{fmt} gemm M=512 N={N} K={K}", flush=True)
-    _sampled(fmt, N, K, 512, "bf16", "gemm", 4, mid, p0, rows=24)
+    _sampled(fmt, N, K, 512, "bf16", "gemm", "prefill_gemm_512", mid, p0, rows=24)
 
 
-def test_workload_config1_all_outputs():
-    c = synth.CONFIGS[1]
+def test_workload_q1_gemv_256x1024_all_outputs():
+    c = synth.WORKLOADS["q1_gemv_256x1024"]
     N, K = c["shapes"][0]
-    codes, sc = synth.draw_matrix(0, 1, 0, N, K, None, scales=c["scales"])
-    x = synth.draw_x(0, 1, 0, 1, K, "f16")
+    codes, sc = synth.draw_matrix(0, c["stream"], 0, N, K, None, scales=c["scales"])
+    x = synth.draw_x(0, c["stream"], 0, 1, K, "f16")
     y = gu.run("gemv", "q1", gu.w_tensor(lb.pack("q1", codes, sc)), x, "f16", "f32", N, K)
-    gu.check(y, codes, sc, x, "f16", "config 1")
+    gu.check(y, codes, sc, x, "f16", "q1 gemv 256x1024")
 
 
 # ------------------------------------------ decode sweep shapes (27B-class) ----
@@ -218,7 +219,7 @@ SWEEP_SHAPES = [(5120, 5120), (17408, 5120), (5120, 17408)]
 def test_workload_sweep_shapes(fmt, shape, M):
     N, K = shape
     print(f"{fmt} gemv sweep shape N={N} K={K} M={M}", flush=True)
-    _sampled(fmt, N, K, M, "bf16", "gemv", 5, SWEEP_SHAPES.index(shape), None if fmt == "q1" else 0.3)
+    _sampled(fmt, N, K, M, "bf16", "gemv", "decode_sweep_27b", SWEEP_SHAPES.index(shape), None if fmt == "q1" else 0.3)
 
 
 @pytest.mark.parametrize("mid", [0, 1])
@@ -226,9 +227,9 @@ def test_workload_sweep_shapes(fmt, shape, M):
 def test_workload_tq5_decode_27b_shapes(mid, M):
     """Base-3 weights at the 27B-class decode shapes (34816x5120: 8 full
     segments per row; 5120x17408: 27 full segments and a 128-trit tail)."""
-    N, K = synth.CONFIGS[3]["shapes"][mid]
+    N, K = synth.WORKLOADS["tq2_decode_27b"]["shapes"][mid]
     print(f"tq5 gemv N={N} K={K} M={M}", flush=True)
-    _sampled("tq5", N, K, M, "bf16", "gemv", 3, mid, 0.3)
+    _sampled("tq5", N, K, M, "bf16", "gemv", "tq2_decode_27b", mid, 0.3)
 
 
 def test_workload_sweep_lm_head_q1():
