@@ -234,7 +234,7 @@ def test_workload_tq5_decode_27b_shapes(mid, M):
 
 def test_workload_sweep_lm_head_q1():
     print("q1 gemv N=151936 K=5120 M=1", flush=True)
-    _sampled("q1", 151936, 5120, 1, "bf16", "gemv", 5, 3, None, rows=32)
+    _sampled("q1", 151936, 5120, 1, "bf16", "gemv", "decode_sweep_27b", 3, None, rows=32)
 
 
 # ------------------------------------------------ bf16 x over a wide range ----
