@@ -30,8 +30,11 @@
  *
  * Product: for m < M, n < N
  *     Y[m][n] = sum_k X[m][k] * t[n][k] * s[n][k/128]
- * W row n is output feature n (nn.Linear order); X is M x K and Y is M x N,
- * both row-major and contiguous.  Y is overwritten.  Accumulation is fp32
+ * (aberweb.com page, section 4.1: the stored bits become signed values
+ * multiplied by the FP16 scale of their 128-weight group; ksqn.cn page:
+ * ternary weights are {-1, 0, +1} times the group scale).  W row n is
+ * output feature n (nn.Linear order); X is M x K and Y is M x N, both
+ * row-major and contiguous.  Y is overwritten.  Accumulation is fp32
  * with every product exact (weights are decoded to exact +-1 / 0 and the
  * FP16 scale is applied in fp32 once per group); an fp16 Y is rounded to
  * nearest even from the fp32 result.  Results are deterministic for a given
@@ -52,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 4
+#define LOWBIT_ABI_VERSION 5
 
 typedef enum { LOWBIT_Q1_G128 = 1, LOWBIT_TQ2_G128 = 2, LOWBIT_TQ5_G128 = 3 } lowbit_format;
 typedef enum { LOWBIT_F16 = 1, LOWBIT_BF16 = 2, LOWBIT_F32 = 3 } lowbit_dtype;
@@ -70,20 +73,33 @@ enum {
   LOWBIT_ERR_DEVICE = -8  /* the HIP runtime reported an error                         */
 };
 
-/* Library ABI version (LOWBIT_ABI_VERSION of the build). */
+/* Library ABI version (LOWBIT_ABI_VERSION of the build).  The formats it
+ * serves are those of the lnrk.cn page (Binary g128 section), the ksqn.cn
+ * page (ternary g128) and the cnblogs.com page (section 2.4, 5 trits per
+ * byte). */
 int lowbit_abi_version(void);
 
-/* Static string describing a status code; never NULL. */
+/* Static string describing a status code; never NULL.  The value checks it
+ * names follow the value maps of the lnrk.cn page (Binary g128 section) and
+ * the ksqn.cn page ("current limitations": ternary codes in 2-bit slots). */
 const char *lowbit_strerror(int status);
 
 /* Size in bytes of a packed blob: plane A + N*(K/128)*2.
- *   q1: N*K/8 + N*(K/128)*2      (1.125 bits per weight)
- *   tq2: N*K/4 + N*(K/128)*2     (2.125 bits per weight)
- *   tq5: N*ceil(K/5) + N*(K/128)*2
+ *   q1: N*K/8 + N*(K/128)*2      (1.125 bits per weight: one sign bit per
+ *       weight and one FP16 scale per 128, lnrk.cn page, Binary g128 section
+ *       and its memory table; the aberweb.com page, Table 2, gives the same
+ *       18/128 bytes per weight for the 8B model)
+ *   tq2: N*K/4 + N*(K/128)*2     (2.125 bits per weight: ternary in 2-bit
+ *       slots, ksqn.cn page, "current limitations")
+ *   tq5: N*ceil(K/5) + N*(K/128)*2  (5 trits per byte, cnblogs.com page,
+ *       section 2.4)
  * Returns a negative status on a bad format or shape. */
 int64_t packed_bytes_lowbit(int fmt, int64_t N, int64_t K);
 
-/* Pack codes and scales (host memory in, host memory out).
+/* Pack codes and scales (host memory in, host memory out): the value maps
+ * of the lnrk.cn page (Binary g128 section: bit 1 -> +scale, bit 0 ->
+ * -scale), the ksqn.cn page (ternary {-1,0,+1} with a g128 FP16 scale, 2-bit
+ * slots) and the cnblogs.com page (section 2.4: 5 trits per byte).
  *   codes:  int8 [N][K], row-major; q1: values in {-1,+1}; tq2/tq5: {-1,0,+1}
  *   scales: uint16 [N][K/128], FP16 bit patterns, stored bit-exactly
  *   out:    caller-owned, at least packed_bytes_lowbit(fmt, N, K) bytes
@@ -111,13 +127,18 @@ int pack_tq5_g128(const int8_t *codes, const uint16_t *scales, int64_t N, int64_
 int import_mlx_q1_g128(const uint32_t *wq, const void *scales, const void *biases, int sb_dtype,
                        int64_t N, int64_t K, void *out, int64_t out_bytes);
 
-/* Exact inverse of pack_* (host memory).  codes_out int8 [N][K] and
- * scales_out uint16 [N][K/128] are caller-owned; either may be NULL to skip it. */
+/* Exact inverse of pack_* (host memory): the same value maps read back
+ * (lnrk.cn page, Binary g128 section; ksqn.cn page, "current limitations";
+ * cnblogs.com page, section 2.4, whose byte of 5 trits has 243 valid values).
+ * codes_out int8 [N][K] and scales_out uint16 [N][K/128] are caller-owned;
+ * either may be NULL to skip it. */
 int unpack_lowbit(int fmt, const void *packed, int64_t packed_bytes, int64_t N, int64_t K,
                   int8_t *codes_out, uint16_t *scales_out);
 
 /* Workspace that lets gemv_lowbit take its fastest path for this problem
- * (0 = the fastest path needs none).  The decode product may cut K into
+ * (0 = the fastest path needs none).  Decode is bound by streaming the
+ * weights (aberweb.com page, sections 2 and 4.4), so small matrices cut K
+ * across workgroups to keep every compute unit streaming.  The decode product may cut K into
  * ranges handled by different workgroups; their fp32 partial sums live here,
  * after 32 KiB of arrival counters at its start.  The size does not depend
  * on the device or on the activation dtype; base-3 (tq5) weights never use
@@ -126,7 +147,10 @@ int unpack_lowbit(int fmt, const void *packed, int64_t packed_bytes, int64_t N, 
 int64_t gemv_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* Decode GEMV: Y = X W^T for small batches (tuned for M <= 16; any M works;
- * more than 16 tokens run as consecutive 16-token launches).
+ * more than 16 tokens run as consecutive 16-token launches).  The packed
+ * bits are decoded inside the matrix kernel and multiplied by their group's
+ * FP16 scale there, with no dense weight tensor (aberweb.com page, section
+ * 4.1); token generation is bandwidth-bound (aberweb.com page, section 2).
  *   Wp: device, packed blob of this (fmt, N, K), 16-byte aligned
  *   X:  device, M x K, x_dtype LOWBIT_F16 or LOWBIT_BF16, 16-byte aligned
  *   Y:  device, M x N, y_dtype LOWBIT_F32 or LOWBIT_F16
@@ -144,11 +168,13 @@ int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, in
                 int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
                 void *hip_stream);
 
-/* Matrices one fused decode call may cover. */
+/* Matrices one fused decode call may cover (the query / key / value or
+ * gate / up projections of a block share x; lnrk.cn page, DSpark section). */
 #define LOWBIT_MAX_FUSED 4
 
 /* Workspace for gemv_multi_lowbit over these matrices (same meaning and
- * rules as gemv_workspace_bytes_lowbit).  Ns: host array of count row counts.
+ * rules as gemv_workspace_bytes_lowbit; decode is bandwidth-bound,
+ * aberweb.com page, section 2).  Ns: host array of count row counts.
  * Returns a negative status on a bad format, count or shape. */
 int64_t gemv_multi_workspace_bytes_lowbit(int fmt, int count, const int64_t *Ns, int64_t M, int64_t K);
 
@@ -169,7 +195,9 @@ int gemv_multi_lowbit(int fmt, int count, const void *const *Ws, const int64_t *
                       int x_dtype, void *const *Ys, int y_dtype, int64_t M, int64_t K,
                       void *workspace, int64_t workspace_bytes, void *hip_stream);
 
-/* Workspace that lets gemm_lowbit balance its work over the whole chip: the
+/* Workspace that lets gemm_lowbit balance its work over the whole chip
+ * (prompt processing is compute-bound, aberweb.com page, summary section 3,
+ * so every compute unit should multiply until the end): the
  * (tile, 128-weight group) work items are cut into one contiguous range per
  * workgroup slot, and tiles split between two ranges are summed through this
  * memory (64 KiB of arrival counters, then two fp32 output tiles per slot:
@@ -184,7 +212,10 @@ int gemv_multi_lowbit(int fmt, int count, const void *const *Ws, const int64_t *
  * format or shape. */
 int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
 
-/* Prefill GEMM: Y = X W^T for large batches (M = prompt tokens).  Same
+/* Prefill GEMM: Y = X W^T for large batches (M = prompt tokens), a dense
+ * contraction on the matrix cores: prompt processing is compute-bound
+ * (aberweb.com page, summary section 3) and the bits are decoded inside the
+ * matrix kernel (aberweb.com page, section 4.1).  Same
  * arguments and rules as gemv_lowbit, including the workspace: caller-owned,
  * 16-byte aligned, zero-filled before its first use (every call leaves its
  * counters zero again), one per concurrently running call.  With at least
@@ -195,6 +226,65 @@ int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K);
 int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype,
                 int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
                 void *hip_stream);
+
+/* ---- Plans: which kernel a product call would launch, and how it splits the
+ * work.  Decode (small M) streams the weights and is bandwidth-bound, prefill
+ * (large M) is compute-bound (aberweb.com page, sections 2 and 4.4 and
+ * summary section 3), so the two products take different kernels and work
+ * splits; these calls report them without launching anything. */
+typedef enum {
+  LOWBIT_KERNEL_NONE = 0,         /* nothing to launch (M * N == 0)                        */
+  LOWBIT_KERNEL_GEMV_STAGED = 1,  /* decode, x staged in LDS once per workgroup            */
+  LOWBIT_KERNEL_GEMV_SPLIT = 2,   /* decode, row blocks x K ranges, x staged per block     */
+  LOWBIT_KERNEL_GEMV_WIDE = 3,    /* decode, x read straight into registers (9..16 tokens) */
+  LOWBIT_KERNEL_GEMV_TQ5 = 4,     /* decode, base-3 weights                                */
+  LOWBIT_KERNEL_GEMV_TQ5_ONE = 5, /* decode, base-3 weights, one token, x in LDS           */
+  LOWBIT_KERNEL_GEMM = 6,         /* prefill                                               */
+  LOWBIT_KERNEL_FILL_ZERO = 7     /* K == 0: Y = 0                                         */
+} lowbit_kernel;
+
+typedef enum {
+  LOWBIT_OPERANDS_NONE = 0,
+  LOWBIT_OPERANDS_F16 = 1,     /* exact f16 operands on v_mfma_f32_16x16x32_f16            */
+  LOWBIT_OPERANDS_BF16 = 2,    /* exact bf16 operands on v_mfma_f32_16x16x32_bf16          */
+  LOWBIT_OPERANDS_FP8_FP4 = 3  /* x as two fp8 pieces, weights as fp4, scaled 16x16x128    */
+} lowbit_operands;
+
+typedef struct {
+  int kernel;            /* lowbit_kernel of the call's main launch                     */
+  int launches;          /* kernel launches the call issues in all                      */
+  int grid;              /* workgroups of the main launch (of its first 16-token block) */
+  int threads;           /* work-items per workgroup                                    */
+  int lds_bytes;         /* dynamic LDS bytes per workgroup                             */
+  int token_slots;       /* token rows one launch covers (1, 2, 4, 8 or 16; GEMM 128)   */
+  int operands;          /* lowbit_operands                                             */
+  int whole_tiles;       /* 1: addresses for whole 16-row tiles and whole 4-group chunks */
+  int tiles_per_wave;    /* row tiles (16 rows each) a wave holds per unit of work      */
+  int waves;             /* waves per workgroup                                         */
+  int waves_per_tile;    /* waves of one workgroup that split one tile set's K          */
+  int k_ranges;          /* K ranges cut across workgroups (partial sums in workspace)  */
+  int groups_per_range;  /* 128-weight groups per K range, or per wave of a wave-row    */
+  int groups_per_pass;   /* groups of x staged in LDS per pass (0: not staged)          */
+  int ring;              /* units of packed weights in flight per wave                  */
+  int items_per_wg;      /* GEMM: (tile, group) items per workgroup (G: whole tiles)    */
+  int x_pieces;          /* GEMM: 1 when x is converted to fp8 pieces first             */
+  int lds_offsets[3];    /* staged decode kernel: scale/correction, x and reduction areas */
+  int reserved[4];
+} lowbit_plan;
+
+/* The plan gemv_multi_lowbit (count matrices; count 1 is gemv_lowbit) would
+ * follow (decode, bandwidth-bound: aberweb.com page, section 2) with a workspace of workspace_bytes bytes on the current device
+ * (256 compute units and one workgroup per CU when no device is visible).
+ * Ns: host array of count row counts.  Nothing is launched or allocated.
+ * Returns the status the product call would return for these shapes and
+ * dtypes (pointer checks aside); out is filled on LOWBIT_OK. */
+int lowbit_gemv_plan(int fmt, int count, const int64_t *Ns, int x_dtype, int y_dtype, int64_t M, int64_t K,
+                     int64_t workspace_bytes, lowbit_plan *out);
+
+/* The same for gemm_lowbit (prefill, compute-bound: aberweb.com page, summary
+ * section 3). */
+int lowbit_gemm_plan(int fmt, int x_dtype, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t workspace_bytes,
+                     lowbit_plan *out);
 
 #ifdef __cplusplus
 }

@@ -12,8 +12,8 @@ The C ABI is declared in include/lowbit.h; this module only marshals
 arguments to it (ctypes), with torch providing device memory and streams.
 """
 from ._lib import (  # noqa: F401
-    DT_BF16, DT_F16, DT_F32, FORMATS, GROUP, LIB_PATH, MAX_FUSED, LowbitError, abi_version, gemm, gemm_raw,
-    gemm_workspace_bytes, gemv, gemv_multi, gemv_multi_raw, gemv_multi_workspace_bytes, gemv_raw,
-    gemv_workspace_bytes, import_mlx_q1, load, pack, packed_bytes, strerror,
+    DT_BF16, DT_F16, DT_F32, FORMATS, GROUP, LIB_PATH, MAX_FUSED, LowbitError, abi_version, gemm, gemm_plan,
+    gemm_raw, gemm_workspace_bytes, gemv, gemv_multi, gemv_multi_raw, gemv_multi_workspace_bytes, gemv_plan,
+    gemv_raw, gemv_workspace_bytes, import_mlx_q1, load, pack, packed_bytes, strerror,
     unpack,
 )

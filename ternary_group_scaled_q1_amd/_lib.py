@@ -19,6 +19,25 @@ GROUP = 128
 
 _lib = None
 
+KERNELS = {0: "none", 1: "gemv_staged", 2: "gemv_split", 3: "gemv_wide", 4: "gemv_tq5", 5: "gemv_tq5_one",
+           6: "gemm", 7: "fill_zero"}
+OPERANDS = {0: "none", 1: "f16", 2: "bf16", 3: "fp8_fp4"}
+
+
+class Plan(ctypes.Structure):
+    """lowbit_plan of include/lowbit.h."""
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "kernel", "launches", "grid", "threads", "lds_bytes", "token_slots", "operands", "whole_tiles",
+        "tiles_per_wave", "waves", "waves_per_tile", "k_ranges", "groups_per_range", "groups_per_pass", "ring",
+        "items_per_wg", "x_pieces")] + [("lds_offsets", ctypes.c_int * 3), ("reserved", ctypes.c_int * 4)]
+
+    def as_dict(self) -> dict:
+        d = {n: getattr(self, n) for n, _ in self._fields_ if n not in ("lds_offsets", "reserved")}
+        d["lds_offsets"] = list(self.lds_offsets)
+        d["kernel_name"] = KERNELS.get(self.kernel, "?")
+        d["operands_name"] = OPERANDS.get(self.operands, "?")
+        return d
+
 
 class LowbitError(RuntimeError):
     def __init__(self, status: int, msg: str):
@@ -59,6 +78,8 @@ def load() -> ctypes.CDLL:
         "gemv_multi_lowbit": (i32, [i32, i32, vp, vp, vp, i32, vp, i32, i64, i64, vp, i64, vp]),
         "gemm_workspace_bytes_lowbit": (i64, [i32, i64, i64, i64]),
         "gemm_lowbit": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp, i64, vp]),
+        "lowbit_gemv_plan": (i32, [i32, i32, vp, i32, i32, i64, i64, i64, ctypes.POINTER(Plan)]),
+        "lowbit_gemm_plan": (i32, [i32, i32, i32, i64, i64, i64, i64, ctypes.POINTER(Plan)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -307,3 +328,26 @@ def gemm_raw(fmt: int, w_ptr: int, x_ptr: int, x_dtype: int, y_ptr: int, y_dtype
              stream_ptr: int, ws_ptr: int = 0, ws_bytes: int = 0) -> None:
     _check(load().gemm_lowbit(fmt, w_ptr, x_ptr, x_dtype, y_ptr, y_dtype, M, N, K, ws_ptr or None, ws_bytes,
                               stream_ptr))
+
+
+def _dt(d) -> int:
+    return {"f16": DT_F16, "bf16": DT_BF16, "f32": DT_F32}[d] if isinstance(d, str) else int(d)
+
+
+def gemv_plan(fmt, Ns, M: int, K: int, x_dtype="bf16", y_dtype="f32", workspace_bytes: int = 0) -> dict:
+    """What gemv_lowbit (one row count) or gemv_multi_lowbit (a list) would
+    launch with a workspace of workspace_bytes bytes (lowbit_gemv_plan)."""
+    Ns = [Ns] if isinstance(Ns, int) else list(Ns)
+    arr = (ctypes.c_int64 * len(Ns))(*Ns)
+    out = Plan()
+    _check(load().lowbit_gemv_plan(_fmt(fmt), len(Ns), arr, _dt(x_dtype), _dt(y_dtype), M, K, workspace_bytes,
+                                   ctypes.byref(out)))
+    return out.as_dict()
+
+
+def gemm_plan(fmt, M: int, N: int, K: int, x_dtype="bf16", y_dtype="f32", workspace_bytes: int = 0) -> dict:
+    """What gemm_lowbit would launch (lowbit_gemm_plan)."""
+    out = Plan()
+    _check(load().lowbit_gemm_plan(_fmt(fmt), _dt(x_dtype), _dt(y_dtype), M, N, K, workspace_bytes,
+                                   ctypes.byref(out)))
+    return out.as_dict()

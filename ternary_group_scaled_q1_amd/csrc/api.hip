@@ -10,8 +10,8 @@ using namespace lowbit;
 
 namespace {
 
-int check_product(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M,
-                  int64_t N, int64_t K) {
+// Format, dtype and shape checks of a product (no pointers).
+int check_shape(int fmt, int x_dtype, int y_dtype, int64_t M, int64_t N, int64_t K) {
   if (fmt < LOWBIT_Q1_G128 || fmt > LOWBIT_TQ5_G128) return LOWBIT_ERR_ENUM;
   if (x_dtype < LOWBIT_F16 || x_dtype > LOWBIT_F32 || y_dtype < LOWBIT_F16 || y_dtype > LOWBIT_F32)
     return LOWBIT_ERR_ENUM;
@@ -22,6 +22,13 @@ int check_product(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, 
       M * N >= (int64_t(1) << 31) || packed_bytes_lowbit(fmt, N, K) >= (int64_t(1) << 31))
     return LOWBIT_ERR_SHAPE;
   if (x_dtype == LOWBIT_F32 || y_dtype == LOWBIT_BF16) return LOWBIT_ERR_DTYPE;
+  return LOWBIT_OK;
+}
+
+int check_product(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M,
+                  int64_t N, int64_t K) {
+  const int st = check_shape(fmt, x_dtype, y_dtype, M, N, K);
+  if (st != LOWBIT_OK) return st;
   if (M == 0 || N == 0) return LOWBIT_OK;
   if (!Y) return LOWBIT_ERR_NULL;
   if (K > 0 && (!Wp || !X)) return LOWBIT_ERR_NULL;
@@ -183,6 +190,81 @@ int gemm_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, in
   if (workspace_bytes < 0) return LOWBIT_ERR_SIZE;
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 15)) return LOWBIT_ERR_ALIGN;
   return run(true, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, workspace, workspace_bytes, hip_stream);
+}
+
+// Plan queries: the launchers run their planning code with a.plan set and
+// record what they would launch instead of launching.  Pointers are
+// placeholders that no code dereferences; a non-null workspace stands for a
+// caller's buffer of workspace_bytes.
+int lowbit_gemv_plan(int fmt, int count, const int64_t *Ns, int x_dtype, int y_dtype, int64_t M, int64_t K,
+                     int64_t workspace_bytes, lowbit_plan *out) {
+  if (!out) return LOWBIT_ERR_NULL;
+  int st = check_multi_shape(fmt, count, Ns, M, K);
+  if (st != LOWBIT_OK) return st;
+  for (int i = 0; i < count; ++i) {
+    st = check_shape(fmt, x_dtype, y_dtype, M, Ns[i], K);
+    if (st != LOWBIT_OK) return st;
+  }
+  if (workspace_bytes < 0) return LOWBIT_ERR_SIZE;
+  *out = lowbit_plan{};
+  alignas(16) static const uint8_t dummy[16] = {};
+  LaunchArgs a;
+  a.nmat = 0;
+  for (int i = 0; i < count; ++i) {
+    if (Ns[i] == 0) continue;
+    a.Ws[a.nmat] = dummy;
+    a.Ys[a.nmat] = const_cast<uint8_t *>(dummy);
+    a.Ns[a.nmat] = Ns[i];
+    ++a.nmat;
+  }
+  if (M == 0 || a.nmat == 0) return LOWBIT_OK;
+  a.ws = workspace_bytes > 0 ? const_cast<uint8_t *>(dummy) : nullptr;
+  a.ws_bytes = workspace_bytes;
+  a.fmt = fmt;
+  a.W = a.Ws[0];
+  a.X = reinterpret_cast<const uint16_t *>(dummy);
+  a.Y = a.Ys[0];
+  a.x_bf16 = x_dtype == LOWBIT_BF16;
+  a.y_f16 = y_dtype == LOWBIT_F16;
+  a.M = M;
+  a.N = launch_rows(a.nmat, a.Ns);
+  a.K = K;
+  a.stream = nullptr;
+  a.plan = out;
+  if (K == 0) {
+    plan_record(a, LOWBIT_KERNEL_FILL_ZERO, 0, 256, 0).launches = a.nmat;
+    return LOWBIT_OK;
+  }
+  return launch_gemv(a) == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_DEVICE;
+}
+
+int lowbit_gemm_plan(int fmt, int x_dtype, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t workspace_bytes,
+                     lowbit_plan *out) {
+  if (!out) return LOWBIT_ERR_NULL;
+  const int st = check_shape(fmt, x_dtype, y_dtype, M, N, K);
+  if (st != LOWBIT_OK) return st;
+  if (workspace_bytes < 0) return LOWBIT_ERR_SIZE;
+  *out = lowbit_plan{};
+  if (M == 0 || N == 0) return LOWBIT_OK;
+  alignas(16) static const uint8_t dummy[16] = {};
+  LaunchArgs a;
+  a.ws = workspace_bytes > 0 ? const_cast<uint8_t *>(dummy) : nullptr;
+  a.ws_bytes = workspace_bytes;
+  a.fmt = fmt;
+  a.W = dummy;
+  a.X = reinterpret_cast<const uint16_t *>(dummy);
+  a.Y = const_cast<uint8_t *>(dummy);
+  a.x_bf16 = x_dtype == LOWBIT_BF16;
+  a.y_f16 = y_dtype == LOWBIT_F16;
+  a.M = M; a.N = N; a.K = K;
+  a.stream = nullptr;
+  a.plan = out;
+  single_matrix(a);
+  if (K == 0) {
+    plan_record(a, LOWBIT_KERNEL_FILL_ZERO, 0, 256, 0);
+    return LOWBIT_OK;
+  }
+  return launch_gemm(a) == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_DEVICE;
 }
 
 }  // extern "C"

@@ -717,6 +717,22 @@ hipError_t launch_t(const LaunchArgs &a) {
     grid = int(tiles);
   }
   const int lds = kStages * (kStageBytes + w_stage_bytes<FMT>());
+  if (a.plan) {
+    lowbit_plan &o = plan_record(a, LOWBIT_KERNEL_GEMM, grid, threads_of<FMT>(), lds);
+    o.token_slots = kBM;
+    o.operands = BF ? LOWBIT_OPERANDS_BF16 : LOWBIT_OPERANDS_F16;
+    o.tiles_per_wave = nbw<FMT>();
+    o.ring = kStages;
+    o.items_per_wg = p.per;
+    if constexpr (FMT == 1 && BF) {
+      if (a.ws && a.ws_bytes >= x_pieces_offset<FMT>() + x_pieces_bytes(a.M, a.K)) {
+        o.x_pieces = 1;
+        o.launches = 2;
+        o.operands = LOWBIT_OPERANDS_FP8_FP4;
+      }
+    }
+    return hipSuccess;
+  }
   if constexpr (FMT == 1 && BF) {
     // Binary weights with bf16 x: x enters as fp8 pieces when the workspace
     // holds them (exact enough for binary weights: see the GEMV split path).

@@ -579,6 +579,23 @@ hipError_t launch_mt_full(const LaunchArgs &a) {
   constexpr int DB = (FMT == 1 && RB < 4) ? 3 : 2;
   const double c1 = make_plan<FMT, BF, MT, RA, DA, FP4, FULL>(a, p1, g1, l1);
   const double c2 = make_plan<FMT, BF, MT, RB, DB, FP4, FULL>(a, p2, g2, l2);
+  if (a.plan) {
+    const bool one = c1 < c2;
+    const GemvParams &p = one ? p1 : p2;
+    lowbit_plan &o = plan_record(a, LOWBIT_KERNEL_GEMV_STAGED, one ? g1 : g2, kThreads, one ? l1 : l2);
+    o.token_slots = MT;
+    o.operands = FP4 ? LOWBIT_OPERANDS_FP8_FP4 : (BF ? LOWBIT_OPERANDS_BF16 : LOWBIT_OPERANDS_F16);
+    o.whole_tiles = FULL;
+    o.tiles_per_wave = one ? RA : RB;
+    o.ring = one ? DA : DB;
+    o.waves_per_tile = p.S;
+    o.groups_per_range = 4 * ((p.chunks + p.S - 1) / p.S);
+    o.groups_per_pass = 4 * p.SC;
+    o.lds_offsets[0] = p.off_corr;
+    o.lds_offsets[1] = p.off_x;
+    o.lds_offsets[2] = p.off_red;
+    return hipSuccess;
+  }
   if (c1 < c2)
     hipLaunchKernelGGL((gemv_kernel<FMT, BF, MT, RA, DA, FP4, FULL>), dim3(g1), dim3(kThreads), l1, a.stream, p1);
   else
@@ -655,8 +672,9 @@ int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemv(const LaunchArgs &a) {
-  // Token blocks of at most 16 rows share one pass over the weights.
-  for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
+  // Token blocks of at most 16 rows share one pass over the weights.  A plan
+  // query records the first block's launch and counts the blocks.
+  for (int64_t m0 = 0; m0 < a.M; m0 += a.plan ? a.M : 16) {
     LaunchArgs b = a;
     b.M = a.M - m0 < 16 ? a.M - m0 : 16;
     b.X = a.X + m0 * a.K;
@@ -667,6 +685,7 @@ hipError_t launch_gemv(const LaunchArgs &a) {
     else if (a.fmt == 2) e = a.x_bf16 ? launch_fmt<2, true>(b) : launch_fmt<2, false>(b);
     else e = launch_gemv_tq5(b);
     if (e != hipSuccess) return e;
+    if (a.plan) a.plan->launches = int((a.M + 15) / 16);
   }
   return hipSuccess;
 }

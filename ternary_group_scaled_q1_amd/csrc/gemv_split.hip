@@ -498,6 +498,18 @@ hipError_t launch_split_full(const LaunchArgs &a) {
     pl.p.count = static_cast<unsigned *>(a.ws);
     pl.p.part = reinterpret_cast<float *>(static_cast<char *>(a.ws) + kPartOffset);
   }
+  if (a.plan) {
+    lowbit_plan &o = plan_record(a, LOWBIT_KERNEL_GEMV_SPLIT, pl.grid, 64 * NW, pl.lds);
+    o.token_slots = MP;
+    o.operands = MODE == kFp4 ? LOWBIT_OPERANDS_FP8_FP4 : (MODE == kBf16 ? LOWBIT_OPERANDS_BF16 : LOWBIT_OPERANDS_F16);
+    o.whole_tiles = FULL;
+    o.tiles_per_wave = NW == 12 ? 1 : R;
+    o.k_ranges = pl.p.KS;
+    o.groups_per_range = pl.p.GK;
+    o.groups_per_pass = pl.p.GP;
+    o.ring = 2;
+    return hipSuccess;
+  }
   const dim3 grid(pl.grid), block(64 * NW);
   if (NW == 12)
     hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL, 12>), grid, block, pl.lds, a.stream, pl.p);

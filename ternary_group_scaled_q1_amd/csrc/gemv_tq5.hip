@@ -602,6 +602,18 @@ hipError_t launch_tq5_x(const LaunchArgs &a) {
   const int lds = XL ? t5_xlds_bytes(a.K) : 0;
   const double c1 = plan_tq5(a, 1, &gemv_tq5_kernel<BF, 1, XL>, lds, p1, g1);
   const double c2 = plan_tq5(a, 2, &gemv_tq5_kernel<BF, 2, XL>, lds, p2, g2);
+  if (a.plan) {
+    const bool one = c1 <= c2 * 1.1;
+    const T5Params &p = one ? p1 : p2;
+    lowbit_plan &o = plan_record(a, LOWBIT_KERNEL_GEMV_TQ5, one ? g1 : g2, kT5Threads, lds);
+    o.token_slots = 16;
+    o.operands = BF ? LOWBIT_OPERANDS_BF16 : LOWBIT_OPERANDS_F16;
+    o.tiles_per_wave = one ? 1 : 2;
+    o.ring = 2;
+    o.waves_per_tile = p.S;
+    o.groups_per_range = 5 * p.SS;
+    return hipSuccess;
+  }
   if (c1 <= c2 * 1.1)
     hipLaunchKernelGGL((gemv_tq5_kernel<BF, 1, XL>), dim3(g1), dim3(kT5Threads), lds, a.stream, p1);
   else
@@ -649,6 +661,17 @@ hipError_t launch_tq5_one(const LaunchArgs &a) {
   int grid;
   const int lds = t5_xlds_bytes(a.K);
   plan_tq5_one(a, reinterpret_cast<const void *>(&gemv_tq5_one_kernel<BF, 1>), lds, p, grid);
+  if (a.plan) {
+    lowbit_plan &o = plan_record(a, LOWBIT_KERNEL_GEMV_TQ5_ONE, grid, kT5Threads, lds);
+    o.token_slots = 1;
+    o.operands = BF ? LOWBIT_OPERANDS_BF16 : LOWBIT_OPERANDS_F16;
+    o.tiles_per_wave = 1;
+    o.ring = 3;
+    o.waves_per_tile = p.S;
+    o.groups_per_range = 5 * p.SS;
+    o.groups_per_pass = p.G;
+    return hipSuccess;
+  }
   hipLaunchKernelGGL((gemv_tq5_one_kernel<BF, 1>), dim3(grid), dim3(kT5Threads), lds, a.stream, p);
   return hipGetLastError();
 }

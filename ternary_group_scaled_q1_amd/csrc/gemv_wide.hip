@@ -278,6 +278,18 @@ hipError_t launch_wide_t(const LaunchArgs &a) {
   int g1, g2;
   const double c1 = plan_wide(a, 2, &gemv_wide_kernel<FMT, BF, 2, D>, p1, g1);
   const double c2 = plan_wide(a, 4, &gemv_wide_kernel<FMT, BF, 4, D>, p2, g2);
+  if (a.plan) {
+    const bool two = c1 <= c2 * 1.1;
+    const WideParams &p = two ? p1 : p2;
+    lowbit_plan &o = plan_record(a, LOWBIT_KERNEL_GEMV_WIDE, two ? g1 : g2, kThreads, 0);
+    o.token_slots = 16;
+    o.operands = BF ? LOWBIT_OPERANDS_BF16 : LOWBIT_OPERANDS_F16;
+    o.tiles_per_wave = two ? 2 : 4;
+    o.ring = D;
+    o.waves_per_tile = p.S;
+    o.groups_per_range = p.GS;
+    return hipSuccess;
+  }
   if (c1 <= c2 * 1.1)
     hipLaunchKernelGGL((gemv_wide_kernel<FMT, BF, 2, D>), dim3(g1), dim3(kThreads), 0, a.stream, p1);
   else

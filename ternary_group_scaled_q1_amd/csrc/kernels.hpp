@@ -28,7 +28,25 @@ struct LaunchArgs {
   const uint8_t *Ws[kMaxMats] = {};
   void *Ys[kMaxMats] = {};
   int64_t Ns[kMaxMats] = {};
+  // When set, the launchers record the plan of the call here and launch
+  // nothing (lowbit_gemv_plan / lowbit_gemm_plan).
+  lowbit_plan *plan = nullptr;
 };
+
+// Starts a plan record: kernel, one launch of `grid` workgroups.
+inline lowbit_plan &plan_record(const LaunchArgs &a, int kernel, int grid, int threads, int lds) {
+  lowbit_plan &o = *a.plan;
+  o = lowbit_plan{};
+  o.kernel = kernel;
+  o.launches = 1;
+  o.grid = grid;
+  o.threads = threads;
+  o.lds_bytes = lds;
+  o.waves = threads / 64;
+  o.waves_per_tile = 1;
+  o.k_ranges = 1;
+  return o;
+}
 
 // Fills the matrix list of a single-matrix launch.
 inline void single_matrix(LaunchArgs &a) {

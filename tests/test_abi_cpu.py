@@ -28,7 +28,57 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(lb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert lb.abi_version() == 4
+    assert lb.abi_version() == 5
+
+
+PAGES = ("lnrk.cn page", "ksqn.cn page", "cnblogs.com page", "aberweb.com page")
+
+
+def declaration_comments():
+    """(function name, the comment block nearest before its declaration)."""
+    text = open(HEADER).read()
+    out = []
+    for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M):
+        before = text[:m.start()]
+        if before.rfind("/*") < 0 or before.rfind("*/") < before.rfind("/*"):
+            continue  # inside a comment
+        c0 = before.rfind("/*")
+        out.append((m.group(1), re.sub(r"\s+", " ", before[c0:])))
+    return out
+
+
+def test_every_declaration_cites_a_page():
+    """Each exported call of the C ABI names the passage that defines what it
+    does (or, for a variant for callers that cannot allocate, says so)."""
+    decls = declaration_comments()
+    assert {n for n, _ in decls} == set(declared_functions())
+    for name, comment in decls:
+        assert any(p in comment for p in PAGES) or "cannot allocate" in comment, name
+
+
+def test_plan_query_reaches_the_timed_plans():
+    """The plan query runs the launchers' own planning code without a GPU
+    (256 compute units assumed): the 16-token LM head of the decode sweep
+    takes the split kernel with two row tiles per wave and all of K, the
+    16-token q/k/v launch cuts K, and one token takes the staged kernel."""
+    K = 5120
+    ws = lb.gemv_multi_workspace_bytes("q1", [5120] * 3, 16, K)
+    p = lb.gemv_plan("q1", [5120] * 3, 16, K, workspace_bytes=ws)
+    assert p["kernel_name"] == "gemv_split" and p["k_ranges"] > 1 and p["operands_name"] == "fp8_fp4"
+    for fmt, ops in (("q1", "fp8_fp4"), ("tq2", "bf16")):
+        p = lb.gemv_plan(fmt, 151936, 16, K, workspace_bytes=lb.gemv_workspace_bytes(fmt, 16, 151936, K))
+        assert (p["kernel_name"], p["tiles_per_wave"], p["k_ranges"], p["waves"], p["operands_name"]) == \
+            ("gemv_split", 2, 1, 8, ops), p
+    assert lb.gemv_plan("q1", 5120, 1, K)["kernel_name"] == "gemv_staged"
+    assert lb.gemv_plan("q1", 5120, 40, K)["launches"] == 3
+    assert lb.gemv_plan("tq5", 34816, 1, K)["kernel_name"] == "gemv_tq5_one"
+    assert lb.gemv_plan("q1", 5120, 3, 0)["kernel_name"] == "fill_zero"
+    assert lb.gemv_plan("q1", 0, 3, K)["kernel_name"] == "none"
+    g = lb.gemm_plan("q1", 512, 17408, K, workspace_bytes=lb.gemm_workspace_bytes("q1", 512, 17408, K))
+    assert g["kernel_name"] == "gemm" and g["x_pieces"] == 1 and g["launches"] == 2
+    assert lb.gemm_plan("q1", 512, 17408, K)["items_per_wg"] == K // 128  # no workspace: whole tiles
+    with pytest.raises(lb.LowbitError):
+        lb.gemv_plan("q1", 16, 1, 100)
 
 
 def test_strerror_covers_all_codes():
@@ -134,7 +184,7 @@ def test_device_calls_validate_before_launch():
 def test_gemv_workspace_sizes():
     """32 KiB of arrival counters, then the partial sums of at most 16 K
     ranges and 8 MiB (16-token launches); none when fewer than two ranges fit;
-    tq5 (it runs on the GEMM kernel) needs none; shape errors reported."""
+    tq5 (its decode kernels never cut K across workgroups) needs none; shape errors reported."""
     L = lb.load()
 
     def rule(M, N, K):
