@@ -168,6 +168,20 @@ int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, in
                 int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
                 void *hip_stream);
 
+/* Decode GEMV for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It is
+ * gemv_lowbit with its workspace in a device array inside the library
+ * (8 MiB + 32 KiB on each device it runs on, held until the process ends)
+ * instead of a caller's buffer: same arguments without the workspace, same
+ * kernels, plans and results as gemv_lowbit given a workspace of that size.
+ * It calls no hipMalloc, hipFree or allocating library routine.  A problem
+ * whose fastest path would need a larger workspace is refused with
+ * LOWBIT_ERR_SIZE (no shape needs one today).  All calls on one device share
+ * that device's array and leave its counters at zero: calls that may overlap
+ * in time on one device (two streams, two host threads) race on it. */
+int gemv_lowbit_noalloc(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype,
+                        int64_t M, int64_t N, int64_t K, void *hip_stream);
+
 /* Matrices one fused decode call may cover (the query / key / value or
  * gate / up projections of a block share x; lnrk.cn page, DSpark section). */
 #define LOWBIT_MAX_FUSED 4

@@ -78,6 +78,7 @@ def load() -> ctypes.CDLL:
         "gemv_multi_lowbit": (i32, [i32, i32, vp, vp, vp, i32, vp, i32, i64, i64, vp, i64, vp]),
         "gemm_workspace_bytes_lowbit": (i64, [i32, i64, i64, i64]),
         "gemm_lowbit": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp, i64, vp]),
+        "gemv_lowbit_noalloc": (i32, [i32, vp, vp, i32, vp, i32, i64, i64, i64, vp]),
         "lowbit_gemv_plan": (i32, [i32, i32, vp, i32, i32, i64, i64, i64, ctypes.POINTER(Plan)]),
         "lowbit_gemm_plan": (i32, [i32, i32, i32, i64, i64, i64, i64, ctypes.POINTER(Plan)]),
     }

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblowbit.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "gemv.hip", "gemv_wide.hip", "gemv_split.hip", "gemv_tq5.hip", "gemm.hip", "device_props.cpp", "pack.cpp"]
+SOURCES = ["api.hip", "noalloc.hip", "gemv.hip", "gemv_wide.hip", "gemv_split.hip", "gemv_tq5.hip", "gemm.hip", "device_props.cpp", "pack.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -119,6 +119,27 @@ int gemv_lowbit(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, in
   return run(false, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, workspace, workspace_bytes, hip_stream);
 }
 
+int gemv_lowbit_noalloc(int fmt, const void *Wp, const void *X, int x_dtype, void *Y, int y_dtype, int64_t M,
+                        int64_t N, int64_t K, void *hip_stream) {
+  const int st = check_product(fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K);
+  if (st != LOWBIT_OK || M == 0 || N == 0) return st;
+  if (K == 0) return run(false, fmt, Wp, X, x_dtype, Y, y_dtype, M, N, K, nullptr, 0, hip_stream);
+  if (gemv_workspace_bytes(fmt, M < 16 ? M : 16, N, K) > noalloc_scratch_bytes()) return LOWBIT_ERR_SIZE;
+  LaunchArgs a;
+  a.fmt = fmt;
+  a.W = static_cast<const uint8_t *>(Wp);
+  a.X = static_cast<const uint16_t *>(X);
+  a.Y = Y;
+  a.x_bf16 = x_dtype == LOWBIT_BF16;
+  a.y_f16 = y_dtype == LOWBIT_F16;
+  a.M = M; a.N = N; a.K = K;
+  a.ws = nullptr;
+  a.ws_bytes = 0;
+  a.stream = static_cast<hipStream_t>(hip_stream);
+  single_matrix(a);
+  return gemv_noalloc(a);
+}
+
 int64_t gemm_workspace_bytes_lowbit(int fmt, int64_t M, int64_t N, int64_t K) {
   if (fmt < LOWBIT_Q1_G128 || fmt > LOWBIT_TQ5_G128) return LOWBIT_ERR_ENUM;
   if (M < 0 || N < 0 || K < 0 || K % kGroup) return LOWBIT_ERR_SHAPE;

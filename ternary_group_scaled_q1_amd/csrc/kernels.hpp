@@ -71,6 +71,10 @@ hipError_t launch_gemm(const LaunchArgs &a);
 // Workspace bytes that let launch_gemm split tiles across workgroups (stream-K).
 int64_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 hipError_t launch_fill_zero(void *Y, int64_t bytes, hipStream_t stream);
+// Bytes of the library's own decode workspace (gemv_lowbit_noalloc), and the
+// call that runs a decode product on it (returns a LOWBIT_* status).
+int64_t noalloc_scratch_bytes();
+int gemv_noalloc(const LaunchArgs &a);
 
 // Compute units of the current device (cached per device, thread-safe).
 int num_cus();
