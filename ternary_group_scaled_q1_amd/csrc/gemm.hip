@@ -594,6 +594,23 @@ __global__ void __launch_bounds__(threads_of<FMT>()) gemm_kernel(GemmParams p) {
       return;
     }
     // Split tile: publish this piece (slot 0: this range's first tile, 1: its last).
+    // Memory ordering.  All three steps below are relaxed atomics, so the HIP
+    // memory model alone orders nothing between them; the order comes from
+    // gfx950's memory pipeline, as follows.
+    //  * Agent-scope atomic stores and loads compile to global_store / load
+    //    with sc1: they write through to, and read from, the device's
+    //    coherence point, past this XCD's own L2, so no stale copy can be read
+    //    and no dirty copy can stay behind in another XCD's L2.
+    //  * s_waitcnt vmcnt(0) returns only once this thread's stores have been
+    //    acknowledged, and the barrier holds thread 0 until every thread of
+    //    the workgroup has passed its own wait.
+    //  * The counter add is issued after that barrier.  Agent-scope atomics
+    //    are coherent across the XCDs (one order of adds per counter).  The
+    //    last workgroup issues its loads only after its add has returned:
+    //    they depend on the result through the LDS flag and a barrier.
+    // A release / acquire pair would add an L2 write-back before the add and
+    // an L2 invalidate after it, on every workgroup of every launch.  The
+    // partial sums never pass through an L2, so neither is needed.
     const int which = tile == first_tile ? 0 : 1;
     const int wf = which ? wf1 : wf0, wl = which ? wl1 : wl0;
     float *piece = p.part + ((int64_t)blockIdx.x * 2 + which) * piece_floats<FMT>();
