@@ -16,7 +16,13 @@ value = HBM GB/s of the decode GEMVs: algorithmic bytes (packed weights +
 scales + x + y of every launch) / GPU time of the sweeps (HIP events on the
 launch stream).  Prefill TFLOP/s = 2*M*N*K / GPU time of each GEMM.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+Outside the timed step the same line also reports: single-launch timings of
+every workload shape and sweep launch over a >= 1 GiB rotation pool, each next
+to a plain streaming read of the same bytes (`shapes`); platform probes
+(`platform_probes`); what each part multiplies (`arithmetic`); and the CPU
+oracle on the host cores (`cpu_baseline`).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-shapes] [--only PART]
 """
 from __future__ import annotations
 
@@ -50,7 +56,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=1.0,
+                    help="seconds of oracle time per (workload shape, thread setting) of the CPU baseline")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape launch timings")
     ap.add_argument("--print-source-digest", action="store_true")
     ap.add_argument("--only", default=None,
                     help="run one part only, for counter passes: a sweep (q1_M1, q1_M16, tq2_M1, tq2_M16) "
@@ -71,7 +79,9 @@ def gen_weights_gpu(torch, lb, fmt, layers, seed):
 
     Plane A: q1 signs are i.i.d. Bernoulli(0.5), so the plane is i.i.d.
     uniform bytes (the layout only permutes bits); tq2 codes are i.i.d. with
-    P(t=0) = 0.3, P(t=+-1) = 0.35 each, four whole 2-bit codes per byte.
+    P(t=0) = 0.3, P(t=+-1) = 0.35 each, four whole 2-bit codes per byte; tq5
+    bytes are uniform below 243 (five uniform trits each; the padding digits
+    of a row's last byte are never read).
     Plane B: FP16 scales |N(0, 0.02)| + 1e-3.
     """
     gen = torch.Generator(device="cuda")
@@ -82,9 +92,11 @@ def gen_weights_gpu(torch, lb, fmt, layers, seed):
         total += (lb.packed_bytes(fmt, N, K) + 255) // 256 * 256
     buf = torch.empty(total, dtype=torch.uint8, device="cuda")
     for (N, K), off in zip(layers, offs):
-        a = N * K // (8 if fmt == "q1" else 4)
+        a = lb.packed_bytes(fmt, N, K) - N * (K // 128) * 2
         if fmt == "q1":
             plane = torch.randint(0, 256, (a,), dtype=torch.uint8, device="cuda", generator=gen)
+        elif fmt == "tq5":  # five uniform trits per byte: a uniform byte below 3^5
+            plane = torch.randint(0, 243, (a,), dtype=torch.uint8, device="cuda", generator=gen)
         else:
             r = torch.randint(0, 20, (a, 4), dtype=torch.uint8, device="cuda", generator=gen)
             c = (r >= 7).to(torch.uint8) + (r >= 13).to(torch.uint8)  # 0:-1 (0.35), 1:0 (0.3), 2:+1 (0.35)
@@ -286,6 +298,8 @@ def main():
                          "kernel": f"gemm {fmt} {M}x{N}x{K}", "avg_launch_us": round(gt * 1e3, 3)}
 
     probes = platform_probes(torch, dev) if args.only is None else None
+    shapes = None if (args.only is not None or args.no_shapes) else shape_timings(torch, lb, dev, args.seed)
+    arithmetic = part_arithmetic(lb, sweeps, gemm_ids, launches, layers, ws_bytes, gws_bytes)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     out = {
@@ -299,18 +313,81 @@ def main():
                                "+ prefill GEMM M=512 (q1 17408x5120, tq5 5120x17408)",
                    "hbm_fraction": round(value / HBM_PEAK_GBS, 4) if value is not None else None,
                    "only": args.only},
-        "sweeps": per_sweep, "prefill_gemm": gemm_out,
-        "roofline": roofline, "roofline_gemm": roofline_gemm, "platform_probes": probes, "cpu_baseline": cpu,
+        "sweeps": per_sweep, "prefill_gemm": gemm_out, "arithmetic": arithmetic,
+        "roofline": roofline, "roofline_gemm": roofline_gemm, "platform_probes": probes,
+        "shapes": shapes, "cpu_baseline": cpu,
     }
     print(json.dumps(out))
 
 
+def load_probes():
+    """libprobes.so: the plain streaming-read, MFMA and empty kernels the
+    platform probes time (built next to liblowbit.so; no part of the product)."""
+    import ctypes
+    path = os.path.join(ROOT, "ternary_group_scaled_q1_amd", "libprobes.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m ternary_group_scaled_q1_amd.build`")
+    lib = ctypes.CDLL(path)
+    i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    lib.probe_stream_read.restype, lib.probe_stream_read.argtypes = i32, [vp, i64, vp, i32, vp]
+    lib.probe_mfma_bf16.restype, lib.probe_mfma_bf16.argtypes = i32, [vp, i32, i32, vp]
+    lib.probe_empty.restype, lib.probe_empty.argtypes = i32, [vp]
+    return lib
+
+
+def read_grid(nbytes):
+    """Workgroups of 512 lanes for a streaming read of nbytes (about four
+    16-byte loads per lane, at least one workgroup per CU)."""
+    return int(min(max(nbytes // (16 * 512 * 4), 256), 8192))
+
+
+def _graph_time_ms(torch, fn, reps=5):
+    """Median over reps replays of a HIP graph holding fn's launches (one
+    untimed replay first); HIP events on the replay stream."""
+    import warnings
+    g = torch.cuda.CUDAGraph()
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")  # an empty capture means launches went to another stream
+        with torch.cuda.graph(g):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del g
+    return sorted(times)[len(times) // 2]
+
+
 def platform_probes(torch, dev):
-    """What this machine sustains outside this library, as context for the
-    rooflines (untimed by the step): a 1 GiB device copy (HBM read + write)
-    and torch's dense bf16 matmul (the platform BLAS) at the q1 prefill
-    shape 512 x 17408 x 5120, with N(0,1) operands."""
+    """What this machine sustains with plain kernels, as context for the
+    rooflines (untimed by the step):
+      * stream_read_GBps: the committed streaming-read kernel over 4 GiB;
+      * hbm_copy_GBps: a 1 GiB device copy (read + write bytes);
+      * mfma_bf16_TFLOPs: the committed MFMA kernel, four chains of
+        v_mfma_f32_16x16x32_bf16 per wave with +-1 B operands that change
+        every step, 16 waves per CU;
+      * empty_launch_us: an empty kernel, per launch in a graph of 256;
+      * dense_bf16_matmul_TFLOPs: torch's matmul (the platform BLAS) at the
+        q1 prefill shape 512 x 17408 x 5120."""
+    pr = load_probes()
+
+    def cs():  # the stream launches go to (graph capture switches it)
+        return torch.cuda.current_stream(dev).cuda_stream
+
     out = {}
+    sink = torch.zeros(4096, device=dev, dtype=torch.uint8)
+    buf = torch.empty(4 << 30, device=dev, dtype=torch.uint8)
+    n = buf.numel()
+    ms = _graph_time_ms(torch, lambda: [pr.probe_stream_read(buf.data_ptr(), n, sink.data_ptr(), 8192, cs())
+                                        for _ in range(4)])
+    out["stream_read_GBps"] = round(4 * n / (ms * 1e-3) / 1e9, 1)
+    del buf
     src = torch.empty(1 << 28, device=dev, dtype=torch.float32).normal_()
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -323,6 +400,12 @@ def platform_probes(torch, dev):
     torch.cuda.synchronize()
     out["hbm_copy_GBps"] = round(2 * src.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     del src, dst
+    mo = torch.zeros(4096, device=dev, dtype=torch.float32)
+    grid, iters = 512, 20000
+    ms = _graph_time_ms(torch, lambda: pr.probe_mfma_bf16(mo.data_ptr(), iters, grid, cs()), reps=3)
+    out["mfma_bf16_TFLOPs"] = round(grid * 8 * 4 * iters * 16384 / (ms * 1e-3) / 1e12, 1)
+    ms = _graph_time_ms(torch, lambda: [pr.probe_empty(cs()) for _ in range(256)])
+    out["empty_launch_us"] = round(ms * 1e3 / 256, 3)
     M, N, K = 512, 17408, 5120
     a = torch.randn((M, K), device=dev).to(torch.bfloat16)
     b = torch.randn((K, N), device=dev).to(torch.bfloat16).contiguous()
@@ -336,6 +419,102 @@ def platform_probes(torch, dev):
     out["dense_bf16_matmul_TFLOPs"] = round(2 * M * N * K * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
     out["dense_bf16_matmul_shape"] = f"{M}x{N}x{K}"
     del a, b, c
+    return out
+
+
+# Single-launch timings: (label, format, fused row counts, K, tokens, x dtype).
+# The workload shapes of the 8B-class q1 decode, the 27B-class tq2 (and tq5)
+# decode, and every distinct launch of the sweep; the first is the small
+# latency case (L2-resident, no bandwidth claim).
+SHAPES = ([("q1 256x1024 M=1 f16 (latency)", "q1", [256], 1024, 1, "f16")]
+          + [(f"q1 {N}x{K} M=1 f16", "q1", [N], K, 1, "f16") for N, K in ((24576, 4096), (4096, 12288), (151936, 4096))]
+          + [(f"tq2 {N}x{K} M={m} bf16", "tq2", [N], K, m, "bf16") for N, K in ((34816, 5120), (5120, 17408))
+             for m in (1, 4, 8)]
+          + [(f"tq5 {N}x{K} M={m} bf16", "tq5", [N], K, m, "bf16") for N, K in ((34816, 5120), (5120, 17408))
+             for m in (1, 8)]
+          + [(f"{f} sweep {name} M={m} bf16", f, Ns, K, m, "bf16") for f in ("q1", "tq2") for m in (1, 16)
+             for name, Ns, K in (("qkv", [5120] * 3, 5120), ("o", [5120], 5120), ("gate_up", [17408] * 2, 5120),
+                                 ("down", [5120], 17408), ("lm_head", [151936], 5120))])
+POOL_BYTES = 1 << 30  # rotation pool: at least 4x the 256 MB last-level cache
+
+
+def shape_timings(torch, lb, dev, seed):
+    """Per-launch time of each shape in SHAPES, the launch repeated over a
+    rotation pool of >= 1 GiB of distinct weight copies (so no launch finds
+    its weights in a cache), next to the committed streaming-read kernel
+    reading the same bytes of the same buffers; median of 5 graph replays."""
+    pr = load_probes()
+    sink = torch.zeros(4096, device=dev, dtype=torch.uint8)
+    out = {}
+    for label, fmt, Ns, K, M, xdt in SHAPES:
+        latency = "latency" in label
+        wbytes = sum(lb.packed_bytes(fmt, N, K) for N in Ns)
+        copies = 1 if latency else max(4, -(-POOL_BYTES // wbytes))
+        layers = [(N, K) for _ in range(copies) for N in Ns]
+        buf, offs = gen_weights_gpu(torch, lb, fmt, layers, seed)
+        x = torch.randn((M, K), device=dev).to(torch.bfloat16 if xdt == "bf16" else torch.float16)
+        ys = [torch.empty((M, N), device=dev, dtype=torch.float32) for N in Ns]
+        wsb = lb.gemv_multi_workspace_bytes(fmt, Ns, M, K)
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+        f, xd = lb.FORMATS[fmt], lb.DT_BF16 if xdt == "bf16" else lb.DT_F16
+        base = buf.data_ptr()
+        n_launch = 1000 if latency else copies * max(1, -(-32 // copies))
+
+        def launches():
+            s = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(n_launch):
+                c = (i % copies) * len(Ns)
+                if len(Ns) == 1:
+                    lb.gemv_raw(f, base + offs[c], x.data_ptr(), xd, ys[0].data_ptr(), lb.DT_F32, M, Ns[0], K, s,
+                                ws.data_ptr(), wsb)
+                else:
+                    lb.gemv_multi_raw(f, [base + offs[c + j] for j in range(len(Ns))], Ns, x.data_ptr(), xd,
+                                      [y.data_ptr() for y in ys], lb.DT_F32, M, K, s, ws.data_ptr(), wsb)
+
+        span = offs[len(Ns) - 1] + lb.packed_bytes(fmt, Ns[-1], K)  # the weights of one launch, contiguous
+
+        def reads():
+            s = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(n_launch):
+                c = (i % copies) * len(Ns)
+                pr.probe_stream_read(base + offs[c], span // 16 * 16, sink.data_ptr(), read_grid(span), s)
+
+        us = _graph_time_ms(torch, launches) * 1e3 / n_launch
+        rd = _graph_time_ms(torch, reads) * 1e3 / n_launch
+        alg = wbytes + M * K * 2 + M * sum(Ns) * 4
+        plan = lb.gemv_plan(fmt, Ns, M, K, x_dtype=xdt, workspace_bytes=wsb)
+        e = {"us": round(us, 3), "read_probe_us": round(rd, 3), "bytes": alg,
+             "kernel": f"{plan['kernel_name']} ({plan['operands_name']}, grid {plan['grid']}, "
+                       f"{plan['k_ranges']} K ranges)"}
+        if not latency:
+            e.update({"GB_s": round(alg / (us * 1e-6) / 1e9, 1), "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "read_probe_GB_s": round(span / (rd * 1e-6) / 1e9, 1), "vs_read_probe": round(rd / us, 3),
+                      "pool_copies": copies})
+        out[label] = e
+        del buf, x, ys, ws
+        torch.cuda.empty_cache()
+    progress(f"shape timings: {len(out)}")
+    return out
+
+
+def part_arithmetic(lb, sweeps, gemm_ids, launches, layers, ws_bytes, gws_bytes):
+    """What each timed part multiplies, from the plan queries of its
+    launches: kernel and operand types (fp8_fp4 = bf16 x as two exact fp8
+    pieces x fp4 weights on the scaled MFMA; bf16 / f16 = exact operands on
+    v_mfma_f32_16x16x32); every part accumulates in fp32."""
+    out = {}
+    for fmt, m in sweeps:
+        kinds = {}
+        for L in launches:
+            p = lb.gemv_plan(fmt, [layers[i][0] for i in L], m, layers[L[0]][1], workspace_bytes=ws_bytes)
+            k = f"{p['kernel_name']} {p['operands_name']}"
+            kinds[k] = kinds.get(k, 0) + 1
+        out[f"{fmt}_M{m}"] = ", ".join(f"{k} x{v}" for k, v in sorted(kinds.items()))
+    for i in gemm_ids:
+        fmt, M, N, K, _ = GEMMS[i]
+        p = lb.gemm_plan(fmt, M, N, K, workspace_bytes=gws_bytes)
+        out[f"gemm_{fmt}"] = (f"{p['kernel_name']} {p['operands_name']}"
+                              + (" (x converted to fp8 pieces by a pre-pass launch)" if p["x_pieces"] else ""))
     return out
 
 
@@ -378,9 +557,48 @@ def measured_traffic(dom):
     return (fetch + write if fetch is not None and write is not None else None), fetch
 
 
-def cpu_baseline(budget_s):
-    """The oracle (float64 numpy: unpack the packed blob, then a dense
-    product) on a bounded sample of the decode workload, on the host cores."""
+# Workload shapes of the CPU baseline: (label, format, N, K, tokens, x dtype,
+# rows timed).  The oracle treats every weight row alike, so a block of rows
+# of full K, timed and scaled by N / rows, gives the full-shape time.
+CPU_CASES = [
+    ("q1 GEMV 256x1024 M=1", "q1", 256, 1024, 1, "f16", 256),
+    ("q1 GEMV 24576x4096 M=1", "q1", 24576, 4096, 1, "f16", 512),
+    ("q1 GEMV 4096x12288 M=1", "q1", 4096, 12288, 1, "f16", 256),
+    ("q1 GEMV 151936x4096 M=1", "q1", 151936, 4096, 1, "f16", 512),
+    ("tq2 GEMV 34816x5120 M=1", "tq2", 34816, 5120, 1, "bf16", 384),
+    ("tq2 GEMV 34816x5120 M=8", "tq2", 34816, 5120, 8, "bf16", 384),
+    ("tq2 GEMV 5120x17408 M=1", "tq2", 5120, 17408, 1, "bf16", 128),
+    ("tq2 GEMV 5120x17408 M=8", "tq2", 5120, 17408, 8, "bf16", 128),
+    ("q1 GEMM 512x17408x5120", "q1", 17408, 5120, 512, "bf16", 256),
+    ("tq5 GEMM 512x5120x17408", "tq5", 5120, 17408, 512, "bf16", 96),
+]
+
+
+def host_cpu():
+    """(CPU model, logical CPUs this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
+
+
+def cpu_baseline(budget_s, cases=None):
+    """The oracle as it stands (float64 numpy: its own unpack of the packed
+    blob, then a dense float64 product) on the host cores, on 1 thread and on
+    all of them, for every workload shape of configs 1-4.  Each shape is
+    timed on a block of weight rows of full K for about budget_s seconds and
+    scaled to its N.  value = packed GB/s of the decode shapes (configs 2
+    and 3) on all threads."""
     import numpy as np
 
     import synth
@@ -388,28 +606,55 @@ def cpu_baseline(budget_s):
     from oracle import ref
 
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    N, K, rows = 17408, 5120, 512
-    sweep = synth.WORKLOADS["decode_sweep_27b"]["stream"]
-    codes, sc = synth.draw_matrix(0, sweep, 0, rows, K, None)
-    blob = lb.pack("q1", codes, sc)
-    x = synth.draw_x(0, sweep, 0, 1, K, "bf16")
-    per_call_bytes = lb.packed_bytes("q1", rows, K) + K * 2 + rows * 4
-    t0 = time.perf_counter()
-    calls = 0
-    while True:
-        ref.product_from_blob("q1", blob, rows, K, x, "bf16")
-        calls += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(per_call_bytes * calls / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"q1 GEMV M=1, {rows} of the {N} rows of the 17408x5120 gate projection, x bf16; "
-                      f"{calls} calls in {dt:.1f} s (oracle unpacks the blob and takes a float64 product)"}
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_info, threadpool_limits = None, None
+    model, ncpu = host_cpu()
+    blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1]) if threadpool_info else 1
+    out, dec_bytes, dec_s = {}, 0, 0.0
+    for label, fmt, N, K, M, xdt, rows in cases or CPU_CASES:
+        p0 = None if fmt == "q1" else (1.0 / 3.0 if fmt == "tq5" else 0.3)
+        codes, sc = synth.draw_matrix(0, 90, len(out), rows, K, p0)
+        blob = lb.pack(fmt, codes, sc)
+        x = synth.draw_x(0, 90, len(out), M, K, xdt)
+        del codes, sc
+        res = {}
+        for tag, limit in (("1", 1), ("all", None)):
+            ctx = threadpool_limits(limits=limit) if (threadpool_limits and limit) else _nullctx()
+            with ctx:
+                calls, t0 = 0, time.perf_counter()
+                while True:
+                    ref.product_from_blob(fmt, blob, rows, K, x, xdt)
+                    calls += 1
+                    if time.perf_counter() - t0 >= budget_s:
+                        break
+                dt = (time.perf_counter() - t0) / calls * N / rows  # seconds per full-shape call
+            wb = lb.packed_bytes(fmt, N, K)
+            res[f"full_shape_s_{tag}"] = round(dt, 4)
+            res[f"weights_per_s_{tag}"] = round(N * K / dt, 1)
+            res[f"packed_GB_s_{tag}"] = round(wb / dt / 1e9, 5)
+            res[f"tok_s_{tag}"] = round(M / dt, 3)
+            if tag == "all" and "GEMV" in label and "256x1024" not in label:
+                dec_bytes += wb + M * K * 2 + M * N * 4
+                dec_s += dt
+        res["rows_timed"] = rows
+        out[label] = res
+    return {"value": round(dec_bytes / dec_s / 1e9, 5) if dec_s else None, "unit": "GB/s",
+            "cores": int(max(blas_threads, 1)), "kind": "oracle",
+            "sample": ("the oracle (its own unpack of the packed blob, then a float64 numpy product) on every "
+                       "workload shape of the 8B-class q1 decode, 27B-class tq2 decode and M=512 prefill; each shape "
+                       f"timed on a block of weight rows of full K for about {budget_s:g} s per thread setting and "
+                       "scaled to its N; value = packed GB/s over the decode shapes on all BLAS threads "
+                       "(unpack runs on one thread)"),
+            "cpu_model": model, "nproc": ncpu, "blas_threads_all": int(blas_threads), "per_shape": out}
+
+
+class _nullctx:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
 
 
 if __name__ == "__main__":

@@ -1,4 +1,6 @@
-"""Build liblowbit.so (HIP kernels for gfx950 + host packer + C ABI) in-tree.
+"""Build liblowbit.so (HIP kernels for gfx950 + host packer + C ABI) in-tree,
+and libprobes.so, the benchmark's platform probes (plain streaming-read,
+MFMA and empty kernels; no part of the product path).
 
     python -m ternary_group_scaled_q1_amd.build      # or build() from Python
 """
@@ -13,6 +15,8 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblowbit.so")
+PROBES_LIB = os.path.join(PKG, "libprobes.so")
+PROBES_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "noalloc.hip", "gemv.hip", "gemv_wide.hip", "gemv_split.hip", "gemv_tq5.hip", "gemm.hip", "device_props.cpp", "pack.cpp"]
@@ -37,11 +41,17 @@ EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
+    _build_lib(SOURCES, LIB, verbose, jobs)
+    _build_lib(PROBES_SOURCES, PROBES_LIB, verbose, jobs)
+    return LIB
+
+
+def _build_lib(sources, lib, verbose, jobs):
     hipcc = _hipcc()
     tmp = tempfile.mkdtemp(prefix="lowbit_build_")
     try:
         objs, procs = [], []
-        for src in SOURCES:
+        for src in sources:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
             cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -53,17 +63,17 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
                 _wait(procs.pop(0))
         while procs:
             _wait(procs.pop(0))
-        out_tmp = LIB + ".tmp"
+        out_tmp = lib + ".tmp"
         cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp, "-lpthread"]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stdout)
-        os.replace(out_tmp, LIB)
+        os.replace(out_tmp, lib)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return lib
 
 
 def _wait(item):

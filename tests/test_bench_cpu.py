@@ -78,7 +78,25 @@ def test_committed_summary_has_the_machine_readable_lines():
 
 
 def test_cpu_baseline_leg_reports_the_oracle():
-    r = bench.cpu_baseline(0.05)
+    cases = [("q1 GEMV 24576x4096 M=1", "q1", 24576, 4096, 1, "f16", 32),
+             ("tq5 GEMM 512x5120x17408", "tq5", 5120, 17408, 16, "bf16", 16)]
+    r = bench.cpu_baseline(0.01, cases=cases)
     assert r["kind"] == "oracle" and r["unit"] == "GB/s"
-    assert r["value"] > 0 and r["cores"] >= 1
-    assert "512 of the 17408 rows" in r["sample"]
+    assert r["value"] > 0 and r["cores"] >= 1 and r["nproc"] >= 1 and r["cpu_model"]
+    for label, *_ in cases:
+        e = r["per_shape"][label]
+        for tag in ("1", "all"):
+            assert e[f"full_shape_s_{tag}"] > 0 and e[f"weights_per_s_{tag}"] > 0 and e[f"tok_s_{tag}"] > 0
+
+
+def test_bench_shape_table_covers_the_workloads():
+    """Single-launch timings cover the 8B-class q1 decode shapes, the
+    27B-class tq2 shapes at 1, 4 and 8 tokens, and every sweep launch."""
+    labels = [s[0] for s in bench.SHAPES]
+    for N, K in ((24576, 4096), (4096, 12288), (151936, 4096)):
+        assert f"q1 {N}x{K} M=1 f16" in labels
+    for N, K in ((34816, 5120), (5120, 17408)):
+        for m in (1, 4, 8):
+            assert f"tq2 {N}x{K} M={m} bf16" in labels
+    assert sum("sweep" in lab for lab in labels) == 20
+    assert bench.POOL_BYTES >= 1 << 30
