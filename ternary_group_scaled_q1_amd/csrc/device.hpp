@@ -244,6 +244,15 @@ __device__ __forceinline__ void split_x_quarter(const uint16_t *src, bool in, XQ
   split_x_regs<FMT>(x, o);
 }
 
+// Workgroup barrier for data exchanged through LDS only: this wave's LDS
+// operations complete (lgkmcnt), then s_barrier.  __syncthreads() would also
+// wait for every global load in flight (its workgroup-scope fence includes
+// vmcnt(0)), draining the weight prefetch at every pass or tile set.  The
+// memory clobber keeps the compiler from moving any access across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float half_to_float(uint16_t h) {
   return float(__builtin_bit_cast(_Float16, h));
 }

@@ -422,7 +422,7 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
   if (!restage) {
     if constexpr (FP4) stage_fp4<FMT, MT, true>(p, lds, 0, p.chunks, xf);
     else stage_x<FMT, BF, MTS, true>(p, lds, 0, p.chunks, xf);
-    __syncthreads();
+    lds_barrier();
   }
 
   Cursor cu = {0, 0, 0};
@@ -448,11 +448,11 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
           for (int e = 0; e < 4; ++e) yacc[r][e] = 0.f;
       }
       if (restage && cu.kl == 0) {
-        __syncthreads();
+        lds_barrier();
         const int c0 = cu.st * p.SC;
         if constexpr (FP4) stage_fp4<FMT, MT, false>(p, lds, c0, min(p.SC, p.chunks - c0), xf);
         else stage_x<FMT, BF, MTS, false>(p, lds, c0, min(p.SC, p.chunks - c0), xf);
-        __syncthreads();
+        lds_barrier();
       }
       if (is_valid(cu)) {
         const int c_local = s + cu.kl * S;
@@ -476,7 +476,7 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
           for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int e = 0; e < E; ++e) red[((wave * R + r) * E + e) * 64 + lane] = yacc[r][e];
-          __syncthreads();
+          lds_barrier();
           if (s == 0 && ts_ok) {
             float tot[R][4];
 #pragma unroll
@@ -490,7 +490,7 @@ __global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
             if constexpr (FP4) store_fp4<FMT, R, E>(p, t0, tot);
             else store_tiles<FMT, R, E>(p, t0, tot);
           }
-          __syncthreads();
+          lds_barrier();
         }
       }
       advance(cu, U, p.n_stages);

@@ -228,7 +228,17 @@ __device__ __forceinline__ void compute_chunk_ex(const SplitParams &p, const cha
 // are fixed for the launch, so their addresses are resolved once and each
 // chunk is one load per tile at a fixed stride (the general path resolves
 // the tile and its ragged shape per chunk).
-template <int FMT, int MP, int R, int MODE, bool FULL, int NW>
+//
+// CPP > 0: every staging pass is CPP chunks (a compile-time count; CPP is
+// even, so a chunk's ring slot is fixed), the loop walks passes and the raw
+// x of the next pass is loaded on every path (past the range as zeros from a
+// clamped address).  Between the raw x of a pass and its conversion at the
+// next pass boundary there are then exactly CPP units of weight loads on
+// every path, so the wait for x is a count that leaves those in flight.  In
+// the general loop (CPP = 0) the number of loads between the two differs
+// between paths and the compiler waits for every load at each boundary,
+// which drains the weight ring once per pass.
+template <int FMT, int MP, int R, int MODE, bool FULL, int NW, int CPP>
 __global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(SplitParams p) {
   constexpr int kThreads = 64 * NW;
   // One fp32 tile per row tile: fp4 A rows hold (token, piece) pairs for up
@@ -275,9 +285,9 @@ __global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(Sp
       *reinterpret_cast<u4_t *>(lds + p.buf_bytes + p.GP * 16 * MP * 16) = u4_t{0u, 0u, 0u, 0u};
     }
   }
-  __syncthreads();
+  lds_barrier();
   // The raw x of pass 1 goes out while pass 0 is multiplied.
-  if (npass > 1) load_raw<MP>(p, raw, g0 + p.GP, min(p.GP, ng - p.GP), threadIdx.x, live);
+  if (CPP > 0 || npass > 1) load_raw<MP>(p, raw, g0 + p.GP, min(p.GP, ng - p.GP), threadIdx.x, live);
 
   float yacc[R][1][4];
 #pragma unroll
@@ -285,6 +295,33 @@ __global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(Sp
 #pragma unroll
     for (int e = 0; e < 4; ++e) yacc[r][0][e] = 0.f;
 
+  auto compute = [&](const char *cur, const Unit<FMT, R> &u, int cl, int png) {
+    if constexpr (MODE == kFp4 && MP > 8) compute_chunk16<FMT, MP, R>(p, cur, u, 4 * cl, min(4, png - 4 * cl), yacc);
+    else if constexpr (MODE == kFp4) compute_chunk<FMT, MP, R>(p, cur, u, 4 * cl, min(4, png - 4 * cl), yacc);
+    else compute_chunk_ex<FMT, MP, R, MODE>(p, cur, u, 4 * cl, min(4, png - 4 * cl), yacc);
+  };
+
+  if constexpr (CPP > 0) {
+    for (int ps = 0; ps < npass; ++ps) {
+      if (ps > 0) {
+        // The x of pass ps, loaded during pass ps - 1, goes into the buffer
+        // of pass ps - 2 (every wave left that pass before the previous
+        // barrier); then the raw x of pass ps + 1 goes out.
+        if (live) convert_raw<FMT, MP, MODE>(p, raw, lds + (ps & 1) * p.buf_bytes, threadIdx.x);
+        lds_barrier();
+        const int nx = (ps + 1) * p.GP;
+        load_raw<MP>(p, raw, g0 + nx, min(p.GP, ng - nx), threadIdx.x, live);
+      }
+      const char *cur = lds + (ps & 1) * p.buf_bytes;
+      const int png = min(p.GP, ng - ps * p.GP);
+#pragma unroll
+      for (int cl = 0; cl < CPP; ++cl) {
+        const int cc = ps * CPP + cl;  // chunk inside the K range
+        if (cc < nchunks) compute(cur, ring[cl % 2], cl, png);
+        load(ring[cl % 2], min(cc + 2, nchunks - 1));
+      }
+    }
+  } else {
   for (int c = 0; c < nchunks; c += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -296,18 +333,17 @@ __global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(Sp
           // the buffer of pass ps - 2 (every wave left that pass before the
           // previous barrier); then the raw x of pass ps + 1 goes out.
           if (live) convert_raw<FMT, MP, MODE>(p, raw, lds + (ps & 1) * p.buf_bytes, threadIdx.x);
-          __syncthreads();
+          lds_barrier();
           const int nx = (ps + 1) * p.GP;
           if (ps + 1 < npass) load_raw<MP>(p, raw, g0 + nx, min(p.GP, ng - nx), threadIdx.x, live);
         }
         const char *cur = lds + (ps & 1) * p.buf_bytes;
         const int png = min(p.GP, ng - ps * p.GP);
-        if constexpr (MODE == kFp4 && MP > 8) compute_chunk16<FMT, MP, R>(p, cur, ring[h], 4 * cl, min(4, png - 4 * cl), yacc);
-        else if constexpr (MODE == kFp4) compute_chunk<FMT, MP, R>(p, cur, ring[h], 4 * cl, min(4, png - 4 * cl), yacc);
-        else compute_chunk_ex<FMT, MP, R, MODE>(p, cur, ring[h], 4 * cl, min(4, png - 4 * cl), yacc);
+        compute(cur, ring[h], cl, png);
       }
       load(ring[h], min(cc + 2, nchunks - 1));
     }
+  }
   }
 
   // This lane's outputs: (tile r, token m, value).  fp4 up to 8 tokens:
@@ -471,6 +507,20 @@ bool make_split(const LaunchArgs &a, int gk, SplitPlan &pl) {
   return true;
 }
 
+template <int FMT, int MP, int MODE, bool FULL, int CPP>
+hipError_t launch_split_plan(const LaunchArgs &a, const SplitPlan &pl, int NW, int R) {
+  const dim3 grid(pl.grid), block(64 * NW);
+  if (NW == 12)
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL, 12, CPP>), grid, block, pl.lds, a.stream, pl.p);
+  else if (R == 1)
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL, kSWaves, CPP>), grid, block, pl.lds, a.stream, pl.p);
+  else if (R == 2)
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2, MODE, FULL, kSWaves, CPP>), grid, block, pl.lds, a.stream, pl.p);
+  else
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4, MODE, FULL, kSWaves, CPP>), grid, block, pl.lds, a.stream, pl.p);
+  return hipGetLastError();
+}
+
 // Plan, from timings of the decode shapes at 2..16 tokens on MI355X: a CU
 // that holds two workgroups runs each about 1.45x slower, and a workgroup's
 // time is a fixed part (x staging, the K-range reduction, launch) plus a
@@ -527,16 +577,10 @@ hipError_t launch_split_full(const LaunchArgs &a) {
     o.ring = 2;
     return hipSuccess;
   }
-  const dim3 grid(pl.grid), block(64 * NW);
-  if (NW == 12)
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL, 12>), grid, block, pl.lds, a.stream, pl.p);
-  else if (R == 1)
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 1, MODE, FULL, kSWaves>), grid, block, pl.lds, a.stream, pl.p);
-  else if (R == 2)
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 2, MODE, FULL, kSWaves>), grid, block, pl.lds, a.stream, pl.p);
-  else
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, MP, 4, MODE, FULL, kSWaves>), grid, block, pl.lds, a.stream, pl.p);
-  return hipGetLastError();
+  // Sixteen tokens stage x in passes of two chunks (pass_groups): those
+  // launches take the pass-structured loop.
+  if (MP == 16 && pl.p.GP == 8) return launch_split_plan<FMT, MP, MODE, FULL, 2>(a, pl, NW, R);
+  return launch_split_plan<FMT, MP, MODE, FULL, 0>(a, pl, NW, R);
 }
 
 // Every matrix of the launch has whole row tiles and K whole chunks.

@@ -199,7 +199,7 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
     }
     lut[v] = uint16_t(v < 243 ? f : 0);
   }
-  __syncthreads();
+  lds_barrier();
 
   const int wave = uni(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -316,7 +316,7 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
         for (int r = 0; r < R; ++r)
 #pragma unroll
           for (int e = 0; e < 4; ++e) red[((wave * R + r) * 4 + e) * 64 + lane] = yacc[r][e];
-        __syncthreads();
+        lds_barrier();
         if (s == 0 && ts_ok) {
           float tot[R][4];
 #pragma unroll
@@ -329,7 +329,7 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_kernel(T5Params p) {
             }
           t5_store<R>(p, t0, tot);
         }
-        __syncthreads();
+        lds_barrier();
       }
     }
   }
@@ -455,7 +455,7 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_one_kernel(T5Params p)
     }
     lut[v] = uint16_t(v < 243 ? f : 0);
   }
-  __syncthreads();
+  lds_barrier();
 
   float yacc[R][4];
   for (int i0 = 0; i0 < total; i0 += D) {
@@ -535,7 +535,7 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_one_kernel(T5Params p)
           for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int e = 0; e < 4; ++e) red[((wave * R + r) * 4 + e) * 64 + lane] = yacc[r][e];
-          __syncthreads();
+          lds_barrier();
           if (s == 0 && ts_ok) {
             float tot[R][4];
 #pragma unroll
@@ -548,7 +548,7 @@ __global__ void __launch_bounds__(kT5Threads, 2) gemv_tq5_one_kernel(T5Params p)
               }
             t5_store<R>(p, t0, tot);
           }
-          __syncthreads();
+          lds_barrier();
         }
       }
     }

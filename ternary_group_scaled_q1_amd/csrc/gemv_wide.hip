@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(kThreads, 2) gemv_wide_kernel(WideParams p) {
           for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int e = 0; e < 4; ++e) red[((wave * R + r) * 4 + e) * 64 + lane] = yacc[r][e];
-          __syncthreads();
+          lds_barrier();
           if (s == 0 && ts_ok) {
             float tot[R][4];
 #pragma unroll
@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(kThreads, 2) gemv_wide_kernel(WideParams p) {
               }
             store_wide<FMT, R>(p, t0, tot);
           }
-          __syncthreads();
+          lds_barrier();
         }
       }
     }

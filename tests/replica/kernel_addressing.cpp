@@ -273,6 +273,18 @@ void split_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X, Buf &ws) 
       }
     };
     stage(0);
+    // Sixteen tokens in passes of two chunks: the raw x of the pass after
+    // the last is loaded too (zeros from clamped addresses, never converted).
+    if (MP == 16 && GP == 8) {
+      const int64_t gb = g0 + npass * GP, npg = std::min<int64_t>(GP, ng - npass * GP);
+      for (int item = 0; item < threads; ++item) {
+        const int q = item & 3, rest = item >> 2;
+        const int64_t gl = rest % GP, m = rest / GP;
+        const bool in = item < MP * GP * 4 && m < M && gl < npg;
+        const int64_t src = in ? m * K + 128 * (gb + gl) + 8 * q : 0;
+        for (int u = 0; u < 4; ++u) X.read(2 * (src + 32 * u), 16, "x (staging past the range)");
+      }
+    }
     for (int64_t ps = 0; ps < npass; ++ps) {
       if (ps > 0) stage(ps);
       const int64_t base = (ps & 1) * buf_bytes;
