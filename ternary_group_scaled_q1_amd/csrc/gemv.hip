@@ -346,6 +346,16 @@ __device__ __forceinline__ bool advance(Cursor &c, int U, int n_stages) {
   return false;
 }
 
+// Waves per SIMD the kernel is built for (the second launch bound).  Four
+// (two workgroups per CU) leave 128 registers per lane, which the fp8 x fp4
+// path with four row tiles per wave and several tokens exceeds: it spilled
+// 36-40 bytes per lane to scratch.  That variant is built for two waves per
+// SIMD (one workgroup per CU), and the plan reads the residency it gets.
+template <int MT, int R, bool FP4>
+constexpr int gemv_min_waves() {
+  return (FP4 && MT > 1 && R >= 4) ? 2 : 4;
+}
+
 // Each wave walks a flat sequence of units (tile set, chunk) with a ring of
 // D units in flight: the loads of unit i + D - 1 are issued before unit i is
 // computed, across chunk, stage and tile-set boundaries.
@@ -354,7 +364,7 @@ __device__ __forceinline__ bool advance(Cursor &c, int U, int n_stages) {
 // tile addresses resolved once per tile set and step a fixed stride per
 // chunk (the general path resolves the tile and its ragged shape per unit).
 template <int FMT, bool BF, int MT, int R, int D, bool FP4, bool FULL>
-__global__ void __launch_bounds__(kThreads, 4) gemv_kernel(GemvParams p) {
+__global__ void __launch_bounds__(kThreads, (gemv_min_waves<MT, R, FP4>())) gemv_kernel(GemvParams p) {
   // Accumulator elements that can hold a token (fp4: A rows, two per token).
   constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
   constexpr int MTS = MT;                // token slots per x cell
