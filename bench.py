@@ -332,6 +332,7 @@ def load_probes():
     lib.probe_stream_read.restype, lib.probe_stream_read.argtypes = i32, [vp, i64, vp, i32, vp]
     lib.probe_mfma_bf16.restype, lib.probe_mfma_bf16.argtypes = i32, [vp, i32, i32, vp]
     lib.probe_empty.restype, lib.probe_empty.argtypes = i32, [vp]
+    lib.probe_tile_read.restype, lib.probe_tile_read.argtypes = i32, [vp, i64, i32, i32, i32, vp, vp]
     return lib
 
 
@@ -374,7 +375,13 @@ def platform_probes(torch, dev):
         every step, 16 waves per CU;
       * empty_launch_us: an empty kernel, per launch in a graph of 256;
       * dense_bf16_matmul_TFLOPs: torch's matmul (the platform BLAS) at the
-        q1 prefill shape 512 x 17408 x 5120."""
+        q1 prefill shape 512 x 17408 x 5120;
+      * tile_read: the q1 gate/up weight bytes (2176 tiles of 16 rows x 5120)
+        read in the decode kernels' order, each wave its own tile, 1 KB per
+        step, with 2 or 4 steps in flight, from its first chunk, from a
+        rotated chunk, or in a chunk-major layout; next to the streaming
+        read of the same bytes.  Each launch reads another copy of a 1 GiB
+        rotation pool; us per launch in a graph of 64."""
     pr = load_probes()
 
     def cs():  # the stream launches go to (graph capture switches it)
@@ -419,6 +426,27 @@ def platform_probes(torch, dev):
     out["dense_bf16_matmul_TFLOPs"] = round(2 * M * N * K * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
     out["dense_bf16_matmul_shape"] = f"{M}x{N}x{K}"
     del a, b, c
+    T, tb = 2176, 10240
+    nb = T * tb
+    copies = POOL_BYTES // nb
+    pool = torch.empty(copies * nb, device=dev, dtype=torch.uint8)
+    base = pool.data_ptr()
+    tr = {}
+
+    def tile_reads(depth, mode):
+        for i in range(64):
+            if pr.probe_tile_read(base + (i % copies) * nb, tb, T, depth, mode, sink.data_ptr(), cs()) != 0:
+                raise RuntimeError("probe_tile_read refused its arguments")
+
+    for depth, mode, name in ((2, 0, "own_tile_2_in_flight_us"), (4, 0, "own_tile_4_in_flight_us"),
+                              (2, 1, "rotated_start_2_in_flight_us"), (2, 2, "chunk_major_2_in_flight_us")):
+        tr[name] = round(_graph_time_ms(torch, lambda: tile_reads(depth, mode)) * 1e3 / 64, 2)
+    tr["stream_read_us"] = round(_graph_time_ms(torch, lambda: [
+        pr.probe_stream_read(base + (i % copies) * nb, nb, sink.data_ptr(), read_grid(nb), cs())
+        for i in range(64)]) * 1e3 / 64, 2)
+    tr["bytes"] = nb
+    out["tile_read"] = tr
+    del pool
     return out
 
 
@@ -521,12 +549,13 @@ def part_arithmetic(lb, sweeps, gemm_ids, launches, layers, ws_bytes, gws_bytes)
 def _source_digest():
     """sha256 over the code of the kernel sources and the launch planner, with
     line comments and blank lines left out (any change to the code
-    invalidates counters taken earlier; a change to a comment does not)."""
+    invalidates counters taken earlier; a change to a comment does not).
+    The measurement probes (probes.hip) are not part of what is measured."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_group_scaled_q1_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
+        if name.endswith((".hip", ".hpp", ".cpp")) and name != "probes.hip":
             with open(os.path.join(csrc, name), encoding="utf-8") as f:
                 code = [ln.split("//", 1)[0].rstrip() for ln in f]
             h.update(name.encode() + b"\0" + "\n".join(ln for ln in code if ln).encode())

@@ -8,6 +8,11 @@
 //    v_mfma_f32_16x16x32_bf16; the B operand is a +-1 pattern that changes
 //    every step (as decoded low-bit weights do), the A operand random bf16.
 //  * probe_empty: a kernel that does nothing, for the launch cost.
+//  * probe_tile_read: the decode kernels' weight stream without the
+//    arithmetic: wave t reads tile t (tile_bytes, a multiple of 1 KB) 1 KB
+//    per step with D steps in flight; mode 1 starts wave t at chunk t mod
+//    (chunks per tile); mode 2 reads a chunk-major layout in which chunk c
+//    of tile t sits at (c T + t) KB, so one step of all waves is contiguous.
 // Built into libprobes.so, a library of its own next to liblowbit.so.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -64,6 +69,36 @@ __global__ void __launch_bounds__(512) mfma_kernel(float *out, int iters) {
 
 __global__ void empty_kernel() {}
 
+template <int D>
+__global__ void __launch_bounds__(512) tile_read_kernel(const char *base, int64_t tile_bytes, int T, int mode,
+                                                        uint32_t *sink) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 8 + wave;
+  if (t >= T) return;
+  const int nch = int(tile_bytes >> 10);
+  const int rot = mode == 1 ? t % nch : 0;
+  auto at = [&](int c) {
+    int cc = c + rot;
+    if (cc >= nch) cc -= nch;
+    const int64_t off = mode == 2 ? (int64_t(cc) * T + t) * 1024 : int64_t(t) * tile_bytes + int64_t(cc) * 1024;
+    return reinterpret_cast<const u4v *>(base + off) + lane;
+  };
+  uint32_t acc = 0;
+  u4v r[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) r[d] = __builtin_nontemporal_load(at(min(d, nch - 1)));
+  for (int c0 = 0; c0 < nch; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      acc ^= r[d].x ^ r[d].y ^ r[d].z ^ r[d].w;
+      r[d] = __builtin_nontemporal_load(at(min(c0 + d + D, nch - 1)));
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc ^= r[d].x;
+  if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,6 +116,21 @@ int probe_stream_read(const void *buf, int64_t bytes, void *sink, int grid, void
 int probe_mfma_bf16(void *out, int iters, int grid, void *stream) {
   hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(512), 0, static_cast<hipStream_t>(stream),
                      static_cast<float *>(out), iters);
+  return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+// Reads tiles * tile_bytes of device memory at buf (tile_bytes a positive
+// multiple of 1024; depth 2 or 4; mode 0, 1 or 2 as above) with 8 waves per
+// workgroup; sink: 2 KiB of device memory.  -2 for arguments out of range.
+int probe_tile_read(const void *buf, int64_t tile_bytes, int tiles, int depth, int mode, void *sink, void *stream) {
+  if (tile_bytes < 1024 || tile_bytes % 1024 || tiles < 1 || (depth != 2 && depth != 4) || mode < 0 || mode > 2)
+    return -2;
+  const dim3 grid((tiles + 7) / 8), block(512);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const char *b = static_cast<const char *>(buf);
+  uint32_t *sk = static_cast<uint32_t *>(sink);
+  if (depth == 2) hipLaunchKernelGGL(tile_read_kernel<2>, grid, block, 0, st, b, tile_bytes, tiles, mode, sk);
+  else hipLaunchKernelGGL(tile_read_kernel<4>, grid, block, 0, st, b, tile_bytes, tiles, mode, sk);
   return hipGetLastError() == hipSuccess ? 0 : -8;
 }
 
