@@ -403,6 +403,8 @@ void staged_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
   const int64_t U = SC / S, KT = n_stages * U;
   const bool restage = n_stages > 1, lockstep = restage || S > 1;
   const int64_t rows_total = grid * Pw;
+  // Every chunk of every tile set is multiplied exactly once.
+  std::vector<int> cover(size_t(tilesets * chunks), 0);
   for (int64_t b = 0; b < grid; ++b) {
     Buf lds("LDS", P["lds_bytes"], true);
     if (!fp4 && MT < 16)
@@ -490,6 +492,7 @@ void staged_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
         const int64_t ch = st * SC + s + kl * S;
         const bool v = it * rows_total + my_row[w] < tilesets && ch < chunks;
         if (v) {
+          ++cover[size_t((it * rows_total + my_row[w]) * chunks + ch)];
           const int64_t c_local = s + kl * S;
           for (int lane = 0; lane < 64; ++lane) {
             const int j = lane & 15, q = lane >> 4;
@@ -543,6 +546,10 @@ void staged_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
       }
     }
   }
+  for (int64_t ts = 0; ts < tilesets; ++ts)
+    for (int64_t c = 0; c < chunks; ++c)
+      if (cover[size_t(ts * chunks + c)] != 1)
+        fail("staged", fmtv("tile set %lld chunk %lld multiplied %lld times", ts, c, cover[size_t(ts * chunks + c)]));
 }
 
 // ---------------------------------------------------------- wide kernel ----
