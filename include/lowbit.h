@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 5
+#define LOWBIT_ABI_VERSION 6
 
 typedef enum { LOWBIT_Q1_G128 = 1, LOWBIT_TQ2_G128 = 2, LOWBIT_TQ5_G128 = 3 } lowbit_format;
 typedef enum { LOWBIT_F16 = 1, LOWBIT_BF16 = 2, LOWBIT_F32 = 3 } lowbit_dtype;
@@ -254,7 +254,9 @@ typedef enum {
   LOWBIT_KERNEL_GEMV_TQ5 = 4,     /* decode, base-3 weights                                */
   LOWBIT_KERNEL_GEMV_TQ5_ONE = 5, /* decode, base-3 weights, one token, x in LDS           */
   LOWBIT_KERNEL_GEMM = 6,         /* prefill                                               */
-  LOWBIT_KERNEL_FILL_ZERO = 7     /* K == 0: Y = 0                                         */
+  LOWBIT_KERNEL_FILL_ZERO = 7,    /* K == 0: Y = 0                                         */
+  LOWBIT_KERNEL_GEMV_KSLICE = 8   /* decode, 9..16 tokens, each wave one chunk of K of all  *
+                                   * the workgroup's row tiles, x in registers              */
 } lowbit_kernel;
 
 typedef enum {

@@ -19,7 +19,7 @@ PROBES_LIB = os.path.join(PKG, "libprobes.so")
 PROBES_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "noalloc.hip", "gemv.hip", "gemv_wide.hip", "gemv_split.hip", "gemv_tq5.hip", "gemm.hip", "device_props.cpp", "pack.cpp"]
+SOURCES = ["api.hip", "noalloc.hip", "gemv.hip", "gemv_wide.hip", "gemv_split.hip", "gemv_kslice.hip", "gemv_tq5.hip", "gemm.hip", "device_props.cpp", "pack.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

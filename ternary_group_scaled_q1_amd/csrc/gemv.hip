@@ -635,12 +635,14 @@ hipError_t launch_mt(const LaunchArgs &a) {
 //  * 2..8 tokens: the staged kernel, or the 2-D split (row blocks x K
 //    ranges, x converted once per block, gemv_split.hip) on long rows, on
 //    4+ tokens below 65536 rows, and on 5+ tokens of very tall matrices;
-//  * 9..16 tokens: the 2-D split; without a workspace on a small matrix, x
-//    loaded straight into registers (gemv_wide.hip).
+//  * 9..16 tokens: waves that split K over three or more row tiles per
+//    workgroup (gemv_kslice.hip) when K is 4..10 whole chunks and the matrix
+//    has the tiles for it; else the 2-D split; without a workspace on a
+//    small matrix, x loaded straight into registers (gemv_wide.hip).
 // Exact f16 / bf16 operands (ternary weights, fp16 x): the staged kernel for
 // up to 4 tokens unless the rows are long or the matrix tall, the 2-D split
-// for 5..8 tokens on 8192+ rows or long rows and for 9..16 tokens, else the
-// register kernel.
+// for 5..8 tokens on 8192+ rows or long rows and for 9..16 tokens (the
+// K-sliced kernel first, as above), else the register kernel.
 //
 // The fp8 x fp4 kernels (the staged one with FP4, and the split) hold each
 // 32-value activation block at one shared exponent: values within 2^7 of
@@ -655,7 +657,11 @@ hipError_t launch_fmt(const LaunchArgs &a) {
   const bool split_ok = ws_ok || a.N >= 65536;
   if constexpr (BF && FMT == 1) {
     constexpr int RB = 4;
-    if (a.M > 8) return split_ok ? launch_gemv_split(a) : launch_gemv_wide(a);
+    if (a.M > 8) {
+      hipError_t e;
+      if (launch_gemv_kslice(a, e)) return e;
+      return split_ok ? launch_gemv_split(a) : launch_gemv_wide(a);
+    }
     const bool split = a.M >= 2 && ((ws_ok && (a.K >= 8192 || (a.M >= 4 && a.N < 65536))) ||
                                     (a.M > 4 && a.N >= 65536));
     if (split) return launch_gemv_split(a);
@@ -664,7 +670,11 @@ hipError_t launch_fmt(const LaunchArgs &a) {
     if (a.M <= 4) return launch_mt<FMT, BF, 4, true, 2, RB>(a);
     return launch_mt<FMT, BF, 8, true, 2, RB>(a);
   } else {
-    if (a.M > 8) return split_ok ? launch_gemv_split(a) : launch_gemv_wide(a);
+    if (a.M > 8) {
+      hipError_t e;
+      if (launch_gemv_kslice(a, e)) return e;
+      return split_ok ? launch_gemv_split(a) : launch_gemv_wide(a);
+    }
     if (a.M >= 2) {
       const bool split = a.K >= 8192 || (a.M > 4 ? a.N >= 8192 : (a.N >= 24576 && a.N < 65536));
       if (split && split_ok) return launch_gemv_split(a);

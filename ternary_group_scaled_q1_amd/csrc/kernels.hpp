@@ -64,6 +64,10 @@ hipError_t launch_gemv_wide(const LaunchArgs &a);
 int64_t gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 // GEMV on fp8 x fp4 instructions with row blocks x K ranges (bf16 x, M <= 16).
 hipError_t launch_gemv_split(const LaunchArgs &a);
+// GEMV for 9..16 tokens with waves that split K (no workspace): launches (or
+// records the plan of) the product and returns true when the launch suits
+// it, with err its hipError_t; returns false otherwise.
+bool launch_gemv_kslice(const LaunchArgs &a, hipError_t &err);
 int64_t gemv_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // GEMV for base-3 (tq5) weights, up to 16 tokens.
 hipError_t launch_gemv_tq5(const LaunchArgs &a);

@@ -383,6 +383,58 @@ void split_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X, Buf &ws) 
     if (ws.u32(4 * rb) != 0) fail("arrival counter", fmtv("row block %lld left at %lld", rb, ws.u32(4 * rb)));
 }
 
+// ------------------------------------------------------- k-slice kernel ----
+// Wave w of a workgroup owns chunk w of K for the workgroup's T row tiles.
+void kslice_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
+  const int fmt = ms.fmt;
+  const int T = int(P["tiles_per_wave"]), NW = int(P["waves"]), D = int(P["ring"]);
+  const bool fp4 = P["operands"] == 3;
+  const int64_t M = ms.M, K = ms.K;
+  if (P["whole_tiles"] != 1 || P["k_ranges"] != 1 || P["token_slots"] != 16)
+    fail("kslice plan", "whole tiles, one K range and 16 token slots expected");
+  if (K % 512 || NW != K / 512) fail("kslice plan", fmtv("%lld waves for K = %lld", NW, K));
+  if (P["threads"] != 64 * NW) fail("kslice plan", fmtv("threads %lld", P["threads"]));
+  if (P["grid"] != cdiv(ms.tiles, T)) fail("kslice plan", fmtv("grid %lld for %lld tiles of %lld", P["grid"], ms.tiles, T));
+  if (P["lds_bytes"] != int64_t(T) * NW * 1024) fail("kslice plan", fmtv("lds %lld", P["lds_bytes"]));
+  if (M < 1 || M > 16) fail("kslice plan", fmtv("M = %lld", M));
+  for (int64_t b = 0; b < P["grid"]; ++b) {
+    Buf lds("LDS", P["lds_bytes"], true);
+    const int64_t t0 = b * T;
+    for (int w = 0; w < NW; ++w) {
+      // A operands: lane (qa, r) reads x of token r (row 0 past M).
+      for (int lane = 0; lane < 64; ++lane) {
+        const int qa = lane >> 4, r = lane & 15;
+        const int64_t row = r < M ? r : 0;
+        for (int g = 0; g < 4; ++g)
+          for (int u = 0; u < 4; ++u) {
+            const int64_t k = 512 * w + 128 * g + (fp4 ? 8 * qa + 32 * u : 32 * u + 8 * qa);
+            X.read(2 * (row * K + k), 16, "x (A operand)");
+          }
+        if (fp4)  // the halves come from lanes of the same token
+          for (int src : {16 * (qa >> 1) + r, 16 * (2 + (qa >> 1)) + r})
+            if (src < 0 || src > 63) fail("kslice", "ds_bpermute source lane");
+      }
+      // Weights: a ring of D units, one per tile step, clamped to the last tile.
+      for (int d = 0; d < D; ++d) load_full(ms, fmt, 1, std::min<int64_t>(t0 + std::min<int64_t>(d, T - 1), ms.tiles - 1), w);
+      for (int t = 0; t + D < T; ++t) load_full(ms, fmt, 1, std::min<int64_t>(t0 + t + D, ms.tiles - 1), w);
+      // This wave's sums into LDS.
+      for (int t = 0; t < T; ++t)
+        for (int lane = 0; lane < 64; ++lane) lds.write(16 * ((int64_t(t) * NW + w) * 64 + lane), 16, "wave sums", 7);
+    }
+    // After the barrier: each output (tile, lane, e) adds the NW waves' sums.
+    for (int64_t o = 0; o < int64_t(T) * 256; ++o) {
+      const int64_t t = o >> 8, ln = (o >> 2) & 63, e = o & 3;
+      const int64_t m = 4 * (ln >> 4) + e;
+      if (t0 + t >= ms.tiles || m >= M) continue;
+      for (int w = 0; w < NW; ++w) lds.read_tagged(4 * (((t * NW + w) * 64 + ln) * 4 + e), 4, 7, "wave sum read");
+      int mi;
+      int64_t tt;
+      ms.tile_ref(t0 + t, mi, tt);
+      ms.store_y(mi, tt, ln & 15, m);
+    }
+  }
+}
+
 // -------------------------------------------------------- staged kernel ----
 void staged_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
   const int fmt = ms.fmt;
@@ -1059,6 +1111,7 @@ int main(int argc, char **argv) {
   if (kernel == "gemv_split") split_kernel(ms, P, X, ws);
   else if (kernel == "gemv_staged") staged_kernel(ms, P, X);
   else if (kernel == "gemv_wide") wide_kernel(ms, P, X);
+  else if (kernel == "gemv_kslice") kslice_kernel(ms, P, X);
   else if (kernel == "gemv_tq5") tq5_kernel(ms, P, X);
   else if (kernel == "gemv_tq5_one") tq5_one_kernel(ms, P, X);
   else if (kernel == "gemm") gemm_kernel(ms, P, X, ws);

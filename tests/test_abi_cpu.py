@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(lb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert lb.abi_version() == 5
+    assert lb.abi_version() == 6
 
 
 PAGES = ("lnrk.cn page", "ksqn.cn page", "cnblogs.com page", "aberweb.com page")
@@ -60,11 +60,18 @@ def test_plan_query_reaches_the_timed_plans():
     """The plan query runs the launchers' own planning code without a GPU
     (256 compute units assumed): the 16-token LM head of the decode sweep
     takes the split kernel with two row tiles per wave and all of K, the
-    16-token q/k/v launch cuts K, and one token takes the staged kernel."""
+    16-token o launch cuts K, the 16-token q/k/v and gate/up launches take
+    the K-sliced kernel (10 waves; 4 and 9 row tiles per workgroup), and one
+    token takes the staged kernel."""
     K = 5120
-    ws = lb.gemv_multi_workspace_bytes("q1", [5120] * 3, 16, K)
-    p = lb.gemv_plan("q1", [5120] * 3, 16, K, workspace_bytes=ws)
+    ws = lb.gemv_multi_workspace_bytes("q1", [5120], 16, K)
+    p = lb.gemv_plan("q1", [5120], 16, K, workspace_bytes=ws)
     assert p["kernel_name"] == "gemv_split" and p["k_ranges"] > 1 and p["operands_name"] == "fp8_fp4"
+    for fmt, ops in (("q1", "fp8_fp4"), ("tq2", "bf16")):
+        for Ns, T in (([5120] * 3, 4), ([17408] * 2, 9)):
+            p = lb.gemv_plan(fmt, Ns, 16, K, workspace_bytes=ws)
+            assert (p["kernel_name"], p["tiles_per_wave"], p["waves"], p["operands_name"]) == \
+                ("gemv_kslice", T, 10, ops), p
     for fmt, ops in (("q1", "fp8_fp4"), ("tq2", "bf16")):
         p = lb.gemv_plan(fmt, 151936, 16, K, workspace_bytes=lb.gemv_workspace_bytes(fmt, 16, 151936, K))
         assert (p["kernel_name"], p["tiles_per_wave"], p["k_ranges"], p["waves"], p["operands_name"]) == \

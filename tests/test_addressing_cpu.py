@@ -8,7 +8,8 @@ sanitizers (no GPU).
   x, packed weights, scales, workspace, outputs and LDS.  Every launch the
   benchmark times and every plan family (staged, 2-D split with one, two or
   four row tiles per wave and 8 or 12 waves, K cut in ranges, x in registers,
-  base-3 kernels, stream-K GEMM with and without fp8 x pieces) is covered,
+  K-sliced waves, base-3 kernels, stream-K GEMM with and without fp8 x
+  pieces) is covered,
   plus ragged shapes.  Planted plan mistakes must make it fail.
 * The packer's C++ (csrc/pack.cpp) is built with AddressSanitizer + UBSan and
   with ThreadSanitizer and driven on exact-size buffers.
@@ -70,6 +71,23 @@ def test_workload_decode_launches_in_bounds(exe, fmt, Ns, K, Ms, xdt):
         _ok(ad.run_gemv(exe, fmt, Ns, M, K, xdt=xdt))
 
 
+@pytest.mark.parametrize("fmt", ["q1", "tq2"])
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+def test_kslice_plans_in_bounds(exe, fmt, xdt):
+    """The K-sliced 16-token kernel (each wave one chunk of K of all the
+    workgroup's row tiles): every plan size it is built for (4, 6, 9 and 12
+    tiles per workgroup), K of 8 and 10 chunks, single and fused launches,
+    9..16 tokens."""
+    seen = set()
+    for Ns, K in (([5120] * 3, 5120), ([17408] * 2, 5120), ([12288], 4096), ([24576], 4096), ([40960], 5120),
+                  ([4096] * 3, 4096)):
+        for M in (9, 13, 16):
+            plan = _ok(ad.run_gemv(exe, fmt, Ns, M, K, xdt=xdt))
+            assert plan["kernel_name"] == "gemv_kslice", plan
+            seen.add(plan["tiles_per_wave"])
+    assert seen == {4, 6, 9, 12}, seen
+
+
 # Ragged and small shapes of the GPU tests: partial row tiles, partial
 # chunks, tq5 row tails, fused launches with a zero-row matrix, 2..17 tokens.
 SMALL = [(1, 128, 1), (17, 640, 3), (16, 512, 1), (33, 1152, 4), (256, 1024, 1), (300, 2048, 5), (64, 17408, 8),
@@ -117,23 +135,30 @@ def test_gemm_launches_in_bounds(exe, fmt, M, N, K):
 def test_replica_catches_planted_mistakes(exe):
     """Plans bent on purpose (on the CPU only) must fail the replica: a
     workspace one partial sum short, a staging pass larger than its LDS
-    buffer, a K range too short to cover K, and a GEMM workspace without
-    room for its pieces."""
+    buffer, a K range too short to cover K, a K-sliced plan with a tile, a
+    wave or 1 KB of LDS too few, and a GEMM workspace without room for its
+    pieces."""
     K = 5120
-    ws = lb.gemv_multi_workspace_bytes("q1", [5120] * 3, 16, K)
-    plan = lb.gemv_plan("q1", [5120] * 3, 16, K, workspace_bytes=ws)
-    assert plan["k_ranges"] > 1
-    used = 32768 + plan["k_ranges"] * 16 * 3 * 5120 * 4  # counters + the plan's partial sums
-    (rc, out), _ = ad.run_gemv(exe, "q1", [5120] * 3, 16, K, ws_bytes=used, plan=plan)
+    ws = lb.gemv_multi_workspace_bytes("q1", [5120], 16, K)
+    plan = lb.gemv_plan("q1", [5120], 16, K, workspace_bytes=ws)
+    assert plan["kernel_name"] == "gemv_split" and plan["k_ranges"] > 1
+    used = 32768 + plan["k_ranges"] * 16 * 5120 * 4  # counters + the plan's partial sums
+    (rc, out), _ = ad.run_gemv(exe, "q1", [5120], 16, K, ws_bytes=used, plan=plan)
     assert rc == 0, out
-    (rc, out), _ = ad.run_gemv(exe, "q1", [5120] * 3, 16, K, ws_bytes=used - 4, plan=plan)
+    (rc, out), _ = ad.run_gemv(exe, "q1", [5120], 16, K, ws_bytes=used - 4, plan=plan)
     assert rc != 0 and "partial sum" in out, out
     bad = dict(plan, groups_per_pass=plan["groups_per_pass"] + 4)
-    (rc, out), _ = ad.run_gemv(exe, "q1", [5120] * 3, 16, K, ws_bytes=ws, plan=bad)
+    (rc, out), _ = ad.run_gemv(exe, "q1", [5120], 16, K, ws_bytes=ws, plan=bad)
     assert rc != 0, out
     short = dict(plan, groups_per_range=plan["groups_per_range"] - 4)
-    (rc, out), _ = ad.run_gemv(exe, "q1", [5120] * 3, 16, K, ws_bytes=ws, plan=short)
+    (rc, out), _ = ad.run_gemv(exe, "q1", [5120], 16, K, ws_bytes=ws, plan=short)
     assert rc != 0, out
+    ksl = lb.gemv_plan("q1", [5120] * 3, 16, K, workspace_bytes=0)
+    assert ksl["kernel_name"] == "gemv_kslice", ksl
+    for bent in (dict(ksl, tiles_per_wave=ksl["tiles_per_wave"] - 1), dict(ksl, waves=ksl["waves"] - 1),
+                 dict(ksl, lds_bytes=ksl["lds_bytes"] - 1024)):
+        (rc, out), _ = ad.run_gemv(exe, "q1", [5120] * 3, 16, K, ws_bytes=0, plan=bent)
+        assert rc != 0, out
     one = lb.gemv_plan("tq2", 151936, 16, K, workspace_bytes=0)
     (rc, out), _ = ad.run_gemv(exe, "tq2", 151936, 16, K, ws_bytes=0, plan=dict(one, tiles_per_wave=1))
     assert rc != 0, out

@@ -545,3 +545,41 @@ def test_split_most_k_ranges_reused_workspace(fmt, M):
         assert np.array_equal(ys[0], ys[2])
         if need:
             assert int(ws[:4 * ((N + 15) // 16)].view(t.int32).abs().sum()) == 0  # counters reset
+
+
+@pytest.mark.parametrize("fmt", ["q1", "tq2"])
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+def test_kslice_every_output(fmt, xdt):
+    """The K-sliced kernel (9..16 tokens; each wave one chunk of K of all
+    the workgroup's row tiles, x in registers): every plan size it is built
+    for (4, 6, 9, 12 tiles per workgroup), K of 8 and 10 chunks, single and
+    fused launches, 9, 13 and 16 tokens; every output element against the
+    oracle, fp32 and fp16 y, and a repeat bitwise equal (no workspace)."""
+    t = gu.torch()
+    g = np.random.default_rng(1200)
+    cases = [(13, [12288], 4096), (16, [24576], 4096), (9, [17408, 17408], 5120), (16, [40960], 5120),
+             (16, [4096, 4096, 4096], 4096)]
+    seen = set()
+    for M, Ns, K in cases:
+        plan = lb.gemv_plan(fmt, Ns, M, K, x_dtype=xdt, workspace_bytes=0)
+        assert plan["kernel_name"] == "gemv_kslice", plan
+        seen.add(plan["tiles_per_wave"])
+        print(f"kslice {fmt} {xdt} M={M} Ns={Ns} K={K} T={plan['tiles_per_wave']}", flush=True)
+        mats = []
+        for N in Ns:
+            codes = _codes(g, fmt, N, K)
+            sc = synth.scales_absnormal(g, N, K // 128)
+            mats.append((codes, sc, gu.w_tensor(lb.pack(fmt, codes, sc))))
+        x = synth.x_normal(g, M, K, xdt)
+        xt = gu.x_tensor(x, xdt)
+        refs = [gu.product_blocked(codes, sc, x, xdt) for codes, sc, _ in mats]
+        for ydt in ("f32", "f16"):
+            odt = t.float32 if ydt == "f32" else t.float16
+            ys = lb.gemv_multi(fmt, [m[2] for m in mats], xt, Ns, K, out_dtype=odt)
+            ys2 = lb.gemv_multi(fmt, [m[2] for m in mats], xt, Ns, K, out_dtype=odt)
+            t.cuda.synchronize()
+            for i, ((codes, sc, _), y, y2, ref) in enumerate(zip(mats, ys, ys2, refs)):
+                assert t.equal(y, y2), (fmt, M, Ns, i)
+                gu.check(y.cpu().numpy().astype(np.float64), codes, sc, x, xdt,
+                         f"kslice {fmt} {xdt} {ydt} M={M} matrix {i}", y_f16=ydt == "f16", ref_ya=ref)
+    assert seen == {4, 6, 9, 12}, seen
