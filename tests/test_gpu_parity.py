@@ -583,3 +583,29 @@ def test_kslice_every_output(fmt, xdt):
                 gu.check(y.cpu().numpy().astype(np.float64), codes, sc, x, xdt,
                          f"kslice {fmt} {xdt} {ydt} M={M} matrix {i}", y_f16=ydt == "f16", ref_ya=ref)
     assert seen == {4, 6, 9, 12}, seen
+
+
+@pytest.mark.parametrize("fmt", ["q1", "tq2"])
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+def test_split_two_tiles_per_wave_every_output(fmt, xdt):
+    """4096 row tiles (N = 65536, and 65529 with a ragged last tile): the
+    2-D split's one-tile row blocks exceed the CUs, so it takes two row
+    tiles per wave and all of K, the plan of the 16-token LM head; 8 and 16
+    tokens, bf16 and fp16 x (fp8 pieces and exact operands), every output
+    element against the oracle."""
+    t = gu.torch()
+    g = np.random.default_rng(1300)
+    K = 2048
+    for N in (65536, 65529):
+        codes = _codes(g, fmt, N, K)
+        sc = synth.scales_absnormal(g, N, K // 128)
+        w = gu.w_tensor(lb.pack(fmt, codes, sc))
+        for M in (8, 16):
+            plan = lb.gemv_plan(fmt, N, M, K, x_dtype=xdt, workspace_bytes=lb.gemv_workspace_bytes(fmt, M, N, K))
+            assert (plan["kernel_name"], plan["tiles_per_wave"], plan["k_ranges"]) == ("gemv_split", 2, 1), plan
+            print(f"split R=2 {fmt} {xdt} N={N} M={M}", flush=True)
+            x = synth.x_normal(g, M, K, xdt)
+            ws = t.zeros(max(lb.gemv_workspace_bytes(fmt, M, N, K), 16), dtype=t.uint8, device="cuda")
+            y = lb.gemv(fmt, w, gu.x_tensor(x, xdt), N, K, workspace=ws)
+            t.cuda.synchronize()
+            gu.check(y.cpu().numpy().astype(np.float64), codes, sc, x, xdt, f"split R=2 {fmt} {xdt} N={N} M={M}")
