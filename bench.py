@@ -548,10 +548,12 @@ def part_arithmetic(lb, sweeps, gemm_ids, launches, layers, ws_bytes, gws_bytes)
 
 def _source_digest():
     """sha256 over the code of the kernel sources and the launch planner, with
-    line comments and blank lines left out (any change to the code
-    invalidates counters taken earlier; a change to a comment does not).
-    The measurement probes (probes.hip) are not part of what is measured."""
+    line comments and blank lines left out, and over the compiler flags
+    they are built with (any change to the code or its flags invalidates
+    counters taken earlier; a change to a comment does not).  The
+    measurement probes (probes.hip) are not part of what is measured."""
     import hashlib
+    from ternary_group_scaled_q1_amd import build as bld
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_group_scaled_q1_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
@@ -559,6 +561,7 @@ def _source_digest():
             with open(os.path.join(csrc, name), encoding="utf-8") as f:
                 code = [ln.split("//", 1)[0].rstrip() for ln in f]
             h.update(name.encode() + b"\0" + "\n".join(ln for ln in code if ln).encode())
+            h.update(" ".join(bld.HIPCC_FLAGS + bld.EXTRA_FLAGS.get(name, [])).encode())
     return h.hexdigest()
 
 

@@ -25,6 +25,12 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # No packed-FP32 instructions in device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Every wave runs its prologue (the first loads of x and of the weight
+    # ring) at raised issue priority and drops to normal priority (s_setprio)
+    # where its main loop begins, so the first loads of all waves on a SIMD
+    # leave before any wave's compute: 1-2% on the decode sweeps, neutral on
+    # the GEMMs.
+    "-mllvm", "-amdgpu-set-wave-priority",
 ]
 
 
@@ -36,8 +42,13 @@ def _hipcc() -> str:
 
 
 # Per-source extra flags: the GEMM keeps its MFMA accumulators in VGPRs (the
-# per-group fp32 scale epilogue then needs no moves out of AGPRs).
-EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-group fp32 scale epilogue then needs no moves out of AGPRs); the
+# K-sliced GEMV is scheduled for instruction-level parallelism rather than
+# occupancy (its 16-token launches 4-8% faster; the same strategy made the
+# one-token staged kernel 3-6% slower and left the split kernel and the
+# GEMMs unchanged, so it stays on this file only).
+EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "gemv_kslice.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:

@@ -38,6 +38,9 @@ def test_source_digest_ignores_comments_only(tmp_path, monkeypatch):
     _fake_tree(tmp_path, code)
     (tmp_path / "ternary_group_scaled_q1_amd" / "csrc" / "notes.txt").write_text("changed")
     assert bench._source_digest() == d0  # only .hip / .hpp / .cpp count
+    from ternary_group_scaled_q1_amd import build as bld
+    monkeypatch.setitem(bld.EXTRA_FLAGS, "k.hip", ["-mllvm", "-some-scheduler-flag"])
+    assert bench._source_digest() != d0  # the flags a source is built with count too
 
 
 def _summary(tmp_path, digest, sweep="tq2_M16", fetch="1000", write="200"):
