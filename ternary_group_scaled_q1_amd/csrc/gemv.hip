@@ -513,7 +513,11 @@ __global__ void __launch_bounds__(kThreads, (gemv_min_waves<MT, R, FP4>())) gemv
 // units plus its waves' units (one more per tile set when waves split K),
 // and a CU that holds n workgroups runs each about 1 + 0.45 (n - 1) times
 // slower.  So every (S, grid cap of 1, 2, ... workgroups per CU) is costed
-// as (units per wave + 2) x that factor, and the cheapest wins.
+// as (units per wave + 2) x that factor, and the cheapest wins.  The fp8
+// split of x grows with K, so on that path the fixed part counts two units
+// per 5120 of K: on the 5120 x 17408 down projection two row tiles per wave
+// on 160 workgroups then win over one tile on 320 (8.35 against 8.8 us;
+// with exact operands the one-tile plan stays ahead, 11.3 against 11.7).
 template <int FMT, bool BF, int MT, int R, int D, bool FP4, bool FULL>
 double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) {
   constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
@@ -562,7 +566,8 @@ double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) 
       // (two barriers): about one unit each.
       const double units = double(its) * R * ((p.chunks + S - 1) / S) + (S > 1 ? double(its) : 0.0);
       const int share = (g + cus - 1) / cus;
-      const double cost = (units + 2.0) * (1.0 + 0.45 * (share - 1));
+      const double fixed = FP4 && p.K > 5120 ? 2.0 * p.K / 5120.0 : 2.0;
+      const double cost = (units + fixed) * (1.0 + 0.45 * (share - 1));
       if (cost < best) {
         best = cost;
         bp = q;
