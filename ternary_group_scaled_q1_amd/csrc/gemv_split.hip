@@ -83,10 +83,33 @@ struct RawQ {
   bool in;    // the item holds x (a token below M, a group of the pass)
 };
 
-template <int MP>
+// Token slot m, lane quarter q and pass group gl of an item.  Exact modes
+// number the items token slot fastest, so the 16-byte LDS writes of
+// neighbouring lanes go to neighbouring cells; numbered lane quarter
+// fastest, all lanes of one token hit the same banks (the group stride is a
+// multiple of the bank width), 6 conflicts per LDS instruction on the
+// ternary launches.  The fp8-piece path keeps lane quarter fastest: token
+// slot fastest was 3-5% slower there (its rows are 144 bytes apart, so it
+// conflicts little either way).
+template <int MP, int MODE>
+__device__ __forceinline__ void item_coords(int item, int GP, int &m, int &q, int &gl) {
+  if constexpr (MODE == kFp4) {
+    q = item & 3;
+    const int rest = item >> 2;
+    gl = rest % GP;
+    m = rest / GP;
+  } else {
+    m = item % MP;
+    const int rest = item / MP;
+    q = rest & 3;
+    gl = rest >> 2;
+  }
+}
+
+template <int MP, int MODE>
 __device__ __forceinline__ void load_raw(const SplitParams &p, RawQ &r, int g0, int np_groups, int item, bool &live) {
-  const int q = item & 3, rest = item >> 2;
-  const int gl = rest % p.GP, m = rest / p.GP;
+  int m, q, gl;
+  item_coords<MP, MODE>(item, p.GP, m, q, gl);
   live = item < MP * p.GP * 4;
   r.in = live && m < p.M && gl < np_groups;
   const uint16_t *src = p.X + (r.in ? (int64_t)m * p.K + 128 * (g0 + gl) + 8 * q : 0);
@@ -96,8 +119,8 @@ __device__ __forceinline__ void load_raw(const SplitParams &p, RawQ &r, int g0, 
 
 template <int FMT, int MP, int MODE>
 __device__ __forceinline__ void convert_raw(const SplitParams &p, const RawQ &r, char *buf, int item) {
-  const int q = item & 3, rest = item >> 2;
-  const int gl = rest % p.GP, m = rest / p.GP;
+  int m, q, gl;
+  item_coords<MP, MODE>(item, p.GP, m, q, gl);
   const u4_t z = {0u, 0u, 0u, 0u};
   u4_t v[4];
 #pragma unroll
@@ -262,7 +285,7 @@ __global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(Sp
   const int cpp = p.GP / 4;  // chunks per pass
   RawQ raw;
   bool live;
-  load_raw<MP>(p, raw, g0, min(p.GP, ng), threadIdx.x, live);
+  load_raw<MP, MODE>(p, raw, g0, min(p.GP, ng), threadIdx.x, live);
 
   // Weights: a ring of two units.  Every step computes one chunk and issues
   // the load of the chunk two ahead, clamped to the range's last chunk, so
@@ -287,7 +310,7 @@ __global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(Sp
   }
   lds_barrier();
   // The raw x of pass 1 goes out while pass 0 is multiplied.
-  if (CPP > 0 || npass > 1) load_raw<MP>(p, raw, g0 + p.GP, min(p.GP, ng - p.GP), threadIdx.x, live);
+  if (CPP > 0 || npass > 1) load_raw<MP, MODE>(p, raw, g0 + p.GP, min(p.GP, ng - p.GP), threadIdx.x, live);
 
   float yacc[R][1][4];
 #pragma unroll
@@ -310,7 +333,7 @@ __global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(Sp
         if (live) convert_raw<FMT, MP, MODE>(p, raw, lds + (ps & 1) * p.buf_bytes, threadIdx.x);
         lds_barrier();
         const int nx = (ps + 1) * p.GP;
-        load_raw<MP>(p, raw, g0 + nx, min(p.GP, ng - nx), threadIdx.x, live);
+        load_raw<MP, MODE>(p, raw, g0 + nx, min(p.GP, ng - nx), threadIdx.x, live);
       }
       const char *cur = lds + (ps & 1) * p.buf_bytes;
       const int png = min(p.GP, ng - ps * p.GP);
@@ -335,7 +358,7 @@ __global__ void __launch_bounds__(64 * NW, NW <= 8 ? 2 : 1) gemv_split_kernel(Sp
           if (live) convert_raw<FMT, MP, MODE>(p, raw, lds + (ps & 1) * p.buf_bytes, threadIdx.x);
           lds_barrier();
           const int nx = (ps + 1) * p.GP;
-          if (ps + 1 < npass) load_raw<MP>(p, raw, g0 + nx, min(p.GP, ng - nx), threadIdx.x, live);
+          if (ps + 1 < npass) load_raw<MP, MODE>(p, raw, g0 + nx, min(p.GP, ng - nx), threadIdx.x, live);
         }
         const char *cur = lds + (ps & 1) * p.buf_bytes;
         const int png = min(p.GP, ng - ps * p.GP);

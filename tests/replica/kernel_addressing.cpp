@@ -250,8 +250,10 @@ void split_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X, Buf &ws) 
       const int64_t gb = g0 + ps * GP, npg = std::min<int64_t>(GP, ng - ps * GP);
       const int64_t base = (ps & 1) * buf_bytes;
       for (int item = 0; item < threads; ++item) {
-        const int q = item & 3, rest = item >> 2;
-        const int64_t gl = rest % GP, m = rest / GP;
+        // Token slot fastest in the exact modes, lane quarter fastest with fp8 pieces.
+        const int64_t m = fp4 ? (item >> 2) / GP : item % MP;
+        const int q = fp4 ? (item & 3) : int((item / MP) & 3);
+        const int64_t gl = fp4 ? (item >> 2) % GP : (item / MP) >> 2;
         const bool live = item < MP * GP * 4;
         const bool in = live && m < M && gl < npg;
         const int64_t src = in ? m * K + 128 * (gb + gl) + 8 * q : 0;
@@ -278,8 +280,10 @@ void split_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X, Buf &ws) 
     if (MP == 16 && GP == 8) {
       const int64_t gb = g0 + npass * GP, npg = std::min<int64_t>(GP, ng - npass * GP);
       for (int item = 0; item < threads; ++item) {
-        const int q = item & 3, rest = item >> 2;
-        const int64_t gl = rest % GP, m = rest / GP;
+        // Token slot fastest in the exact modes, lane quarter fastest with fp8 pieces.
+        const int64_t m = fp4 ? (item >> 2) / GP : item % MP;
+        const int q = fp4 ? (item & 3) : int((item / MP) & 3);
+        const int64_t gl = fp4 ? (item >> 2) % GP : (item / MP) >> 2;
         const bool in = item < MP * GP * 4 && m < M && gl < npg;
         const int64_t src = in ? m * K + 128 * (gb + gl) + 8 * q : 0;
         for (int u = 0; u < 4; ++u) X.read(2 * (src + 32 * u), 16, "x (staging past the range)");
