@@ -639,7 +639,9 @@ hipError_t launch_mt(const LaunchArgs &a) {
 //  * one token: the workgroup-staged kernel above (x of the whole K in LDS);
 //  * 2..8 tokens: the staged kernel, or the 2-D split (row blocks x K
 //    ranges, x converted once per block, gemv_split.hip) on long rows, on
-//    4+ tokens below 65536 rows, and on 5+ tokens of very tall matrices;
+//    2 tokens from 24576 rows, on 3+ tokens below 65536 rows (at 3-4
+//    tokens only where the split's plan fills two thirds of the CUs),
+//    and on 5+ tokens of very tall matrices;
 //  * 9..16 tokens: waves that split K over three or more row tiles per
 //    workgroup (gemv_kslice.hip) when K is 4..10 whole chunks and the matrix
 //    has the tiles for it; else the 2-D split; without a workspace on a
@@ -656,6 +658,20 @@ hipError_t launch_mt(const LaunchArgs &a) {
 // bound (|w| = s throughout a group), so that error stays below 2^-12 of the
 // bound's sum; a ternary zero can drop the large value from the sum, so tq2
 // always takes exact operands.
+// Whether the split kernel's plan for this call keeps at least two thirds
+// of the CUs busy (asked of its own planner, which launches nothing when it
+// records a plan).  At 4 tokens a matrix of 1088 row tiles gets 136 row
+// blocks and no K cut from it, and there the staged kernel takes 9.9 us
+// against 12.0 us; 182 blocks (2176 tiles, 12 waves each) tie with it at
+// 4 tokens and win at 2 (11.9 against 12.3 us).
+inline bool split_fills_chip(const LaunchArgs &a) {
+  lowbit_plan pl{};
+  LaunchArgs b = a;
+  b.plan = &pl;
+  if (launch_gemv_split(b) != hipSuccess) return false;
+  return 3 * int64_t(pl.grid) >= 2 * int64_t(num_cus());
+}
+
 template <int FMT, bool BF>
 hipError_t launch_fmt(const LaunchArgs &a) {
   const bool ws_ok = a.ws && a.ws_bytes >= gemv_split_workspace_bytes(a.M, a.N, a.K);
@@ -667,8 +683,9 @@ hipError_t launch_fmt(const LaunchArgs &a) {
       if (launch_gemv_kslice(a, e)) return e;
       return split_ok ? launch_gemv_split(a) : launch_gemv_wide(a);
     }
-    const bool split = a.M >= 2 && ((ws_ok && (a.K >= 8192 || (a.M >= 4 && a.N < 65536))) ||
-                                    (a.M > 4 && a.N >= 65536));
+    bool split = a.M >= 2 && ((ws_ok && (a.K >= 8192 || (a.M >= 3 ? a.N < 65536 : a.N >= 24576))) ||
+                              (a.M > 4 && a.N >= 65536));
+    if (split && a.M <= 4 && a.K < 8192) split = split_fills_chip(a);
     if (split) return launch_gemv_split(a);
     if (a.M <= 1) return launch_mt<FMT, BF, 1, true, 1, 2>(a);
     if (a.M <= 2) return launch_mt<FMT, BF, 2, true, 2, RB>(a);

@@ -628,8 +628,15 @@ hipError_t launch_split_fmt(const LaunchArgs &a) {
     if (a.M <= 8) return launch_split_mp<FMT, 8, MODE>(a);
     return launch_split_mp<FMT, 16, MODE>(a);
   } else {
+    // Exact operands take 16 token slots from two tokens on: the 16-slot
+    // launches stage x in passes of two chunks on the pass-structured loop,
+    // and with 4 slots (passes of eight chunks, the general loop) the
+    // 27B-class tq2 GEMVs at 2-4 tokens took 19.1-19.3 us on 34816 x 5120
+    // and 13.5-14.1 us on 5120 x 17408, against 16.2-16.6 and 12.5-13.0 us
+    // with 16.  The fp8-piece path keeps its 2, 4 and 8 slots: there one
+    // MFMA per (tile, group) covers both pieces of up to 8 tokens, and 16
+    // slots were 10-30% slower.
     if (a.M <= 1) return launch_split_mp<FMT, 1, MODE>(a);
-    if (a.M <= 4) return launch_split_mp<FMT, 4, MODE>(a);
     return launch_split_mp<FMT, 16, MODE>(a);
   }
 }
