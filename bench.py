@@ -576,12 +576,18 @@ def measured_traffic(dom):
     except OSError:
         return None, None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_sha256") != _source_digest() or kv.get("sweep") != f"{dom[0]}_M{dom[1]}":
+    name = f"{dom[0]}_M{dom[1]}"
+    if kv.get("source_sha256") != _source_digest():
+        return None, None
+    # Per-sweep figures ("fetch_bytes_per_launch.<sweep>: ..."), or one sweep's
+    # figures under a "sweep: <sweep>" line.
+    suffix = f".{name}" if f"fetch_bytes_per_launch.{name}" in kv else ""
+    if not suffix and kv.get("sweep") != name:
         return None, None
 
     def num(key):
         try:
-            return int(float(kv[key]))
+            return int(float(kv[key + suffix]))
         except (KeyError, ValueError):
             return None
 

@@ -68,6 +68,22 @@ def test_measured_traffic_reads_only_a_current_summary(tmp_path, monkeypatch):
     assert bench.measured_traffic(("tq2", 16)) == (None, None)
 
 
+def test_measured_traffic_per_sweep_lines(tmp_path):
+    digest = bench._source_digest()
+    p = tmp_path / "traffic.txt"
+    p.write_text("\n".join(["# summary", f"source_sha256: {digest}",
+                             "fetch_bytes_per_launch.tq2_M16: 1000", "write_bytes_per_launch.tq2_M16: 200",
+                             "fetch_bytes_per_launch.q1_M16: 700", "write_bytes_per_launch.q1_M16: 100"]) + "\n")
+    old = bench.TRAFFIC_FILE
+    bench.TRAFFIC_FILE = str(p)
+    try:
+        assert bench.measured_traffic(("tq2", 16)) == (1200, 1000)
+        assert bench.measured_traffic(("q1", 16)) == (800, 700)
+        assert bench.measured_traffic(("q1", 1)) == (None, None)  # not measured
+    finally:
+        bench.TRAFFIC_FILE = old
+
+
 def test_committed_summary_has_the_machine_readable_lines():
     keys = {}
     with open(bench.TRAFFIC_FILE) as f:
