@@ -92,8 +92,10 @@ def test_committed_summary_has_the_machine_readable_lines():
                 k, v = ln.split(":", 1)
                 keys[k.strip()] = v.strip()
     assert len(keys["source_sha256"]) == 64
-    assert keys["sweep"] in {f"{f}_M{m}" for f in ("q1", "tq2") for m in (1, 16)}
-    assert int(keys["fetch_bytes_per_launch"]) > 0 and int(keys["write_bytes_per_launch"]) > 0
+    sweeps = [k.split(".", 1)[1] for k in keys if k.startswith("fetch_bytes_per_launch.")]
+    assert sweeps and set(sweeps) <= {f"{f}_M{m}" for f in ("q1", "tq2") for m in (1, 16)}
+    for sw in sweeps:
+        assert int(keys[f"fetch_bytes_per_launch.{sw}"]) > 0 and int(keys[f"write_bytes_per_launch.{sw}"]) > 0
 
 
 def test_cpu_baseline_leg_reports_the_oracle():
