@@ -528,7 +528,8 @@ def shape_timings(torch, lb, dev, seed):
 def part_arithmetic(lb, sweeps, gemm_ids, launches, layers, ws_bytes, gws_bytes):
     """What each timed part multiplies, from the plan queries of its
     launches: kernel and operand types (fp8_fp4 = bf16 x as two exact fp8
-    pieces x fp4 weights on the scaled MFMA; bf16 / f16 = exact operands on
+    pieces x fp4 weights on the scaled MFMA; fp8x3_fp4 = fp16 x as three
+    pieces, the same MFMA; bf16 / f16 = exact operands on
     v_mfma_f32_16x16x32); every part accumulates in fp32."""
     out = {}
     for fmt, m in sweeps:

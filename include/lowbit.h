@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LOWBIT_ABI_VERSION 6
+#define LOWBIT_ABI_VERSION 7
 
 typedef enum { LOWBIT_Q1_G128 = 1, LOWBIT_TQ2_G128 = 2, LOWBIT_TQ5_G128 = 3 } lowbit_format;
 typedef enum { LOWBIT_F16 = 1, LOWBIT_BF16 = 2, LOWBIT_F32 = 3 } lowbit_dtype;
@@ -263,7 +263,8 @@ typedef enum {
   LOWBIT_OPERANDS_NONE = 0,
   LOWBIT_OPERANDS_F16 = 1,     /* exact f16 operands on v_mfma_f32_16x16x32_f16            */
   LOWBIT_OPERANDS_BF16 = 2,    /* exact bf16 operands on v_mfma_f32_16x16x32_bf16          */
-  LOWBIT_OPERANDS_FP8_FP4 = 3  /* x as two fp8 pieces, weights as fp4, scaled 16x16x128    */
+  LOWBIT_OPERANDS_FP8_FP4 = 3,   /* bf16 x as two fp8 pieces, weights as fp4, scaled 16x16x128 */
+  LOWBIT_OPERANDS_FP8X3_FP4 = 4  /* fp16 x as three fp8 pieces, weights as fp4, the same MFMA    */
 } lowbit_operands;
 
 typedef struct {

@@ -21,7 +21,7 @@ _lib = None
 
 KERNELS = {0: "none", 1: "gemv_staged", 2: "gemv_split", 3: "gemv_wide", 4: "gemv_tq5", 5: "gemv_tq5_one",
            6: "gemm", 7: "fill_zero", 8: "gemv_kslice"}
-OPERANDS = {0: "none", 1: "f16", 2: "bf16", 3: "fp8_fp4"}
+OPERANDS = {0: "none", 1: "f16", 2: "bf16", 3: "fp8_fp4", 4: "fp8x3_fp4"}
 
 
 class Plan(ctypes.Structure):

@@ -230,6 +230,81 @@ __device__ __forceinline__ void split_x_regs(const u4_t (&x)[4], XQuarter &o) {
   o.sb = uint8_t(sb);
 }
 
+// fp16 x in three pieces: the same 32 values and nibble order, with pieces
+// hi, mid and lo (x = S (hi + mid + lo)).  An fp16 value has 11 significant
+// bits and each piece 4, so the split is exact for every value within 2^6
+// of the block's largest (the lowest bit of those lands at or above 2^-9 of
+// the scaled range, the smallest fp8 step); a value further below carries
+// an error below 2^-17 of that largest, as in the two-piece bf16 split.  sb
+// puts the largest magnitude in [128, 256) for normal values and scales
+// fp16 subnormals as if their exponent were the smallest normal one (they
+// then scale to at most 128 and stay exact); a block holding inf or nan
+// gets the nan scale 0xFF.
+struct XQuarter3 {
+  u4_t h0, h1, m0, m1, l0, l1;
+  uint8_t sb;
+};
+
+template <int FMT>
+__device__ __forceinline__ void split_x_regs_f16(const u4_t (&x)[4], XQuarter3 &o) {
+  uint32_t v[16];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    v[4 * u + 0] = x[u].x;
+    v[4 * u + 1] = x[u].y;
+    v[4 * u + 2] = x[u].z;
+    v[4 * u + 3] = x[u].w;
+  }
+  typedef unsigned short u2h_t __attribute__((ext_vector_type(2)));
+  u2h_t m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u2h_t, v[i] & 0x7FFF7FFFu));
+  const uint32_t mx = max(uint32_t(m2.x), uint32_t(m2.y));
+  const int ef = int(mx >> 10);  // fp16 exponent field of the largest magnitude
+  const int sb = ef == 31 ? 255 : max(ef, 1) + 105;
+  const float S = __builtin_bit_cast(float, uint32_t(min(sb, 254)) << 23);
+  typedef short s2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  int hi[8], mid[8], lo[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t h[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int sidx = fp4_src(FMT, 4 * w + b);  // 8u + e
+      h[b] = (sidx & 1) ? (v[sidx / 2] >> 16) : (v[sidx / 2] & 0xFFFFu);
+    }
+    s2_t ph = {0, 0}, pm = {0, 0}, pl = {0, 0};
+    ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(ph, __builtin_bit_cast(h2_t, h[0] | (h[1] << 16)), S, false);
+    ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(ph, __builtin_bit_cast(h2_t, h[2] | (h[3] << 16)), S, true);
+    hi[w] = __builtin_bit_cast(int, ph);
+    const f2_t b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi[w], S, false);
+    const f2_t b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi[w], S, true);
+    // Residuals in fp32 are exact: both terms are multiples of the value's
+    // lowest bit and the difference is below 2^4 of S.
+    const float r0 = float(__builtin_bit_cast(_Float16, uint16_t(h[0]))) - b01.x;
+    const float r1 = float(__builtin_bit_cast(_Float16, uint16_t(h[1]))) - b01.y;
+    const float r2 = float(__builtin_bit_cast(_Float16, uint16_t(h[2]))) - b23.x;
+    const float r3 = float(__builtin_bit_cast(_Float16, uint16_t(h[3]))) - b23.y;
+    pm = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pm, r0, r1, S, false);
+    pm = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pm, r2, r3, S, true);
+    mid[w] = __builtin_bit_cast(int, pm);
+    const f2_t c01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(mid[w], S, false);
+    const f2_t c23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(mid[w], S, true);
+    pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, r0 - c01.x, r1 - c01.y, S, false);
+    pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, r2 - c23.x, r3 - c23.y, S, true);
+    lo[w] = __builtin_bit_cast(int, pl);
+  }
+  o.h0 = u4_t{uint32_t(hi[0]), uint32_t(hi[1]), uint32_t(hi[2]), uint32_t(hi[3])};
+  o.h1 = u4_t{uint32_t(hi[4]), uint32_t(hi[5]), uint32_t(hi[6]), uint32_t(hi[7])};
+  o.m0 = u4_t{uint32_t(mid[0]), uint32_t(mid[1]), uint32_t(mid[2]), uint32_t(mid[3])};
+  o.m1 = u4_t{uint32_t(mid[4]), uint32_t(mid[5]), uint32_t(mid[6]), uint32_t(mid[7])};
+  o.l0 = u4_t{uint32_t(lo[0]), uint32_t(lo[1]), uint32_t(lo[2]), uint32_t(lo[3])};
+  o.l1 = u4_t{uint32_t(lo[4]), uint32_t(lo[5]), uint32_t(lo[6]), uint32_t(lo[7])};
+  o.sb = uint8_t(sb);
+}
+
 // The same from memory: src points at x[m][128 g + 8 q]; in == false gives
 // zeros (src must still be a readable address).
 template <int FMT>

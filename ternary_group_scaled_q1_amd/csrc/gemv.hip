@@ -79,15 +79,16 @@ inline LdsMap lds_map(int MTS, int S, int SC, int R, int E) {
   return m;
 }
 
-// fp8 x fp4 path: per group, 2*MP A rows of kRowBytes (gemv_common.hpp),
-// then MP*4 E8M0 scale bytes per group.
+// fp8 x fp4 path: per group, NPC*MP A rows of kRowBytes (gemv_common.hpp),
+// then MP*4 E8M0 scale bytes per group.  NPC = pieces per token: two for
+// bf16 x, three for fp16 x (one token only).
 
-inline LdsMap lds_map_fp4(int MP, int S, int SC, int R, int E) {
+inline LdsMap lds_map_fp4(int MP, int NPC, int S, int SC, int R, int E) {
   LdsMap m;
   const int groups = 4 * SC;
   m.corr = 0;
   m.x = 0;
-  int o = groups * 2 * MP * kRowBytes;
+  int o = groups * NPC * MP * kRowBytes;
   m.corr = o;  // E8M0 scale bytes
   o += (groups * MP * 4 + 15) / 16 * 16;
   m.red = o;
@@ -125,12 +126,13 @@ __device__ __forceinline__ void fp4_item_load(const GemvParams &p, int it, int c
   for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const u4_t *>(src + 32 * u);
 }
 
-// Splits the item's 32 values (split_x_regs) into A rows 2m (hi) and 2m + 1
-// (lo) of its group and writes its E8M0 scale byte.  The quarter's values sit
-// at hardware k 32q + n; the A operand holds k < 64 in bytes 0..15 and
+// Splits the item's 32 values into A rows 2m (hi) and 2m + 1 (lo) of its
+// group (bf16 x, split_x_regs), or 3m, 3m + 1, 3m + 2 (hi, mid, lo: fp16 x,
+// split_x_regs_f16), and writes its E8M0 scale byte.  The quarter's values
+// sit at hardware k 32q + n; the A operand holds k < 64 in bytes 0..15 and
 // k >= 64 in bytes 16..31 of lane quarter (k % 64) / 16, so nibbles 0..15 go
 // to lane quarter 2(q % 2) and 16..31 to 2(q % 2) + 1.
-template <int FMT, int MP>
+template <int FMT, bool BF, int MP>
 __device__ __forceinline__ void fp4_item_write(const GemvParams &p, char *lds, int it, int c0, int nc,
                                                const u4_t (&raw)[4]) {
   const int q = it & 3, rest = it >> 2;
@@ -141,32 +143,45 @@ __device__ __forceinline__ void fp4_item_write(const GemvParams &p, char *lds, i
   u4_t x[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) x[u] = in ? raw[u] : z;
-  XQuarter xq;
-  split_x_regs<FMT>(x, xq);
-  char *row = lds + p.off_x + (gl * 2 * MP + 2 * m) * kRowBytes;
   const int qa = 2 * (q & 1), half = 16 * (q >> 1);
-  *reinterpret_cast<u4_t *>(row + qa * 32 + half) = xq.h0;
-  *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = xq.h1;
-  *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = xq.l0;
-  *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = xq.l1;
-  reinterpret_cast<uint8_t *>(lds + p.off_corr)[(gl * MP + m) * 4 + q] = xq.sb;
+  if constexpr (BF) {
+    XQuarter xq;
+    split_x_regs<FMT>(x, xq);
+    char *row = lds + p.off_x + (gl * 2 * MP + 2 * m) * kRowBytes;
+    *reinterpret_cast<u4_t *>(row + qa * 32 + half) = xq.h0;
+    *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = xq.h1;
+    *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = xq.l0;
+    *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = xq.l1;
+    reinterpret_cast<uint8_t *>(lds + p.off_corr)[(gl * MP + m) * 4 + q] = xq.sb;
+  } else {
+    XQuarter3 xq;
+    split_x_regs_f16<FMT>(x, xq);
+    char *row = lds + p.off_x + (gl * 3 * MP + 3 * m) * kRowBytes;
+    *reinterpret_cast<u4_t *>(row + qa * 32 + half) = xq.h0;
+    *reinterpret_cast<u4_t *>(row + (qa + 1) * 32 + half) = xq.h1;
+    *reinterpret_cast<u4_t *>(row + kRowBytes + qa * 32 + half) = xq.m0;
+    *reinterpret_cast<u4_t *>(row + kRowBytes + (qa + 1) * 32 + half) = xq.m1;
+    *reinterpret_cast<u4_t *>(row + 2 * kRowBytes + qa * 32 + half) = xq.l0;
+    *reinterpret_cast<u4_t *>(row + 2 * kRowBytes + (qa + 1) * 32 + half) = xq.l1;
+    reinterpret_cast<uint8_t *>(lds + p.off_corr)[(gl * MP + m) * 4 + q] = xq.sb;
+  }
 }
 
 // Stage chunks [c0, c0 + nc) of x for the fp8 x fp4 path: one item per
 // (token slot, group, lane quarter); tokens m >= M and groups past K stage as
 // zeros.  PRE: the thread's first item was loaded into first.
-template <int FMT, int MP, bool PRE>
+template <int FMT, bool BF, int MP, bool PRE>
 __device__ void stage_fp4(const GemvParams &p, char *lds, int c0, int nc, const XFirst<true> &first) {
   const int items = MP * 4 * nc * 4;
   int it = threadIdx.x;
   if constexpr (PRE) {
-    if (it < items) fp4_item_write<FMT, MP>(p, lds, it, c0, nc, first.v);
+    if (it < items) fp4_item_write<FMT, BF, MP>(p, lds, it, c0, nc, first.v);
     it += kThreads;
   }
   for (; it < items; it += kThreads) {
     u4_t raw[4];
     fp4_item_load<MP>(p, it, c0, nc, raw);
-    fp4_item_write<FMT, MP>(p, lds, it, c0, nc, raw);
+    fp4_item_write<FMT, BF, MP>(p, lds, it, c0, nc, raw);
   }
 }
 
@@ -280,20 +295,20 @@ __device__ __forceinline__ void store_tiles(const GemvParams &p, int t0, const f
 }
 
 // fp8 x fp4 path, one unit (R tiles x 4 groups).  Lane 16qa + r reads A row
-// r (token r / 2, piece r % 2) of each group; rows past 2*MP are zero.
-template <int FMT, int MP, int R, int E>
+// r (token r / NPC, piece r % NPC) of each group; rows past NPC*MP are zero.
+template <int FMT, int MP, int NPC, int R, int E>
 __device__ __forceinline__ void compute_fp4(const GemvParams &p, const char *lds, const Unit<FMT, R> &u, int c_local,
                                             float (&yacc)[R][4]) {
   const int lane = threadIdx.x & 63, qa = lane >> 4, r = lane & 15;
-  // Lanes of A rows past 2 MP read row 0 again: an A row only feeds the same
-  // row of the product, and those rows are never stored.
-  const int rr = r < 2 * MP ? r : 0;
-  const char *xa = lds + p.off_x + (c_local * 4 * 2 * MP + rr) * kRowBytes + qa * 32;
-  const uint8_t *sa = reinterpret_cast<const uint8_t *>(lds + p.off_corr) + (c_local * 4 * MP + (rr >> 1)) * 4 + qa;
+  // Lanes of A rows past NPC MP read row 0 again: an A row only feeds the
+  // same row of the product, and those rows are never stored.
+  const int rr = r < NPC * MP ? r : 0;
+  const char *xa = lds + p.off_x + (c_local * 4 * NPC * MP + rr) * kRowBytes + qa * 32;
+  const uint8_t *sa = reinterpret_cast<const uint8_t *>(lds + p.off_corr) + (c_local * 4 * MP + rr / NPC) * 4 + qa;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const u4_t a0 = *reinterpret_cast<const u4_t *>(xa + g * 2 * MP * kRowBytes);
-    const u4_t a1 = *reinterpret_cast<const u4_t *>(xa + g * 2 * MP * kRowBytes + 16);
+    const u4_t a0 = *reinterpret_cast<const u4_t *>(xa + g * NPC * MP * kRowBytes);
+    const u4_t a1 = *reinterpret_cast<const u4_t *>(xa + g * NPC * MP * kRowBytes + 16);
     const int sc = sa[g * MP * 4];
 #pragma unroll
     for (int r2 = 0; r2 < R; ++r2) {
@@ -308,9 +323,10 @@ __device__ __forceinline__ void compute_fp4(const GemvParams &p, const char *lds
   }
 }
 
-// Accumulator element e of lane 16qa + j is A row 4qa + e: token 2qa + e / 2,
-// piece e % 2.
-template <int FMT, int R, int E>
+// Accumulator element e of lane 16qa + j is A row 4qa + e: with two pieces
+// token 2qa + e / 2, piece e % 2; with three (one token) token 0, piece e,
+// all in lane quarter 0.
+template <int FMT, int NPC, int R, int E>
 __device__ __forceinline__ void store_fp4(const GemvParams &p, int t0, const float (&yacc)[R][4]) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, qa = lane >> 4;
@@ -319,10 +335,14 @@ __device__ __forceinline__ void store_fp4(const GemvParams &p, int t0, const flo
   for (int r = 0; r < R; ++r) {
     if (t0 + r >= p.tiles) continue;
     const TileRef tr = tile_ref(p.ms, t0 + r);
+    if constexpr (NPC == 3) {
+      if (qa == 0) store_y(tr, j, 0, ((yacc[r][0] + yacc[r][1]) + yacc[r][2]) * mul, p.y_f16);
+    } else {
 #pragma unroll
-    for (int tt = 0; tt < E / 2; ++tt) {
-      const int m = 2 * qa + tt;
-      if (m < p.M) store_y(tr, j, m, (yacc[r][2 * tt] + yacc[r][2 * tt + 1]) * mul, p.y_f16);
+      for (int tt = 0; tt < E / 2; ++tt) {
+        const int m = 2 * qa + tt;
+        if (m < p.M) store_y(tr, j, m, (yacc[r][2 * tt] + yacc[r][2 * tt + 1]) * mul, p.y_f16);
+      }
     }
   }
 }
@@ -366,7 +386,10 @@ constexpr int gemv_min_waves() {
 template <int FMT, bool BF, int MT, int R, int D, bool FP4, bool FULL>
 __global__ void __launch_bounds__(kThreads, (gemv_min_waves<MT, R, FP4>())) gemv_kernel(GemvParams p) {
   // Accumulator elements that can hold a token (fp4: A rows, two per token).
-  constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
+  // fp8 pieces per token: two for bf16 x, three for fp16 x (one token only).
+  constexpr int NPC = BF ? 2 : 3;
+  static_assert(!FP4 || BF || MT == 1, "fp16 x on the fp8 x fp4 path covers one token");
+  constexpr int E = FP4 ? (MT == 1 ? NPC : 4) : (MT == 1 ? 1 : 4);
   constexpr int MTS = MT;                // token slots per x cell
   extern __shared__ __align__(16) char lds[];
   const int wave = uni(threadIdx.x >> 6);
@@ -430,7 +453,7 @@ __global__ void __launch_bounds__(kThreads, (gemv_min_waves<MT, R, FP4>())) gemv
 #pragma unroll
   for (int d = 0; d < D - 1; ++d) load(ring[d], d < total);
   if (!restage) {
-    if constexpr (FP4) stage_fp4<FMT, MT, true>(p, lds, 0, p.chunks, xf);
+    if constexpr (FP4) stage_fp4<FMT, BF, MT, true>(p, lds, 0, p.chunks, xf);
     else stage_x<FMT, BF, MTS, true>(p, lds, 0, p.chunks, xf);
     lds_barrier();
   }
@@ -460,14 +483,14 @@ __global__ void __launch_bounds__(kThreads, (gemv_min_waves<MT, R, FP4>())) gemv
       if (restage && cu.kl == 0) {
         lds_barrier();
         const int c0 = cu.st * p.SC;
-        if constexpr (FP4) stage_fp4<FMT, MT, false>(p, lds, c0, min(p.SC, p.chunks - c0), xf);
+        if constexpr (FP4) stage_fp4<FMT, BF, MT, false>(p, lds, c0, min(p.SC, p.chunks - c0), xf);
         else stage_x<FMT, BF, MTS, false>(p, lds, c0, min(p.SC, p.chunks - c0), xf);
         lds_barrier();
       }
       if (is_valid(cu)) {
         const int c_local = s + cu.kl * S;
         if constexpr (FP4) {
-          compute_fp4<FMT, MT, R, E>(p, lds, ring[d], c_local, yacc);
+          compute_fp4<FMT, MT, NPC, R, E>(p, lds, ring[d], c_local, yacc);
         } else {
           const int xbase = xact ? p.off_x + (c_local * 64 * MTS + q * MTS + j) * 16 : 0;
           compute_unit<FMT, BF, R, E, MTS>(p, lds, ring[d], c_local, xbase, yacc);
@@ -477,7 +500,7 @@ __global__ void __launch_bounds__(kThreads, (gemv_min_waves<MT, R, FP4>())) gemv
         const bool ts_ok = t0 < p.tiles;
         if (S == 1) {
           if (ts_ok) {
-            if constexpr (FP4) store_fp4<FMT, R, E>(p, t0, yacc);
+            if constexpr (FP4) store_fp4<FMT, NPC, R, E>(p, t0, yacc);
             else store_tiles<FMT, R, E>(p, t0, yacc);
           }
         } else {
@@ -497,7 +520,7 @@ __global__ void __launch_bounds__(kThreads, (gemv_min_waves<MT, R, FP4>())) gemv
                 for (int s2 = 0; s2 < S; ++s2) v += red[(((pr * S + s2) * R + r) * E + e) * 64 + lane];
                 tot[r][e] = v;
               }
-            if constexpr (FP4) store_fp4<FMT, R, E>(p, t0, tot);
+            if constexpr (FP4) store_fp4<FMT, NPC, R, E>(p, t0, tot);
             else store_tiles<FMT, R, E>(p, t0, tot);
           }
           lds_barrier();
@@ -520,7 +543,8 @@ __global__ void __launch_bounds__(kThreads, (gemv_min_waves<MT, R, FP4>())) gemv
 // with exact operands the one-tile plan stays ahead, 11.3 against 11.7).
 template <int FMT, bool BF, int MT, int R, int D, bool FP4, bool FULL>
 double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) {
-  constexpr int E = FP4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
+  constexpr int NPC = BF ? 2 : 3;
+  constexpr int E = FP4 ? (MT == 1 ? NPC : 4) : (MT == 1 ? 1 : 4);
   p = GemvParams{};
   const int64_t G = a.K / kGroup;
   p.ms = mat_set(a);
@@ -532,9 +556,9 @@ double make_plan(const LaunchArgs &a, GemvParams &p, int &grid, int &lds_bytes) 
   p.y_f16 = a.y_f16;
   const int cus = num_cus();
   const void *kern = reinterpret_cast<const void *>(&gemv_kernel<FMT, BF, MT, R, D, FP4, FULL>);
-  auto map = [&](int S, int SC) { return FP4 ? lds_map_fp4(MT, S, SC, R, E) : lds_map(MT, S, SC, R, E); };
+  auto map = [&](int S, int SC) { return FP4 ? lds_map_fp4(MT, NPC, S, SC, R, E) : lds_map(MT, S, SC, R, E); };
   // x bytes a stage of SC chunks occupies.
-  auto xbytes = [&](int SC) { return FP4 ? SC * 4 * (2 * MT * kRowBytes + 4 * MT) : MT * SC * 1024; };
+  auto xbytes = [&](int SC) { return FP4 ? SC * 4 * (NPC * MT * kRowBytes + 4 * MT) : MT * SC * 1024; };
 
   double best = 1e300;
   GemvParams bp = p;
@@ -599,7 +623,8 @@ hipError_t launch_mt_full(const LaunchArgs &a) {
     const GemvParams &p = one ? p1 : p2;
     lowbit_plan &o = plan_record(a, LOWBIT_KERNEL_GEMV_STAGED, one ? g1 : g2, kThreads, one ? l1 : l2);
     o.token_slots = MT;
-    o.operands = FP4 ? LOWBIT_OPERANDS_FP8_FP4 : (BF ? LOWBIT_OPERANDS_BF16 : LOWBIT_OPERANDS_F16);
+    o.operands = FP4 ? (BF ? LOWBIT_OPERANDS_FP8_FP4 : LOWBIT_OPERANDS_FP8X3_FP4)
+                     : (BF ? LOWBIT_OPERANDS_BF16 : LOWBIT_OPERANDS_F16);
     o.whole_tiles = FULL;
     o.tiles_per_wave = one ? RA : RB;
     o.ring = one ? DA : DB;
@@ -646,6 +671,8 @@ hipError_t launch_mt(const LaunchArgs &a) {
 //    workgroup (gemv_kslice.hip) when K is 4..10 whole chunks and the matrix
 //    has the tiles for it; else the 2-D split; without a workspace on a
 //    small matrix, x loaded straight into registers (gemv_wide.hip).
+// Binary weights with fp16 x at one token: the staged kernel on the fp8 x
+// fp4 instruction with three pieces per value (fp16 has 11 significant bits).
 // Exact f16 / bf16 operands (ternary weights, fp16 x): the staged kernel for
 // up to 4 tokens unless the rows are long or the matrix tall, the 2-D split
 // for 5..8 tokens on 8192+ rows or long rows and for 9..16 tokens (the
@@ -653,8 +680,8 @@ hipError_t launch_mt(const LaunchArgs &a) {
 //
 // The fp8 x fp4 kernels (the staged one with FP4, and the split) hold each
 // 32-value activation block at one shared exponent: values within 2^7 of
-// the block's largest stay exact, smaller ones carry an error below 2^-17 of
-// it.  With binary weights every product of the block counts in the error
+// the block's largest stay exact (bf16 x, two pieces; fp16 x, three pieces:
+// within 2^6), smaller ones carry an error below 2^-17 of it.  With binary weights every product of the block counts in the error
 // bound (|w| = s throughout a group), so that error stays below 2^-12 of the
 // bound's sum; a ternary zero can drop the large value from the sum, so tq2
 // always takes exact operands.
@@ -701,7 +728,12 @@ hipError_t launch_fmt(const LaunchArgs &a) {
       const bool split = a.K >= 8192 || (a.M > 4 ? a.N >= 8192 : (a.N >= 24576 && a.N < 65536));
       if (split && split_ok) return launch_gemv_split(a);
     }
-    if (a.M <= 1) return launch_mt<FMT, BF, 1, false, 1, 2>(a);
+    if (a.M <= 1) {
+      // Binary weights, fp16 x, one token: three fp8 pieces per value on the
+      // fp8 x fp4 instruction (one MFMA per tile and group, as for bf16 x).
+      if constexpr (FMT == 1 && !BF) return launch_mt<FMT, BF, 1, true, 1, 2>(a);
+      else return launch_mt<FMT, BF, 1, false, 1, 2>(a);
+    }
     if (a.M <= 4) return launch_mt<FMT, BF, 4, false, 1, 2>(a);
     return launch_gemv_wide(a);
   }

@@ -443,7 +443,9 @@ void kslice_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
 void staged_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
   const int fmt = ms.fmt;
   const int MT = int(P["token_slots"]), R = int(P["tiles_per_wave"]), D = int(P["ring"]);
-  const bool fp4 = P["operands"] == 3, full = P["whole_tiles"] != 0;
+  // fp8 x fp4 operands: two pieces per token (bf16 x) or three (fp16 x, one token).
+  const bool fp4 = P["operands"] == 3 || P["operands"] == 4, full = P["whole_tiles"] != 0;
+  const int NPC = P["operands"] == 4 ? 3 : 2;
   const int S = int(P["waves_per_tile"]), Pw = 8 / S;
   const int64_t G = ms.G, M = ms.M, K = ms.K;
   const int64_t chunks = cdiv(G, 4);
@@ -452,8 +454,9 @@ void staged_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
   const int64_t tilesets = cdiv(ms.tiles, R);
   const int64_t grid = P["grid"];
   const int64_t off_corr = P["lds0"], off_x = P["lds1"], off_red = P["lds2"];
-  const int E = fp4 ? (MT == 1 ? 2 : 4) : (MT == 1 ? 1 : 4);
+  const int E = fp4 ? (MT == 1 ? NPC : 4) : (MT == 1 ? 1 : 4);
   const int kRowBytes = 144;
+  if (NPC == 3 && MT != 1) fail("staged plan", "three pieces per token on more than one token slot");
   if (SC % S) fail("staged plan", "stage not a multiple of the K split");
   if (MT < M) fail("staged plan", fmtv("token slots %lld < M %lld", MT, M));
   const int64_t U = SC / S, KT = n_stages * U;
@@ -476,12 +479,12 @@ void staged_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
           const bool in = m < M && 4 * c0 + gl < G;
           const int64_t src = in ? m * K + 128 * (4 * c0 + gl) + 8 * q : 0;
           for (int u = 0; u < 4; ++u) X.read(2 * (src + 32 * u), 16, "x (staging)");
-          const int64_t row = off_x + (gl * 2 * MT + 2 * m) * kRowBytes;
+          const int64_t row = off_x + (gl * NPC * MT + NPC * m) * kRowBytes;
           const int qa = 2 * (q & 1), half = 16 * (q >> 1);
-          lds.write(row + qa * 32 + half, 16, "x pieces", tag);
-          lds.write(row + (qa + 1) * 32 + half, 16, "x pieces", tag);
-          lds.write(row + kRowBytes + qa * 32 + half, 16, "x pieces", tag);
-          lds.write(row + kRowBytes + (qa + 1) * 32 + half, 16, "x pieces", tag);
+          for (int pc = 0; pc < NPC; ++pc) {
+            lds.write(row + pc * kRowBytes + qa * 32 + half, 16, "x pieces", tag);
+            lds.write(row + pc * kRowBytes + (qa + 1) * 32 + half, 16, "x pieces", tag);
+          }
           lds.write(off_corr + (gl * MT + m) * 4 + q, 1, "x scales", tag);
         }
         // The first item of each thread was loaded before the weights
@@ -553,12 +556,12 @@ void staged_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
           for (int lane = 0; lane < 64; ++lane) {
             const int j = lane & 15, q = lane >> 4;
             if (fp4) {
-              const int rr = j < 2 * MT ? j : 0;
+              const int rr = j < NPC * MT ? j : 0;
               for (int g = 0; g < 4; ++g) {
                 if (4 * ch + g >= G) break;
-                const int64_t xa = off_x + (c_local * 4 * 2 * MT + rr) * kRowBytes + q * 32 + g * 2 * MT * kRowBytes;
+                const int64_t xa = off_x + (c_local * 4 * NPC * MT + rr) * kRowBytes + q * 32 + g * NPC * MT * kRowBytes;
                 lds.read_tagged(xa, 32, tag, "x pieces read");
-                lds.read_tagged(off_corr + (c_local * 4 * MT + (rr >> 1)) * 4 + q + g * MT * 4, 1, tag,
+                lds.read_tagged(off_corr + (c_local * 4 * MT + rr / NPC) * 4 + q + g * MT * 4, 1, tag,
                                 "x scale read");
               }
             } else {
@@ -593,6 +596,10 @@ void staged_kernel(Mats &ms, std::map<std::string, int64_t> &P, Buf &X) {
             ms.tile_ref(t0 + r, mi, t);
             for (int lane = 0; lane < 64; ++lane) {
               const int j = lane & 15, q = lane >> 4;
+              if (fp4 && NPC == 3) {  // three pieces of token 0 in lane quarter 0
+                if (q == 0) ms.store_y(mi, t, j, 0);
+                continue;
+              }
               for (int e = 0; e < (fp4 ? E / 2 : E); ++e) {
                 const int64_t m = fp4 ? 2 * q + e : 4 * q + e;
                 if (m < M) ms.store_y(mi, t, j, m);

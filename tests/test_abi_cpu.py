@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(lb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert lb.abi_version() == 6
+    assert lb.abi_version() == 7
 
 
 PAGES = ("lnrk.cn page", "ksqn.cn page", "cnblogs.com page", "aberweb.com page")

@@ -281,6 +281,31 @@ def test_bf16_x_wide_dynamic_range(fmt, M):
         gu.check(y, codes, sc, x, "bf16", f"wide range {fmt} M={M} y={ydt}", y_f16=ydt == "f16", ref_ya=ya)
 
 
+@pytest.mark.parametrize("N,K", [(96, 2048), (4096 + 48, 12288)])
+def test_f16_x_wide_dynamic_range_one_token(N, K):
+    """Binary weights with fp16 x at one token run on three fp8 pieces per
+    value: activations spread over the whole fp16 range (2^-24 .. 2^15)
+    inside every 32-value block, a group of zeros, a group of fp16
+    subnormals and a group far below its neighbours must all stay within the
+    bound, for fp32 and fp16 output."""
+    g = np.random.default_rng(320 + K)
+    M = 1
+    codes = synth.codes_binary(g, N, K)
+    sc = synth.scales_absnormal(g, N, K // 128)
+    xf = np.exp2(g.uniform(-24, 15, size=(M, K))) * np.where(g.random((M, K)) < 0.5, -1.0, 1.0)
+    xf[:, 640:768] = 0.0                                                   # a group of zeros
+    xf[:, 768:896] = np.exp2(g.uniform(-24, -15, size=(M, 128))) * np.where(g.random((M, 128)) < 0.5, -1.0, 1.0)
+    xf[:, 1024:1152] = np.exp2(g.uniform(-12, -8, size=(M, 128)))          # far below the groups around it
+    x = synth.f64_to_f16_bits(xf)
+    plan = lb.gemv_plan("q1", [N], M, K, x_dtype="f16")
+    assert plan["operands_name"] == "fp8x3_fp4", plan
+    blob = gu.w_tensor(lb.pack("q1", codes, sc))
+    ya = ref.product(codes, sc, x, "f16")
+    for ydt in ("f32", "f16"):
+        y = gu.run("gemv", "q1", blob, x, "f16", ydt, N, K)
+        gu.check(y, codes, sc, x, "f16", f"f16 wide range N={N} K={K} y={ydt}", y_f16=ydt == "f16", ref_ya=ya)
+
+
 @pytest.mark.parametrize("fmt", ["tq2", "tq5"])
 @pytest.mark.parametrize("M,K", [(1, 1024), (2, 1024), (4, 1024), (8, 1024), (16, 1024), (130, 1024), (4, 8192),
                                  (16, 8192)])
