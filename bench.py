@@ -342,17 +342,25 @@ def read_grid(nbytes):
     return int(min(max(nbytes // (16 * 512 * 4), 256), 8192))
 
 
-def _graph_time_ms(torch, fn, reps=5):
-    """Median over reps replays of a HIP graph holding fn's launches (one
-    untimed replay first); HIP events on the replay stream."""
+def _graph_time_ms(torch, fn, reps=5, warm_ms=30.0):
+    """Median over reps replays of a HIP graph holding fn's launches, after
+    untimed replays that keep the GPU busy for at least warm_ms (a single
+    warm-up replay left the clocks short of their loaded state: the first
+    shape timed after a pause read up to 12% slower than the same launches
+    timed again); HIP events on the replay stream."""
+    import time as _time
     import warnings
     g = torch.cuda.CUDAGraph()
     with warnings.catch_warnings():
         warnings.simplefilter("error")  # an empty capture means launches went to another stream
         with torch.cuda.graph(g):
             fn()
-    g.replay()
-    torch.cuda.synchronize()
+    t0 = _time.perf_counter()
+    n = 0
+    while n < 2 or (_time.perf_counter() - t0) * 1e3 < warm_ms:
+        g.replay()
+        torch.cuda.synchronize()
+        n += 1
     times = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
