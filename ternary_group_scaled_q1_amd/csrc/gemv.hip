@@ -25,8 +25,11 @@
 //    split is exact unless a value sits more than 2^10 below the largest of
 //    its 32 (then the error is below 2^-17 of that largest value).  The A rows
 //    are (token, piece) pairs; the two pieces' products are added in fp32.
-//  * fp16 x, or more than 8 tokens: v_mfma_f32_16x16x32 on exact f16/bf16
-//    operands.
+//    fp16 x at one token takes the same instruction with three pieces
+//    (hi, mid, lo: an fp16 value has 11 significant bits), exact for values
+//    within 2^6 of their block's largest (split_x_regs_f16).
+//  * fp16 x at several tokens, ternary weights, or more than 8 tokens:
+//    v_mfma_f32_16x16x32 on exact f16/bf16 operands.
 //
 // Work split: a workgroup of 8 waves stages x in LDS as [k/8][token][8]
 // 16-byte cells, all of K at once when it fits (then the stage is loaded
@@ -295,7 +298,7 @@ __device__ __forceinline__ void store_tiles(const GemvParams &p, int t0, const f
 }
 
 // fp8 x fp4 path, one unit (R tiles x 4 groups).  Lane 16qa + r reads A row
-// r (token r / NPC, piece r % NPC) of each group; rows past NPC*MP are zero.
+// r (token r / NPC, piece r % NPC) of each group.
 template <int FMT, int MP, int NPC, int R, int E>
 __device__ __forceinline__ void compute_fp4(const GemvParams &p, const char *lds, const Unit<FMT, R> &u, int c_local,
                                             float (&yacc)[R][4]) {
